@@ -1,0 +1,289 @@
+"""The SageAttention forward method, step by step, on the CPU.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+What the pages fix, and where:
+  * K is smoothed along the channel direction before it is quantised to INT8
+    (jisaku.com glossary, 概要 and 主な特徴・仕組み; heatdrop.ai review, "The
+    interesting bit", calls it outlier smoothing).
+  * QK^T runs in INT8, PV in FP8 or FP16 (thu-ml/SageAttention repo card,
+    "How it works"; heatdrop.ai review, "What it does").
+  * The attention weights P are handled in FP8 (jisaku.com glossary, 概要).
+  * PV uses two-level accumulation (repo card, "How it works"; heatdrop.ai,
+    "The interesting bit" and "Key highlights").
+  * Group-query attention, causal masking and the HND/NHD layouts are part of
+    the interface (heatdrop.ai "Key highlights"; cnnetsun.cn guide, basic
+    usage and performance-tuning tips).
+The shape of the computation (per-channel mean over tokens, per-block INT8 with
+INT32 accumulation, online FlashAttention-style softmax, P in FP8 e4m3) is the
+plain reading of those passages.
+
+Readings where the pages are silent (each also listed in the design notes):
+  [R1] INT8 codes round half to even.
+  [R2] scale s = fp32(a/127); codes use x * fp32(127/a) -- one correctly rounded
+       multiply, never fused with the smoothing subtraction.
+  [R3] codes are symmetric in [-127, 127].
+  [R4] an all-zero block gets scale 0 and codes 0.
+  [R5] the K mean runs over all Nk tokens of a (batch, kv-head).
+  [R6] K channel sums are taken in fp64 (exact for these inputs), divided by
+       Nk in fp64 and rounded once to fp32.
+  [R7] quantisation blocks: BLK_Q = 128 query tokens, BLK_K = 64 key tokens,
+       starting at token 0, the last block possibly short; one scale per
+       (batch, head, block) over all d channels.
+  [R8] only K is smoothed (Q and V are not).
+  [R9] V is quantised to e4m3 per channel over all tokens: s_v = fp32(a_v/448),
+       codes e4m3(fp32(V * fp32(448/a_v))).
+  [R10] sm_scale and log2(e) enter through the dequantisation factor
+       c = fp32(s_q * s_k * sm_scale * log2 e); scores live in the log2 domain.
+  [R11] causal masking is top-left aligned (key j > query i is masked).
+  [R12] P goes to e4m3 as e4m3(fp32(448 * P~)); the 1/448 is undone in the
+       epilogue together with s_v.
+  [R13] in FP16-PV mode P is rounded to the input dtype (fp16 or bf16) and
+       multiplied with the unquantised V.
+  [R14] the online softmax walks KV tiles of BKV keys from key 0 upward; BKV
+       is part of the method's definition (P codes depend on the running max).
+  [R15] level-1 accumulation spans one KV tile; level 2 is O = alpha*O + R.
+  [R16] the row sum l accumulates the unquantised fp32 P~.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from .fp8_e4m3 import E4M3_MAX, e4m3_encode, e4m3_decode, e4m3_round
+
+LOG2E = 1.4426950408889634
+INT8_MAX = 127.0
+
+BLK_Q = 128        # [R7]
+BLK_K = 64         # [R7]
+BKV = {64: 64, 128: 64}   # [R14] KV tile per head dim
+
+
+def as_hnd(x: np.ndarray, layout: str) -> np.ndarray:
+    """[B,N,H,d] -> [B,H,N,d] view for NHD inputs (interface layouts: cnnetsun.cn
+    guide, performance-tuning tips, HND or NHD)."""
+    return np.swapaxes(x, 1, 2) if layout == "NHD" else x
+
+
+# ---------------------------------------------------------------------------
+# Step 1: K channel mean  (glossary 概要: smoothing along the channel direction)
+# ---------------------------------------------------------------------------
+def k_channel_mean(k: np.ndarray) -> np.ndarray:
+    """mu[b,h,c] = fp32( (sum_t K[b,h,t,c]) / Nk ), sum and division in fp64 [R5, R6].
+
+    ``k``: float32 array [B,Hkv,Nk,d] holding the fp16/bf16 input values.
+    """
+    n = k.shape[2]
+    total = np.asarray(k, dtype=np.float64).sum(axis=2)
+    return (total / n).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Steps 2-3: smoothing and per-block INT8 quantisation
+#            (repo card "How it works": INT8 for QK^T; glossary 概要)
+# ---------------------------------------------------------------------------
+def smooth_k(k: np.ndarray, mu: np.ndarray) -> np.ndarray:
+    """Ks = fp32(K - mu), one fp32 subtraction per element."""
+    return (np.asarray(k, dtype=np.float32) - mu[:, :, None, :].astype(np.float32)).astype(np.float32)
+
+
+def quant_int8_blocks(x: np.ndarray, blk: int):
+    """Per-block symmetric INT8 [R1-R4, R7].
+
+    ``x``: float32 [B,H,N,d]. Returns (codes int8 [B,H,N,d], scales float32
+    [B,H,ceil(N/blk)]). For each (b, h, block): a = max |x| over the block's
+    tokens and channels, s = fp32(a/127), code = RNE(fp32(x * fp32(127/a))).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    B, H, N, d = x.shape
+    nblk = -(-N // blk)
+    pad = nblk * blk - N
+    xp = np.concatenate([x, np.zeros((B, H, pad, d), np.float32)], axis=2) if pad else x
+    xb = xp.reshape(B, H, nblk, blk, d)
+    a = np.abs(xb).max(axis=(3, 4))                                   # exact
+    scale = (a / np.float32(INT8_MAX)).astype(np.float32)             # fp32 divide, RN
+    with np.errstate(divide="ignore"):
+        inv = np.where(a > 0, np.float32(INT8_MAX) / np.where(a > 0, a, 1), 0).astype(np.float32)
+    prod = (xb * inv[:, :, :, None, None]).astype(np.float32)         # fp32 multiply, RN
+    codes = np.rint(prod)                                             # ties to even [R1]
+    if np.abs(codes).max(initial=0) > INT8_MAX:
+        raise AssertionError("INT8 code outside [-127, 127]")
+    codes = codes.astype(np.int8).reshape(B, H, nblk * blk, d)[:, :, :N]
+    return codes, scale
+
+
+def quant_qk(q: np.ndarray, k: np.ndarray, *, blk_q: int = BLK_Q, blk_k: int = BLK_K, k_mean=None):
+    """The whole Q/K quantisation stage on canonical [B,H,N,d] float32 arrays.
+
+    Returns dict(q8, q_scale, k8, k_scale, k_mean). ``k_mean`` may be given to
+    quantise K against an externally supplied mean.
+    """
+    mu = k_channel_mean(k) if k_mean is None else np.asarray(k_mean, np.float32)
+    q8, sq = quant_int8_blocks(q, blk_q)
+    k8, sk = quant_int8_blocks(smooth_k(k, mu), blk_k)
+    return dict(q8=q8, q_scale=sq, k8=k8, k_scale=sk, k_mean=mu)
+
+
+# ---------------------------------------------------------------------------
+# V to FP8 per channel (repo card / heatdrop.ai: FP8 for the PV product) [R9]
+# ---------------------------------------------------------------------------
+def quant_v_fp8(v: np.ndarray):
+    """Returns (codes uint8 [B,H,d,N] -- keys contiguous per channel --,
+    scales float32 [B,H,d])."""
+    v = np.asarray(v, dtype=np.float32)
+    a = np.abs(v).max(axis=2)                                         # [B,H,d]
+    scale = (a / np.float32(E4M3_MAX)).astype(np.float32)
+    with np.errstate(divide="ignore"):
+        inv = np.where(a > 0, np.float32(E4M3_MAX) / np.where(a > 0, a, 1), 0).astype(np.float32)
+    prod = (v * inv[:, :, None, :]).astype(np.float32)
+    codes = e4m3_encode(prod)
+    return np.ascontiguousarray(np.swapaxes(codes, 2, 3)), scale
+
+
+# ---------------------------------------------------------------------------
+# Step 4: INT32 QK^T
+# ---------------------------------------------------------------------------
+def qk_int32(q8_rows: np.ndarray, k8: np.ndarray) -> np.ndarray:
+    """S_int = q8 . k8^T for one head: [R,d] x [Nk,d] -> int64 [R,Nk].
+
+    Products of int8 codes summed over d <= 256 stay below 2^23 in magnitude,
+    so an fp64 matrix product (a library primitive) is exact; the result is
+    returned as integers.
+    """
+    s = np.asarray(q8_rows, np.float64) @ np.asarray(k8, np.float64).T
+    return s.astype(np.int64)
+
+
+def dequant_factor(sq_rows: np.ndarray, sk_keys: np.ndarray, sm_scale: float) -> np.ndarray:
+    """c[i,j] = fp32(s_q[blk(i)] * s_k[blk(j)] * sm_scale * log2 e) [R10]."""
+    return (sq_rows.astype(np.float64)[:, None] * sk_keys.astype(np.float64)[None, :]
+            * (float(sm_scale) * LOG2E)).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Steps 5-9: tiled online softmax with P quantisation and two-level PV
+# ---------------------------------------------------------------------------
+def online_softmax_pv(s2: np.ndarray, vals: np.ndarray, *, bkv: int, p_codec, work_dtype):
+    """FlashAttention-style online softmax over KV tiles of ``bkv`` keys [R14, R15].
+
+    ``s2``  : [R, Nk] log2-domain scores, -inf where masked.
+    ``vals``: [Nk, dv] float64 values entering the PV product (dequantised-code
+              domain: V8 codes' values in FP8 mode, V itself in FP16 mode).
+    ``p_codec``: maps the fp32 P~ tile to the values that enter the PV product
+              (None: identity).
+    ``work_dtype``: np.float32 for the method (scores, max, P~ in fp32),
+              np.float64 for the unquantised reference recurrence.
+
+    Per tile t, in ascending order:
+      m_new = max(m_old, max_j s2);  alpha = exp2(m_old - m_new)  (0 on the first tile)
+      P~    = exp2(s2 - m_new)
+      l     = alpha * l + sum_j P~                     [R16]
+      R     = codec(P~) . vals_tile                    (level 1: fresh per tile)
+      O     = alpha * O + R                            (level 2)
+    Returns (O [R,dv] float64, l [R] float64) -- not yet normalised.
+    """
+    R_, nk = s2.shape
+    dv = vals.shape[1]
+    m = np.full(R_, -np.inf, dtype=work_dtype)
+    l = np.zeros(R_, dtype=np.float64)
+    o = np.zeros((R_, dv), dtype=np.float64)
+    for t0 in range(0, nk, bkv):
+        st = s2[:, t0:t0 + bkv].astype(work_dtype)
+        m_new = np.maximum(m, st.max(axis=1))
+        live = np.isfinite(m_new)                     # rows with at least one visible key so far
+        m_safe = np.where(live, m_new, 0).astype(work_dtype)
+        with np.errstate(invalid="ignore"):
+            alpha = np.where(np.isfinite(m), np.exp2((m - m_safe).astype(work_dtype)), 0.0)
+            p = np.exp2((st - m_safe[:, None]).astype(work_dtype)).astype(work_dtype)
+        p = np.where(live[:, None], p, 0).astype(work_dtype)
+        alpha = np.where(live, alpha, 0.0).astype(np.float64)
+        l = alpha * l + p.astype(np.float64).sum(axis=1)
+        pq = p.astype(np.float64) if p_codec is None else p_codec(p)
+        r = pq @ vals[t0:t0 + bkv]                    # level 1 (exact for e4m3 x e4m3)
+        o = alpha[:, None] * o + r                    # level 2
+        m = m_new
+    return o, l
+
+
+def _p_codec_fp8(p: np.ndarray) -> np.ndarray:
+    """P8 value = e4m3(fp32(448 * P~)) [R12]."""
+    return e4m3_round((p.astype(np.float32) * np.float32(E4M3_MAX)).astype(np.float32))
+
+
+def _round_to(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round to fp16/bf16 (RNE) and return the rounded values as float64."""
+    if dtype == "fp16":
+        return np.asarray(x).astype(np.float16).astype(np.float64)
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(np.asarray(x, dtype=np.float32)))
+        return t.to(torch.bfloat16).to(torch.float64).numpy()
+    raise ValueError(dtype)
+
+
+def _p_codec_half(dtype: str):
+    def codec(p):
+        return _round_to(p.astype(np.float32), dtype)       # [R13]
+    return codec
+
+
+def sage_attention(q, k, v, *, dtype: str, is_causal: bool, sm_scale: float, pv: str,
+                   layout: str = "HND", blk_q: int = BLK_Q, blk_k: int = BLK_K, bkv=None,
+                   rows=None, parts=None, return_fp64: bool = False):
+    """Quantised attention forward, step by step.
+
+    ``q,k,v``: float32 numpy arrays holding the fp16/bf16 input values in
+    ``layout`` ([B,H,N,d] for HND, [B,N,H,d] for NHD). ``rows``: optional
+    sorted query rows to compute (output row i depends only on Q's block
+    containing i and on all of K and V). ``parts``: optional precomputed
+    quantisation outputs (dict from ``quant_qk`` plus ``v8``/``v_scale``).
+    Returns [B,Hq,R,d] in HND order, rounded to ``dtype`` (float64 array of the
+    rounded values), or the unrounded fp64 result when ``return_fp64``.
+    """
+    q = as_hnd(np.asarray(q, np.float32), layout)
+    k = as_hnd(np.asarray(k, np.float32), layout)
+    v = as_hnd(np.asarray(v, np.float32), layout)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    bkv = BKV[d] if bkv is None else bkv
+    rows = np.arange(Nq) if rows is None else np.asarray(rows)
+
+    if parts is None:
+        parts = quant_qk(q, k, blk_q=blk_q, blk_k=blk_k)
+        if pv == "fp8":
+            parts["v8"], parts["v_scale"] = quant_v_fp8(v)
+    q8, sq, k8, sk = parts["q8"], parts["q_scale"], parts["k8"], parts["k_scale"]
+    if pv == "fp8":
+        vals_all = e4m3_decode(parts["v8"])                 # [B,Hkv,d,Nk]
+        codec = _p_codec_fp8
+    elif pv == "fp16":
+        codec = _p_codec_half(dtype)
+    else:
+        raise ValueError(pv)
+
+    keys = np.arange(Nk)
+    out = np.empty((B, Hq, len(rows), d), dtype=np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            s_int = qk_int32(q8[b, h, rows], k8[b, g])                          # step 4
+            c = dequant_factor(sq[b, h, rows // blk_q], sk[b, g, keys // blk_k], sm_scale)
+            s2 = (s_int.astype(np.float32) * c).astype(np.float32)              # step 5
+            if is_causal:
+                s2 = np.where(keys[None, :] > rows[:, None], np.float32(-np.inf), s2)
+            if pv == "fp8":
+                vals = np.ascontiguousarray(vals_all[b, g].T)                   # [Nk, d] code values
+            else:
+                vals = v[b, g].astype(np.float64)
+            o, l = online_softmax_pv(s2, vals, bkv=bkv, p_codec=codec, work_dtype=np.float32)
+            if pv == "fp8":                                                     # epilogue
+                o = o * (parts["v_scale"][b, g].astype(np.float64) / E4M3_MAX)[None, :]
+            out[b, h] = o / l[:, None]
+    if return_fp64:
+        return out
+    return _round_to(out, dtype)

@@ -1,0 +1,211 @@
+"""Pins for the oracle's attention path (CPU only).
+
+* The oracle's tiled online-softmax recurrence, run in fp64 with quantisation
+  switched off, reaches exact softmax attention (closed form) for any tile
+  size, causal or not, ragged or not, with GQA.
+* Exact attention is invariant to subtracting a per-channel K mean -- the fact
+  channel smoothing relies on.
+* Closed forms of the quantised method: Q = 0 (uniform weights, P~ = 1 and the
+  FP8 code of 448 exactly), causal row 0 (only key 0 is visible), all K tokens
+  identical (smoothing zeroes K entirely).
+* Structure: GQA equals explicit K/V head repetition, NHD equals HND, sampled
+  rows equal the full computation's rows.
+* Method accuracy: the quantised oracle against fp64 exact attention.
+* Planted mistakes: each of several plausible oracle bugs fails one of the pins.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import exact, sage_ref
+from oracle.fp8_e4m3 import e4m3_decode
+
+
+def _inputs(w):
+    q, k, v = W.generate(w)
+    return tuple(sage_ref.as_hnd(x.float().numpy(), w.layout) for x in (q, k, v))
+
+
+def cos(a, b):
+    a, b = np.ravel(a).astype(np.float64), np.ravel(b).astype(np.float64)
+    return float(a @ b / np.sqrt((a @ a) * (b @ b)))
+
+
+SMALL = W.TINY.with_(B=2, Hq=4, Hkv=2, N=200, d=64)
+
+
+# --------------------------------------------------------------------------- recurrence
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("bkv", [16, 64, 100, 256])
+def test_online_softmax_equals_exact(causal, bkv):
+    q, k, v = _inputs(SMALL.with_(N=203))
+    ref = exact.exact_attention(q, k, v, is_causal=causal, sm_scale=0.125)
+    got = exact.online_softmax_attention(q, k, v, is_causal=causal, sm_scale=0.125, bkv=bkv)
+    assert np.abs(got - ref).max() <= 1e-12 * np.abs(ref).max()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_exact_attention_invariant_to_k_channel_shift(causal):
+    q, k, v = _inputs(SMALL)
+    mu = k.astype(np.float64).mean(axis=2, keepdims=True)
+    a = exact.exact_attention(q, k, v, is_causal=causal, sm_scale=0.125)
+    b = exact.exact_attention(q, k.astype(np.float64) - mu, v, is_causal=causal, sm_scale=0.125)
+    assert np.abs(a - b).max() <= 1e-12 * np.abs(a).max()
+
+
+# --------------------------------------------------------------------------- closed forms
+def _dequant_v(v, pv):
+    if pv == "fp16":
+        return v.astype(np.float64)
+    codes, scale = sage_ref.quant_v_fp8(v)
+    return np.swapaxes(e4m3_decode(codes), 2, 3) * scale[:, :, None, :].astype(np.float64)
+
+
+@pytest.mark.parametrize("pv", ["fp16", "fp8"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_q_gives_mean_of_values(pv, causal):
+    w = SMALL.with_(N=150)
+    q, k, v = _inputs(w)
+    q = np.zeros_like(q)
+    o = sage_ref.sage_attention(q, k, v, dtype="fp16", is_causal=causal, sm_scale=0.125, pv=pv,
+                                return_fp64=True)
+    vd = np.repeat(_dequant_v(v, pv), 2, axis=1)                 # GQA: 2 query heads per kv head
+    if causal:
+        want = np.cumsum(vd, axis=2) / np.arange(1, 151)[None, None, :, None]
+    else:
+        want = np.broadcast_to(vd.mean(axis=2, keepdims=True), vd.shape)
+    assert np.allclose(o, want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+
+
+@pytest.mark.parametrize("pv", ["fp16", "fp8"])
+def test_causal_row0_is_value0(pv):
+    q, k, v = _inputs(SMALL)
+    o = sage_ref.sage_attention(q, k, v, dtype="fp16", is_causal=True, sm_scale=0.125, pv=pv,
+                                rows=[0], return_fp64=True)
+    v0 = np.repeat(v[:, :, :1].astype(np.float64), 2, axis=1)[:, :, 0]
+    if pv == "fp16":
+        assert np.array_equal(o[:, :, 0], v0)          # weight 1 on key 0, exactly
+    else:
+        # V[0] through one e4m3 rounding: within half an e4m3 ulp of the raw value
+        a = np.repeat(np.abs(v).max(axis=2), 2, axis=1)
+        assert np.all(np.abs(o[:, :, 0] - v0) <= 2.0 ** -4 * np.abs(v0) * (1 + 1e-9) + a / 448 * 2.0 ** -10)
+
+
+@pytest.mark.parametrize("pv", ["fp16", "fp8"])
+def test_identical_keys_give_uniform_attention(pv):
+    q, k, v = _inputs(SMALL)
+    k = np.broadcast_to(k[:, :, :1], k.shape).copy()
+    parts = sage_ref.quant_qk(q, k)
+    assert not parts["k8"].any() and not parts["k_scale"].any()      # smoothing zeroes K
+    o = sage_ref.sage_attention(q, k, v, dtype="fp16", is_causal=False, sm_scale=0.125, pv=pv,
+                                return_fp64=True)
+    want = np.repeat(_dequant_v(v, pv), 2, axis=1).mean(axis=2, keepdims=True)
+    assert np.allclose(o, np.broadcast_to(want, o.shape), rtol=1e-12, atol=1e-14)
+
+
+# --------------------------------------------------------------------------- structure
+@pytest.mark.parametrize("pv", ["fp16", "fp8"])
+def test_gqa_equals_repeated_heads(pv):
+    q, k, v = _inputs(SMALL)
+    a = sage_ref.sage_attention(q, k, v, dtype="fp16", is_causal=True, sm_scale=0.125, pv=pv)
+    b = sage_ref.sage_attention(q, np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1), dtype="fp16",
+                                is_causal=True, sm_scale=0.125, pv=pv)
+    assert np.array_equal(a, b)
+
+
+def test_nhd_equals_hnd_and_rows_subset():
+    w = SMALL.with_(dtype="bf16", N=257)
+    q, k, v = _inputs(w)
+    full = sage_ref.sage_attention(q, k, v, dtype="bf16", is_causal=True, sm_scale=0.125, pv="fp8")
+    nhd = [np.ascontiguousarray(np.swapaxes(x, 1, 2)) for x in (q, k, v)]
+    b = sage_ref.sage_attention(*nhd, dtype="bf16", is_causal=True, sm_scale=0.125, pv="fp8", layout="NHD")
+    assert np.array_equal(full, b)
+    rows = [0, 5, 127, 128, 256]
+    c = sage_ref.sage_attention(q, k, v, dtype="bf16", is_causal=True, sm_scale=0.125, pv="fp8", rows=rows)
+    assert np.array_equal(full[:, :, rows], c)
+
+
+# --------------------------------------------------------------------------- method accuracy
+ACCURACY = [
+    (W.TINY, None, "fp16", 0.999),
+    (W.GQA_CAUSAL.with_(B=1, Hq=8, Hkv=2, N=2048), 96, "fp8", 0.999),
+    (W.LONG_D64.with_(Hq=2, Hkv=2, N=4096), 96, "fp16", 0.999),
+    (W.LONG_D64.with_(Hq=2, Hkv=2, N=4096), 96, "fp8", 0.999),
+    (W.PEAK.with_(Hq=2, Hkv=2, N=8192), 64, "fp8", 0.999),
+    (W.PEAK.with_(Hq=2, Hkv=2, N=8192, causal=True), 64, "fp8", 0.999),
+    # 4 shared outlier channels x10 make attention very peaked (logit std ~17);
+    # per-block INT8 Q/K then bounds the method near 0.998 (finer granularity
+    # does not reach 0.999 either), so the bound here is the method's own.
+    (W.MID_OUTLIER.with_(B=1, Hq=4, Hkv=4), 96, "fp8", 0.9975),
+]
+
+
+@pytest.mark.parametrize("w,nrows,pv,bound", ACCURACY, ids=[f"{a[0].name}-{a[2]}-{'c' if a[0].causal else 'nc'}" for a in ACCURACY])
+def test_method_accuracy_vs_fp64(w, nrows, pv, bound):
+    q, k, v = _inputs(w)
+    rows = None if nrows is None else W.sample_rows(w.N, nrows, sage_ref.BLK_Q)
+    o = sage_ref.sage_attention(q, k, v, dtype=w.dtype, is_causal=w.causal, sm_scale=w.sm_scale,
+                                pv=pv, rows=rows)
+    e = exact.exact_attention(q, k, v, is_causal=w.causal, sm_scale=w.sm_scale, rows=rows)
+    assert cos(o, e) >= bound
+    rel_l1 = np.abs(o - e).sum() / np.abs(e).sum()
+    assert rel_l1 <= 0.06
+
+
+# --------------------------------------------------------------------------- planted mistakes
+def _fails(check):
+    try:
+        check()
+    except AssertionError:
+        return True
+    return False
+
+
+def test_planted_mistakes_are_caught(monkeypatch):
+    from tests import test_oracle_quant as tq
+
+    # 1. smoothing with the wrong sign
+    with monkeypatch.context() as m:
+        m.setattr(sage_ref, "smooth_k", lambda k, mu: (k + mu[:, :, None, :]).astype(np.float32))
+        assert _fails(tq.test_smoothed_k_has_zero_channel_mean)
+    # 2. smoothing dropped
+    with monkeypatch.context() as m:
+        m.setattr(sage_ref, "smooth_k", lambda k, mu: k.astype(np.float32))
+        assert _fails(tq.test_smoothed_k_has_zero_channel_mean)
+    # 3. K mean divided by N+1
+    orig_mean = sage_ref.k_channel_mean
+    with monkeypatch.context() as m:
+        m.setattr(sage_ref, "k_channel_mean",
+                  lambda k: (orig_mean(k).astype(np.float64) * k.shape[2] / (k.shape[2] + 1)).astype(np.float32))
+        assert _fails(tq.test_k_mean_is_exact_sum_correctly_divided)
+    # 4. P scaled by 240 (the FNUZ maximum) instead of 448
+    with monkeypatch.context() as m:
+        from oracle.fp8_e4m3 import e4m3_round
+        m.setattr(sage_ref, "_p_codec_fp8",
+                  lambda p: e4m3_round((p.astype(np.float32) * np.float32(240)).astype(np.float32)))
+        assert _fails(lambda: test_zero_q_gives_mean_of_values("fp8", False))
+    # 5. log2(e) dropped from the dequantisation factor (natural-log scores fed to exp2)
+    orig_dq = sage_ref.dequant_factor
+    with monkeypatch.context() as m:
+        m.setattr(sage_ref, "dequant_factor", lambda a, b, s: orig_dq(a, b, s / sage_ref.LOG2E))
+        assert _fails(lambda: test_method_accuracy_vs_fp64(*ACCURACY[0]))
+    # 6. INT8 rounding half away from zero instead of half to even
+    orig_rint = np.rint
+    with monkeypatch.context() as m:
+        m.setattr(sage_ref.np, "rint", lambda x: np.trunc(x + np.copysign(0.5, x)))
+        assert _fails(tq.test_int8_worked_examples)
+    assert np.rint is orig_rint
+    # 7. V codes left token-major (the layout the PV product does not expect)
+    orig_v = sage_ref.quant_v_fp8
+    with monkeypatch.context() as m:
+        def v_untransposed(v):
+            c, s = orig_v(v)
+            return np.ascontiguousarray(np.swapaxes(c, 2, 3)).reshape(c.shape), s
+        m.setattr(sage_ref, "quant_v_fp8", v_untransposed)
+        assert _fails(tq.test_v_fp8_invariants_and_layout)
+        assert _fails(lambda: test_causal_row0_is_value0("fp8"))
+    # 8. keys paired with the wrong rows of K (a mis-indexed operand)
+    with monkeypatch.context() as m:
+        orig_q = sage_ref.qk_int32
+        m.setattr(sage_ref, "qk_int32", lambda q8, k8: orig_q(q8, k8[::-1]))   # keys reversed
+        assert _fails(lambda: test_method_accuracy_vs_fp64(*ACCURACY[0]))
