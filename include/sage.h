@@ -1,0 +1,147 @@
+/*
+ * sage.h -- C ABI of the MI355X (gfx950) quantised-attention library (libsage.so).
+ *
+ * The library implements the forward hot path of SageAttention-style quantised
+ * scaled-dot-product attention:
+ *   K is smoothed by subtracting its per-channel mean over tokens; Q and K are
+ *   quantised per block to INT8; S = Q K^T runs on INT8 matrix cores with INT32
+ *   accumulation and is dequantised; an online (FlashAttention-style) softmax
+ *   produces P, which is quantised to FP8 e4m3 (or kept in FP16/BF16) for the PV
+ *   product, accumulated in two levels.
+ * Sources: thu-ml/SageAttention repo card (vibecrowd.fund), "How it works"
+ * (INT8 for QK^T, FP16/FP8 for PV, two-level PV accumulation); jisaku.com
+ * glossary "SageAttention", 概要 and 主な特徴・仕組み (K smoothed along the
+ * channel direction, P handled in FP8); heatdrop.ai review, "What it does" and
+ * "The interesting bit" (drop-in for scaled_dot_product_attention, outlier
+ * smoothing, two-level accumulation inside FP8 matrix units); cnnetsun.cn guide,
+ * basic usage (q, k, v shaped (batch, heads, seq, head_dim), tensor_layout,
+ * is_causal) and tuning tips (HND or NHD layout, causal masking).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.   Every tensor pointer is a DEVICE pointer (hipMalloc'd or from a
+ *             framework allocator) on the current HIP device. The caller owns
+ *             every buffer; the library allocates nothing, frees nothing and
+ *             keeps no pointer after a call returns.
+ * Stream.     `stream` is a hipStream_t passed as void* (NULL = the default
+ *             stream). All work is enqueued asynchronously on it; no call
+ *             synchronises. Calls on one stream are ordered; concurrent calls
+ *             that share a workspace race.
+ * Errors.     Arguments are validated on the host BEFORE any HIP call, and a
+ *             non-SAGE_OK status means nothing was enqueued (SAGE_ERR_HIP aside:
+ *             a launch that the runtime rejected). Faults inside kernels surface
+ *             at the caller's next synchronisation. Nothing throws across the ABI.
+ * Layouts.    Inputs/outputs use the caller's `layout`: HND = [B, H, N, d],
+ *             NHD = [B, N, H, d], dense with d contiguous. Quantised codes and
+ *             scales always use the canonical per-head orders given below.
+ * Alignment.  Tensor and code pointers must be 16-byte aligned, scale/mean
+ *             pointers 4-byte aligned, workspaces 256-byte aligned.
+ * Sizes.      1 <= B, Hq, Hkv; Hq % Hkv == 0 (group-query attention: query head
+ *             h uses kv head h / (Hq/Hkv)); head_dim in {64, 128}; 0 <= Nq, Nk
+ *             <= 2^20 (Nq == 0 or B == 0 is a valid no-op; Nk == 0 with Nq > 0
+ *             is invalid: softmax over no keys).
+ */
+#ifndef SAGE_H
+#define SAGE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sage_status {
+  SAGE_OK = 0,
+  SAGE_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size, bad enum, aliasing output */
+  SAGE_ERR_UNSUPPORTED = 2,      /* valid request this build does not implement (head_dim, causal Nq != Nk) */
+  SAGE_ERR_WORKSPACE = 3,        /* workspace smaller than the query function reports */
+  SAGE_ERR_HIP = 4               /* the HIP runtime rejected a launch */
+} sage_status;
+
+typedef enum sage_layout { SAGE_LAYOUT_HND = 0, SAGE_LAYOUT_NHD = 1 } sage_layout;
+typedef enum sage_dtype { SAGE_DTYPE_F16 = 0, SAGE_DTYPE_BF16 = 1 } sage_dtype;
+/* PV product precision (repo card "How it works": FP16 or FP8 for PV).
+ * SAGE_PV_FP16 keeps P and V in the input dtype (fp16, or bf16 for bf16 inputs). */
+typedef enum sage_pv_dtype { SAGE_PV_FP16 = 0, SAGE_PV_FP8_E4M3 = 1 } sage_pv_dtype;
+
+typedef struct sage_shape {
+  int32_t batch;     /* B   */
+  int32_t heads_q;   /* Hq  */
+  int32_t heads_kv;  /* Hkv */
+  int32_t seq_q;     /* Nq  */
+  int32_t seq_k;     /* Nk  */
+  int32_t head_dim;  /* d   */
+  int32_t layout;    /* sage_layout of q, k, v and o */
+  int32_t dtype;     /* sage_dtype of q, k, v and o  */
+} sage_shape;
+
+/* Quantisation block sizes and the online-softmax KV tile for `head_dim`.
+ * BLK_Q query tokens / BLK_K key tokens share one INT8 scale (blocks start at
+ * token 0, the last one may be short); the softmax walks KV tiles of BKV keys
+ * from key 0 upward, so BKV is part of the result's definition (P's FP8 codes
+ * depend on the running row max).
+ * Returns SAGE_ERR_UNSUPPORTED for other head dims; null outputs are skipped. */
+sage_status sage_block_sizes(int32_t head_dim, int32_t* blk_q, int32_t* blk_k, int32_t* bkv);
+
+/* Nk rounded up to the padded key count of transposed V codes (multiple of 64). */
+int64_t sage_v_codes_stride(int32_t seq_k);
+
+/* Workspace bytes sage_quant_qk needs for `s` (K channel-sum partials). */
+size_t sage_quant_qk_workspace_bytes(const sage_shape* s);
+/* Workspace bytes sage_quant_v needs for `s` (V channel-absmax partials). */
+size_t sage_quant_v_workspace_bytes(const sage_shape* s);
+/* Workspace bytes sage_attn_fwd needs for `s` and `pv` (all quantised
+ * intermediates: Q/K codes and scales, K mean, V codes or transposed V, V
+ * scales, reduction partials). Returns 0 for an invalid shape. */
+size_t sage_workspace_bytes(const sage_shape* s, int32_t pv_dtype);
+
+/* K smoothing + per-block INT8 quantisation of Q and K.
+ * (glossary 概要: K smoothed along the channel direction, then INT8;
+ *  repo card "How it works": INT8 for QK^T.)
+ *   k_mean [B,Hkv,d] fp32      mu = fp32((sum over all Nk tokens, in fp64) / Nk)
+ *   q_codes [B,Hq,Nq,d] int8   round-half-even(fp32(q * fp32(127/a))), a = block absmax
+ *   q_scale [B,Hq,ceil(Nq/BLK_Q)] fp32  a/127 (0 for an all-zero block, codes 0)
+ *   k_codes [B,Hkv,Nk,d] int8  the same rule on fp32(k - mu)
+ *   k_scale [B,Hkv,ceil(Nk/BLK_K)] fp32
+ * Codes are in canonical HND order whatever `s->layout` is. */
+sage_status sage_quant_qk(const sage_shape* s, const void* q, const void* k,
+                          int8_t* q_codes, float* q_scale,
+                          int8_t* k_codes, float* k_scale, float* k_mean,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Per-channel FP8 e4m3 (OCP, saturating, round-half-even) quantisation of V.
+ * (repo card / heatdrop.ai "What it does": FP8 for the PV product.)
+ *   v_scale [B,Hkv,d] fp32                       a_v/448, a_v = max over all tokens of |v|
+ *   v_codes [B,Hkv,d,sage_v_codes_stride(Nk)] u8  e4m3(fp32(v * fp32(448/a_v))),
+ *           keys contiguous per channel; padding keys are written as 0. */
+sage_status sage_quant_v(const sage_shape* s, const void* v,
+                         uint8_t* v_codes, float* v_scale,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* The whole forward: o = SageAttention(q, k, v).
+ * is_causal: query i attends keys j <= i (top-left; requires Nq == Nk).
+ * sm_scale:  softmax temperature (finite, > 0; 1/sqrt(d) for the drop-in).
+ * pv_dtype:  sage_pv_dtype. o has q's shape, dtype and layout and must not
+ *            overlap q, k, v or the workspace.
+ * Runs, in order on `stream`: channel statistics, Q/K (and V) quantisation,
+ * then the fused attention kernel (INT8 QK^T, dequantisation, online softmax,
+ * P quantisation, PV with two-level accumulation, normalisation). */
+sage_status sage_attn_fwd(const sage_shape* s, const void* q, const void* k, const void* v,
+                          void* o, int32_t is_causal, float sm_scale, int32_t pv_dtype,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Test hook: the INT32 QK^T of the attention kernel's own matrix-core tile code,
+ * for canonical-order codes as produced by sage_quant_qk.
+ *   s_out [B,Hq,Nq,Nk] int32, s_out[b,h,i,j] = sum_c q_codes[b,h,i,c] * k_codes[b,h/G,j,c]. */
+sage_status sage_debug_qk_i32(const sage_shape* s, const int8_t* q_codes, const int8_t* k_codes,
+                              int32_t* s_out, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* sage_status_string(sage_status st);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAGE_H */

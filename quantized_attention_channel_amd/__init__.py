@@ -1,0 +1,234 @@
+"""Python binding of libsage (include/sage.h): MI355X quantised attention forward.
+
+Argument marshalling only. Every step of the computation runs in the gfx950 HIP
+kernels behind the C ABI; PyTorch supplies device memory and the current stream.
+There is no fallback: if ``libsage.so`` is missing or fails to load, importing
+the binding raises.
+
+Entry points (same names as the C ABI):
+  sage_block_sizes, sage_v_codes_stride, sage_workspace_bytes,
+  sage_quant_qk, sage_quant_v, sage_attn_fwd, sage_debug_qk_i32.
+User-facing wrapper:
+  sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None,
+           pv_dtype="fp8") -- the call shape the SageAttention pages show
+  (cnnetsun.cn guide, basic usage; thu-ml/SageAttention repo card, "How to use").
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsage.so")
+
+SAGE_OK, SAGE_ERR_INVALID_ARGUMENT, SAGE_ERR_UNSUPPORTED, SAGE_ERR_WORKSPACE, SAGE_ERR_HIP = range(5)
+LAYOUTS = {"HND": 0, "NHD": 1}
+DTYPES = {torch.float16: 0, torch.bfloat16: 1}
+PV_DTYPES = {"fp16": 0, "fp8": 1, "fp8_e4m3": 1}
+
+# Every function the header declares, with its ctypes signature.
+_c_shape_p = ctypes.c_void_p
+_vp = ctypes.c_void_p
+_SIGNATURES = {
+    "sage_block_sizes": (ctypes.c_int, [ctypes.c_int32, _vp, _vp, _vp]),
+    "sage_v_codes_stride": (ctypes.c_int64, [ctypes.c_int32]),
+    "sage_quant_qk_workspace_bytes": (ctypes.c_size_t, [_c_shape_p]),
+    "sage_quant_v_workspace_bytes": (ctypes.c_size_t, [_c_shape_p]),
+    "sage_workspace_bytes": (ctypes.c_size_t, [_c_shape_p, ctypes.c_int32]),
+    "sage_quant_qk": (ctypes.c_int, [_c_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "sage_quant_v": (ctypes.c_int, [_c_shape_p, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "sage_attn_fwd": (ctypes.c_int, [_c_shape_p, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_float,
+                                     ctypes.c_int32, _vp, ctypes.c_size_t, _vp]),
+    "sage_debug_qk_i32": (ctypes.c_int, [_c_shape_p, _vp, _vp, _vp, _vp]),
+    "sage_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+}
+
+
+class SageShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("batch", "heads_q", "heads_kv", "seq_q", "seq_k", "head_dim", "layout", "dtype")]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run quantized_attention_channel_amd/build.py "
+                          "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+class SageError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {lib.sage_status_string(status).decode()}")
+
+
+def _check(status: int, where: str):
+    if status != SAGE_OK:
+        raise SageError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def make_shape(B, Hq, Hkv, Nq, Nk, d, layout="HND", dtype=torch.float16) -> SageShape:
+    return SageShape(B, Hq, Hkv, Nq, Nk, d, LAYOUTS[layout], DTYPES[dtype])
+
+
+def shape_of(q: torch.Tensor, k: torch.Tensor, layout: str) -> SageShape:
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be 4-D")
+    if layout == "HND":
+        B, Hq, Nq, d = q.shape
+        _, Hkv, Nk, _ = k.shape
+    elif layout == "NHD":
+        B, Nq, Hq, d = q.shape
+        _, Nk, Hkv, _ = k.shape
+    else:
+        raise ValueError(f"tensor_layout must be HND or NHD, got {layout!r}")
+    if q.dtype not in DTYPES:
+        raise TypeError(f"q/k/v must be float16 or bfloat16, got {q.dtype}")
+    return make_shape(B, Hq, Hkv, Nq, Nk, d, layout, q.dtype)
+
+
+def _ref(s: SageShape):
+    return ctypes.byref(s)
+
+
+# ------------------------------------------------------------------ queries
+def sage_block_sizes(head_dim: int):
+    bq, bk, bkv = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(lib.sage_block_sizes(head_dim, ctypes.byref(bq), ctypes.byref(bk), ctypes.byref(bkv)),
+           "sage_block_sizes")
+    return bq.value, bk.value, bkv.value
+
+
+def sage_v_codes_stride(seq_k: int) -> int:
+    return int(lib.sage_v_codes_stride(seq_k))
+
+
+def sage_workspace_bytes(shape: SageShape, pv_dtype: str = "fp8") -> int:
+    return int(lib.sage_workspace_bytes(_ref(shape), PV_DTYPES[pv_dtype]))
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def _check_inputs(*ts):
+    dev = ts[0].device
+    for t in ts:
+        if not t.is_cuda or t.device != dev:
+            raise ValueError("all tensors must be on the same GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous in the stated layout")
+
+
+# ------------------------------------------------------------------ entry points
+def sage_quant_qk(q: torch.Tensor, k: torch.Tensor, tensor_layout: str = "HND"):
+    """Returns dict(q_codes, q_scale, k_codes, k_scale, k_mean) (canonical HND order)."""
+    _check_inputs(q, k)
+    s = shape_of(q, k, tensor_layout)
+    blk_q, blk_k, _ = sage_block_sizes(s.head_dim)
+    dev = q.device
+    out = dict(
+        q_codes=torch.empty((s.batch, s.heads_q, s.seq_q, s.head_dim), dtype=torch.int8, device=dev),
+        q_scale=torch.empty((s.batch, s.heads_q, -(-s.seq_q // blk_q)), dtype=torch.float32, device=dev),
+        k_codes=torch.empty((s.batch, s.heads_kv, s.seq_k, s.head_dim), dtype=torch.int8, device=dev),
+        k_scale=torch.empty((s.batch, s.heads_kv, -(-s.seq_k // blk_k)), dtype=torch.float32, device=dev),
+        k_mean=torch.empty((s.batch, s.heads_kv, s.head_dim), dtype=torch.float32, device=dev),
+    )
+    ws = _workspace(lib.sage_quant_qk_workspace_bytes(_ref(s)), dev)
+    _check(lib.sage_quant_qk(_ref(s), _ptr(q), _ptr(k), _ptr(out["q_codes"]), _ptr(out["q_scale"]),
+                             _ptr(out["k_codes"]), _ptr(out["k_scale"]), _ptr(out["k_mean"]),
+                             _ptr(ws), ws.numel(), _stream(dev)), "sage_quant_qk")
+    return out
+
+
+def sage_quant_v(v: torch.Tensor, tensor_layout: str = "HND"):
+    """Returns (v_codes uint8 [B,Hkv,d,Nk_pad], v_scale fp32 [B,Hkv,d])."""
+    _check_inputs(v)
+    s = shape_of(v, v, tensor_layout)
+    dev = v.device
+    npad = sage_v_codes_stride(s.seq_k)
+    codes = torch.empty((s.batch, s.heads_kv, s.head_dim, npad), dtype=torch.uint8, device=dev)
+    scale = torch.empty((s.batch, s.heads_kv, s.head_dim), dtype=torch.float32, device=dev)
+    ws = _workspace(lib.sage_quant_v_workspace_bytes(_ref(s)), dev)
+    _check(lib.sage_quant_v(_ref(s), _ptr(v), _ptr(codes), _ptr(scale), _ptr(ws), ws.numel(), _stream(dev)),
+           "sage_quant_v")
+    return codes, scale
+
+
+def sage_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, is_causal: bool = False,
+                  sm_scale: Optional[float] = None, pv_dtype: str = "fp8", tensor_layout: str = "HND",
+                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _check_inputs(q, k, v)
+    s = shape_of(q, k, tensor_layout)
+    if tuple(v.shape) != tuple(k.shape) or v.dtype != q.dtype or k.dtype != q.dtype:
+        raise ValueError("v must have k's shape and all inputs one dtype")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(s.head_dim)
+    dev = q.device
+    o = torch.empty_like(q) if out is None else out
+    need = sage_workspace_bytes(s, pv_dtype)
+    ws = workspace if workspace is not None and workspace.numel() >= need else _workspace(need, dev)
+    _check(lib.sage_attn_fwd(_ref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(o), int(bool(is_causal)),
+                             float(sm_scale), PV_DTYPES[pv_dtype], _ptr(ws), ws.numel(), _stream(dev)),
+           "sage_attn_fwd")
+    return o
+
+
+def sage_debug_qk_i32(q_codes: torch.Tensor, k_codes: torch.Tensor) -> torch.Tensor:
+    """INT32 S for canonical-order codes [B,Hq,Nq,d] x [B,Hkv,Nk,d] -> [B,Hq,Nq,Nk]."""
+    _check_inputs(q_codes, k_codes)
+    B, Hq, Nq, d = q_codes.shape
+    _, Hkv, Nk, _ = k_codes.shape
+    s = make_shape(B, Hq, Hkv, Nq, Nk, d)
+    out = torch.empty((B, Hq, Nq, Nk), dtype=torch.int32, device=q_codes.device)
+    _check(lib.sage_debug_qk_i32(_ref(s), _ptr(q_codes), _ptr(k_codes), _ptr(out), _stream(q_codes.device)),
+           "sage_debug_qk_i32")
+    return out
+
+
+def sageattn(q, k, v, tensor_layout: str = "HND", is_causal: bool = False, sm_scale: Optional[float] = None,
+             pv_dtype: str = "fp8", **kwargs):
+    """Quantised attention with the scaled-dot-product-attention call shape.
+
+    SDPA arguments this method does not implement are rejected rather than
+    silently ignored (a plain monkey-patch of SDPA breaks many models when
+    arguments are dropped -- heatdrop.ai review, "Caveats").
+    """
+    for name in ("attn_mask", "dropout_p", "enable_gqa", "scale"):
+        if name in kwargs:
+            val = kwargs.pop(name)
+            if name == "scale":
+                sm_scale = val if val is not None else sm_scale
+            elif name == "dropout_p" and val:
+                raise NotImplementedError("dropout is not supported")
+            elif name == "attn_mask" and val is not None:
+                raise NotImplementedError("explicit attention masks are not supported")
+    if kwargs:
+        raise TypeError(f"unexpected arguments: {sorted(kwargs)}")
+    return sage_attn_fwd(q.contiguous(), k.contiguous(), v.contiguous(), is_causal=is_causal,
+                         sm_scale=sm_scale, pv_dtype=pv_dtype, tensor_layout=tensor_layout)
+
+
+__all__ = ["sageattn", "sage_attn_fwd", "sage_quant_qk", "sage_quant_v", "sage_debug_qk_i32",
+           "sage_block_sizes", "sage_v_codes_stride", "sage_workspace_bytes", "make_shape", "shape_of",
+           "SageError", "SageShape", "lib", "LIB_PATH"]

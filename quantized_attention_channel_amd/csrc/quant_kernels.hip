@@ -1,0 +1,285 @@
+// Channel statistics, K smoothing and the INT8 / FP8 quantisation kernels.
+//
+// These are HBM-bound scans: every kernel reads each input element once per
+// pass with 16-byte coalesced loads (a token row of one head is d contiguous
+// 16-bit values in both layouts) and writes codes with 8/16-byte stores.
+//
+// Arithmetic is kept bit-compatible with a plain IEEE reading of the method:
+// fp64 channel sums, correctly rounded fp32 divides, separate (never fused)
+// subtract and multiply, round-half-to-even to integers.
+#include "sage_device.h"
+#include "sage_launch.h"
+
+#pragma clang fp contract(off)
+
+namespace sage {
+
+constexpr int kStatChunk = 256;  // tokens per statistics work-group
+
+// Per (b, kv-head, 256-token chunk): fp64 sums of K over tokens per channel and,
+// optionally, fp32 max |V| per channel. Partials go to [B*H][chunks][D] in a
+// fixed order (no atomics), so the result does not depend on scheduling.
+template <typename T, int D, bool WITH_K, bool WITH_V>
+__global__ __launch_bounds__(256) void channel_stats_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, TensorGeom geo, int H, int N,
+    int chunks, double* __restrict__ ksum_part, float* __restrict__ vmax_part) {
+  constexpr int TPR = D / 8;        // threads per token row (8 values each)
+  constexpr int RPI = 256 / TPR;    // token rows per iteration
+  __shared__ double red_k[RPI][D];
+  __shared__ float red_v[RPI][D];
+  const int tid = threadIdx.x;
+  const int col = (tid % TPR) * 8;
+  const int r0 = tid / TPR;
+  const int bh = blockIdx.y;
+  const int b = bh / H, h = bh % H;
+  const int64_t base = (int64_t)b * geo.batch_stride + (int64_t)h * geo.head_stride + col;
+  const int t_begin = blockIdx.x * kStatChunk;
+  const int t_end = min(N, t_begin + kStatChunk);
+
+  double ks[8];
+  float vm[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) { ks[e] = 0.0; vm[e] = 0.0f; }
+  for (int t = t_begin + r0; t < t_end; t += RPI) {
+    const int64_t off = base + (int64_t)t * geo.tok_stride;
+    if (WITH_K) {
+      i32x4 raw = *reinterpret_cast<const i32x4*>(k + off);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint16_t bits = (uint16_t)(((uint32_t)raw[e / 2]) >> (16 * (e & 1)));
+        ks[e] += (double)T::to_f32(bits);
+      }
+    }
+    if (WITH_V) {
+      i32x4 raw = *reinterpret_cast<const i32x4*>(v + off);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint16_t bits = (uint16_t)(((uint32_t)raw[e / 2]) >> (16 * (e & 1)));
+        vm[e] = fmaxf(vm[e], fabsf(T::to_f32(bits)));
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (WITH_K) red_k[r0][col + e] = ks[e];
+    if (WITH_V) red_v[r0][col + e] = vm[e];
+  }
+  __syncthreads();
+  if (tid < D) {
+    const int64_t o = ((int64_t)bh * chunks + blockIdx.x) * D + tid;
+    if (WITH_K) {
+      double s = 0.0;
+      for (int r = 0; r < RPI; ++r) s += red_k[r][tid];
+      ksum_part[o] = s;
+    }
+    if (WITH_V) {
+      float m = 0.0f;
+      for (int r = 0; r < RPI; ++r) m = fmaxf(m, red_v[r][tid]);
+      vmax_part[o] = m;
+    }
+  }
+}
+
+// Per (b, kv-head, channel): mu = fp32(sum / N) (fp64 divide, one rounding to
+// fp32); s_v = a_v / 448 and 448 / a_v (both correctly rounded fp32 divides).
+template <int D, bool WITH_K, bool WITH_V>
+__global__ __launch_bounds__(D) void channel_finalize_kernel(
+    int N, int chunks, const double* __restrict__ ksum_part, const float* __restrict__ vmax_part,
+    float* __restrict__ k_mean, float* __restrict__ v_scale, float* __restrict__ v_inv) {
+  const int bh = blockIdx.x, c = threadIdx.x;
+  const int64_t p = (int64_t)bh * chunks * D + c;
+  if (WITH_K) {
+    double s = 0.0;
+    for (int i = 0; i < chunks; ++i) s += ksum_part[p + (int64_t)i * D];
+    k_mean[bh * D + c] = (float)(s / (double)N);
+  }
+  if (WITH_V) {
+    float a = 0.0f;
+    for (int i = 0; i < chunks; ++i) a = fmaxf(a, vmax_part[p + (int64_t)i * D]);
+    v_scale[bh * D + c] = a / kE4m3Max;
+    v_inv[bh * D + c] = a > 0.0f ? kE4m3Max / a : 0.0f;
+  }
+}
+
+// One work-group per (b, head, block of BLK tokens): optional smoothing
+// x - mu[c], block absmax, s = a/127, codes = rne(x * (127/a)).
+template <typename T, int D, int BLK, bool SMOOTH>
+__global__ __launch_bounds__(256) void quant_int8_kernel(
+    const uint16_t* __restrict__ x, TensorGeom geo, int H, int N, int nblk,
+    const float* __restrict__ mean, int8_t* __restrict__ codes, float* __restrict__ scale) {
+  constexpr int TPR = D / 8;
+  constexpr int ITER = BLK * TPR / 256;   // 16-byte chunks per thread
+  static_assert(ITER * 256 == BLK * TPR, "block must tile the work-group");
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  const int col = (tid % TPR) * 8;        // 256 % TPR == 0: fixed per thread
+  const int bh = blockIdx.y;
+  const int b = bh / H, h = bh % H;
+  const int t0 = blockIdx.x * BLK;
+  const int64_t base = (int64_t)b * geo.batch_stride + (int64_t)h * geo.head_stride + col;
+
+  float mu[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) mu[e] = SMOOTH ? mean[bh * D + col + e] : 0.0f;
+
+  float val[ITER][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+    const int t = t0 + (it * 256 + tid) / TPR;
+    if (t < N) {
+      i32x4 raw = *reinterpret_cast<const i32x4*>(x + base + (int64_t)t * geo.tok_stride);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint16_t bits = (uint16_t)(((uint32_t)raw[e / 2]) >> (16 * (e & 1)));
+        float f = T::to_f32(bits);
+        if (SMOOTH) f = f - mu[e];
+        val[it][e] = f;
+        amax = fmaxf(amax, fabsf(f));
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) val[it][e] = 0.0f;
+    }
+  }
+  amax = wave_max(amax);
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
+  if (tid == 0) scale[(int64_t)bh * nblk + blockIdx.x] = amax / 127.0f;
+
+  int8_t* out = codes + (int64_t)bh * N * D + col;
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+    const int t = t0 + (it * 256 + tid) / TPR;
+    if (t < N) {
+      uint32_t w[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float prod = val[it][e] * inv;
+        const int q = (int)__builtin_rintf(prod);
+        w[e / 4] |= ((uint32_t)(q & 0xff)) << (8 * (e & 3));
+      }
+      *reinterpret_cast<i32x2*>(out + (int64_t)t * D) = i32x2{(int)w[0], (int)w[1]};
+    }
+  }
+}
+
+// One work-group per (b, kv-head, 64-token tile): V transposed to
+// [D][Nk_pad] with keys contiguous per channel. FP8: e4m3(v * (448/a_v[c]));
+// otherwise the 16-bit values are copied. Tokens >= N are written as 0.
+template <typename T, int D, bool FP8>
+__global__ __launch_bounds__(256) void transpose_v_kernel(
+    const uint16_t* __restrict__ v, TensorGeom geo, int H, int N, int n_pad,
+    const float* __restrict__ v_inv, void* __restrict__ out) {
+  constexpr int EB = FP8 ? 1 : 2;               // output bytes per element
+  constexpr int ROWB = 64 * EB;                 // bytes per channel row of the tile
+  constexpr int UNITS = (64 / 4) * (D / 8);     // 4 tokens x 8 channels per unit
+  __shared__ __attribute__((aligned(16))) uint8_t tile[D * ROWB];
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.y;
+  const int b = bh / H, h = bh % H;
+  const int t0 = blockIdx.x * 64;
+  const int64_t base = (int64_t)b * geo.batch_stride + (int64_t)h * geo.head_stride;
+
+  for (int u = tid; u < UNITS; u += 256) {
+    const int c0 = (u % (D / 8)) * 8;
+    const int tt = (u / (D / 8)) * 4;           // first token of the unit inside the tile
+    uint32_t raw16[4][8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = t0 + tt + j;
+      if (t < N) {
+        i32x4 raw = *reinterpret_cast<const i32x4*>(v + base + (int64_t)t * geo.tok_stride + c0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) raw16[j][e] = (((uint32_t)raw[e / 2]) >> (16 * (e & 1))) & 0xffffu;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) raw16[j][e] = 0u;   // +0.0 in both dtypes and in e4m3
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = c0 + e;
+      if (FP8) {
+        const float s = v_inv[bh * D + c];
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(T::to_f32((uint16_t)raw16[0][e]) * s,
+                                                T::to_f32((uint16_t)raw16[1][e]) * s, 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(T::to_f32((uint16_t)raw16[2][e]) * s,
+                                            T::to_f32((uint16_t)raw16[3][e]) * s, w, true);
+        *reinterpret_cast<int*>(tile + c * ROWB + tt) = w;
+      } else {
+        const uint32_t lo = raw16[0][e] | (raw16[1][e] << 16);
+        const uint32_t hi = raw16[2][e] | (raw16[3][e] << 16);
+        *reinterpret_cast<i32x2*>(tile + c * ROWB + tt * 2) = i32x2{(int)lo, (int)hi};
+      }
+    }
+  }
+  __syncthreads();
+  uint8_t* dst = reinterpret_cast<uint8_t*>(out) + ((int64_t)bh * D * n_pad + t0) * EB;
+  constexpr int CHUNKS = D * ROWB / 16;
+  for (int ci = tid; ci < CHUNKS; ci += 256) {
+    const int c = ci / (ROWB / 16), j = ci % (ROWB / 16);
+    *reinterpret_cast<i32x4*>(dst + (int64_t)c * n_pad * EB + j * 16) =
+        *reinterpret_cast<const i32x4*>(tile + c * ROWB + j * 16);
+  }
+}
+
+// ---------------------------------------------------------------- host launchers
+template <typename T, int D>
+static hipError_t launch_qk_t(const QuantQKArgs& a, hipStream_t st) {
+  const int chunks = (a.Nk + kStatChunk - 1) / kStatChunk;
+  const int bhk = a.B * a.Hkv;
+  if (a.Nk > 0) {
+    hipLaunchKernelGGL((channel_stats_kernel<T, D, true, false>), dim3(chunks, bhk), dim3(256), 0, st,
+                       (const uint16_t*)a.k, (const uint16_t*)nullptr, a.kgeo, a.Hkv, a.Nk, chunks,
+                       a.ksum_part, (float*)nullptr);
+    hipLaunchKernelGGL((channel_finalize_kernel<D, true, false>), dim3(bhk), dim3(D), 0, st,
+                       a.Nk, chunks, a.ksum_part, (const float*)nullptr, a.k_mean, (float*)nullptr,
+                       (float*)nullptr);
+    const int nbk = (a.Nk + kBlkK - 1) / kBlkK;
+    hipLaunchKernelGGL((quant_int8_kernel<T, D, kBlkK, true>), dim3(nbk, bhk), dim3(256), 0, st,
+                       (const uint16_t*)a.k, a.kgeo, a.Hkv, a.Nk, nbk, a.k_mean, a.k_codes, a.k_scale);
+  }
+  if (a.Nq > 0) {
+    const int nbq = (a.Nq + kBlkQ - 1) / kBlkQ;
+    hipLaunchKernelGGL((quant_int8_kernel<T, D, kBlkQ, false>), dim3(nbq, a.B * a.Hq), dim3(256), 0, st,
+                       (const uint16_t*)a.q, a.qgeo, a.Hq, a.Nq, nbq, (const float*)nullptr, a.q_codes,
+                       a.q_scale);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_qk(const QuantQKArgs& a, hipStream_t st) {
+  if (a.bf16) return a.D == 64 ? launch_qk_t<BF16, 64>(a, st) : launch_qk_t<BF16, 128>(a, st);
+  return a.D == 64 ? launch_qk_t<F16, 64>(a, st) : launch_qk_t<F16, 128>(a, st);
+}
+
+template <typename T, int D>
+static hipError_t launch_v_t(const QuantVArgs& a, hipStream_t st) {
+  const int bhk = a.B * a.Hkv;
+  const int tiles = a.n_pad / 64;
+  if (a.fp8) {
+    const int chunks = (a.Nk + kStatChunk - 1) / kStatChunk;
+    hipLaunchKernelGGL((channel_stats_kernel<T, D, false, true>), dim3(chunks, bhk), dim3(256), 0, st,
+                       (const uint16_t*)nullptr, (const uint16_t*)a.v, a.vgeo, a.Hkv, a.Nk, chunks,
+                       (double*)nullptr, a.vmax_part);
+    hipLaunchKernelGGL((channel_finalize_kernel<D, false, true>), dim3(bhk), dim3(D), 0, st,
+                       a.Nk, chunks, (const double*)nullptr, a.vmax_part, (float*)nullptr, a.v_scale,
+                       a.v_inv);
+    hipLaunchKernelGGL((transpose_v_kernel<T, D, true>), dim3(tiles, bhk), dim3(256), 0, st,
+                       (const uint16_t*)a.v, a.vgeo, a.Hkv, a.Nk, a.n_pad, (const float*)a.v_inv, a.out);
+  } else {
+    hipLaunchKernelGGL((transpose_v_kernel<T, D, false>), dim3(tiles, bhk), dim3(256), 0, st,
+                       (const uint16_t*)a.v, a.vgeo, a.Hkv, a.Nk, a.n_pad, (const float*)nullptr, a.out);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_v(const QuantVArgs& a, hipStream_t st) {
+  if (a.bf16) return a.D == 64 ? launch_v_t<BF16, 64>(a, st) : launch_v_t<BF16, 128>(a, st);
+  return a.D == 64 ? launch_v_t<F16, 64>(a, st) : launch_v_t<F16, 128>(a, st);
+}
+
+}  // namespace sage

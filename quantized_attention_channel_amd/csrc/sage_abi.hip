@@ -1,0 +1,305 @@
+// C-ABI front end of libsage: argument validation, workspace layout, launches.
+//
+// Every entry point validates all arguments on the host before it makes any
+// HIP call, so an invalid request enqueues nothing; this also lets the
+// validation be exercised on a machine without a GPU.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "sage.h"
+#include "sage_device.h"
+#include "sage_launch.h"
+
+namespace {
+
+using sage::TensorGeom;
+
+constexpr int kStatChunk = 256;
+constexpr int64_t kMaxSeq = int64_t(1) << 20;
+
+struct Dims {
+  int64_t B, Hq, Hkv, Nq, Nk, D;
+  bool nhd, bf16;
+};
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Shape checks common to every entry point. `need_keys`: Nk must be > 0 when Nq > 0.
+sage_status check_shape(const sage_shape* s, Dims* d) {
+  if (!s) return SAGE_ERR_INVALID_ARGUMENT;
+  if (s->layout != SAGE_LAYOUT_HND && s->layout != SAGE_LAYOUT_NHD) return SAGE_ERR_INVALID_ARGUMENT;
+  if (s->dtype != SAGE_DTYPE_F16 && s->dtype != SAGE_DTYPE_BF16) return SAGE_ERR_INVALID_ARGUMENT;
+  if (s->batch < 0 || s->heads_q < 1 || s->heads_kv < 1 || s->seq_q < 0 || s->seq_k < 0 || s->head_dim < 1)
+    return SAGE_ERR_INVALID_ARGUMENT;
+  if (s->heads_q % s->heads_kv != 0) return SAGE_ERR_INVALID_ARGUMENT;
+  if (s->seq_q > kMaxSeq || s->seq_k > kMaxSeq) return SAGE_ERR_INVALID_ARGUMENT;
+  if (s->head_dim != 64 && s->head_dim != 128) return SAGE_ERR_UNSUPPORTED;
+  d->B = s->batch;
+  d->Hq = s->heads_q;
+  d->Hkv = s->heads_kv;
+  d->Nq = s->seq_q;
+  d->Nk = s->seq_k;
+  d->D = s->head_dim;
+  d->nhd = s->layout == SAGE_LAYOUT_NHD;
+  d->bf16 = s->dtype == SAGE_DTYPE_BF16;
+  // grid and buffer-offset limits: (b, head) pairs fit a grid dimension,
+  // per-head slices fit a 32-bit byte offset
+  if (d->B * d->Hq > (int64_t(1) << 24)) return SAGE_ERR_INVALID_ARGUMENT;
+  return SAGE_OK;
+}
+
+TensorGeom geom(const Dims& d, int64_t H, int64_t N) {
+  TensorGeom g;
+  if (d.nhd) {
+    g.batch_stride = N * H * d.D;
+    g.head_stride = d.D;
+    g.tok_stride = H * d.D;
+  } else {
+    g.batch_stride = H * N * d.D;
+    g.head_stride = N * d.D;
+    g.tok_stride = d.D;
+  }
+  return g;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+// Workspace layout (each region 256-byte aligned), shared by all entry points.
+struct Layout {
+  size_t q_codes, q_scale, k_codes, k_scale, k_mean, vt, v_scale, v_inv, ksum, vmax, total;
+};
+
+Layout layout_for(const Dims& d, bool fp8) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  const int64_t nbq = cdiv(d.Nq, sage::kBlkQ), nbk = cdiv(d.Nk, sage::kBlkK);
+  const int64_t npad = round_up(d.Nk, sage::kVPad);
+  const int64_t chunks = cdiv(d.Nk, kStatChunk);
+  L.q_codes = take(size_t(d.B * d.Hq * d.Nq * d.D));
+  L.q_scale = take(size_t(d.B * d.Hq * nbq) * 4);
+  L.k_codes = take(size_t(d.B * d.Hkv * d.Nk * d.D));
+  L.k_scale = take(size_t(d.B * d.Hkv * nbk) * 4);
+  L.k_mean = take(size_t(d.B * d.Hkv * d.D) * 4);
+  L.vt = take(size_t(d.B * d.Hkv * d.D * npad) * (fp8 ? 1 : 2));
+  L.v_scale = take(size_t(d.B * d.Hkv * d.D) * 4);
+  L.v_inv = take(size_t(d.B * d.Hkv * d.D) * 4);
+  L.ksum = take(size_t(d.B * d.Hkv * chunks * d.D) * 8);
+  L.vmax = take(size_t(d.B * d.Hkv * chunks * d.D) * 4);
+  L.total = off;
+  return L;
+}
+
+size_t qk_ws_bytes(const Dims& d) { return align256(size_t(d.B * d.Hkv * cdiv(d.Nk, kStatChunk) * d.D) * 8); }
+size_t v_ws_bytes(const Dims& d) {
+  return align256(size_t(d.B * d.Hkv * d.D) * 4) + align256(size_t(d.B * d.Hkv * cdiv(d.Nk, kStatChunk) * d.D) * 4);
+}
+
+template <typename P>
+P* at(void* base, size_t off) { return reinterpret_cast<P*>(static_cast<uint8_t*>(base) + off); }
+
+sage_status from_hip(hipError_t e) { return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+sage_status sage_block_sizes(int32_t head_dim, int32_t* blk_q, int32_t* blk_k, int32_t* bkv) {
+  if (head_dim != 64 && head_dim != 128) return SAGE_ERR_UNSUPPORTED;
+  if (blk_q) *blk_q = sage::kBlkQ;
+  if (blk_k) *blk_k = sage::kBlkK;
+  if (bkv) *bkv = sage::kBkv;
+  return SAGE_OK;
+}
+
+int64_t sage_v_codes_stride(int32_t seq_k) { return seq_k <= 0 ? 0 : round_up(seq_k, sage::kVPad); }
+
+size_t sage_quant_qk_workspace_bytes(const sage_shape* s) {
+  Dims d;
+  return check_shape(s, &d) == SAGE_OK ? qk_ws_bytes(d) : 0;
+}
+
+size_t sage_quant_v_workspace_bytes(const sage_shape* s) {
+  Dims d;
+  return check_shape(s, &d) == SAGE_OK ? v_ws_bytes(d) : 0;
+}
+
+size_t sage_workspace_bytes(const sage_shape* s, int32_t pv_dtype) {
+  Dims d;
+  if (check_shape(s, &d) != SAGE_OK) return 0;
+  if (pv_dtype != SAGE_PV_FP16 && pv_dtype != SAGE_PV_FP8_E4M3) return 0;
+  return layout_for(d, pv_dtype == SAGE_PV_FP8_E4M3).total;
+}
+
+sage_status sage_quant_qk(const sage_shape* s, const void* q, const void* k, int8_t* q_codes, float* q_scale,
+                          int8_t* k_codes, float* k_scale, float* k_mean, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  Dims d;
+  sage_status st = check_shape(s, &d);
+  if (st != SAGE_OK) return st;
+  if (d.B == 0 || (d.Nq == 0 && d.Nk == 0)) return SAGE_OK;
+  const bool has_q = d.Nq > 0, has_k = d.Nk > 0;
+  if (has_q && (!q || !q_codes || !q_scale)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (has_k && (!k || !k_codes || !k_scale || !k_mean)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (has_q && (!aligned(q, 16) || !aligned(q_codes, 16) || !aligned(q_scale, 4))) return SAGE_ERR_INVALID_ARGUMENT;
+  if (has_k && (!aligned(k, 16) || !aligned(k_codes, 16) || !aligned(k_scale, 4) || !aligned(k_mean, 4)))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  if (has_k) {
+    if (!workspace || !aligned(workspace, 256)) return SAGE_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < qk_ws_bytes(d)) return SAGE_ERR_WORKSPACE;
+  }
+  sage::QuantQKArgs a{};
+  a.q = q;
+  a.k = k;
+  a.qgeo = geom(d, d.Hq, d.Nq);
+  a.kgeo = geom(d, d.Hkv, d.Nk);
+  a.B = int(d.B), a.Hq = int(d.Hq), a.Hkv = int(d.Hkv), a.Nq = int(d.Nq), a.Nk = int(d.Nk), a.D = int(d.D);
+  a.bf16 = d.bf16;
+  a.q_codes = q_codes;
+  a.q_scale = q_scale;
+  a.k_codes = k_codes;
+  a.k_scale = k_scale;
+  a.k_mean = k_mean;
+  a.ksum_part = static_cast<double*>(workspace);
+  return from_hip(sage::launch_quant_qk(a, static_cast<hipStream_t>(stream)));
+}
+
+sage_status sage_quant_v(const sage_shape* s, const void* v, uint8_t* v_codes, float* v_scale, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  Dims d;
+  sage_status st = check_shape(s, &d);
+  if (st != SAGE_OK) return st;
+  if (d.B == 0 || d.Nk == 0) return SAGE_OK;
+  if (!v || !v_codes || !v_scale || !workspace) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!aligned(v, 16) || !aligned(v_codes, 16) || !aligned(v_scale, 4) || !aligned(workspace, 256))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < v_ws_bytes(d)) return SAGE_ERR_WORKSPACE;
+  sage::QuantVArgs a{};
+  a.v = v;
+  a.vgeo = geom(d, d.Hkv, d.Nk);
+  a.B = int(d.B), a.Hkv = int(d.Hkv), a.Nk = int(d.Nk), a.D = int(d.D);
+  a.n_pad = int(round_up(d.Nk, sage::kVPad));
+  a.bf16 = d.bf16;
+  a.fp8 = true;
+  a.out = v_codes;
+  a.v_scale = v_scale;
+  a.v_inv = static_cast<float*>(workspace);
+  a.vmax_part = at<float>(workspace, align256(size_t(d.B * d.Hkv * d.D) * 4));
+  return from_hip(sage::launch_quant_v(a, static_cast<hipStream_t>(stream)));
+}
+
+sage_status sage_attn_fwd(const sage_shape* s, const void* q, const void* k, const void* v, void* o,
+                          int32_t is_causal, float sm_scale, int32_t pv_dtype, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  Dims d;
+  sage_status st = check_shape(s, &d);
+  if (st != SAGE_OK) return st;
+  if (pv_dtype != SAGE_PV_FP16 && pv_dtype != SAGE_PV_FP8_E4M3) return SAGE_ERR_INVALID_ARGUMENT;
+  if (is_causal != 0 && is_causal != 1) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (d.B == 0 || d.Nq == 0) return SAGE_OK;
+  if (d.Nk == 0) return SAGE_ERR_INVALID_ARGUMENT;
+  if (is_causal && d.Nq != d.Nk) return SAGE_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !o || !workspace) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(workspace, 256))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  const bool fp8 = pv_dtype == SAGE_PV_FP8_E4M3;
+  const Layout L = layout_for(d, fp8);
+  if (workspace_bytes < L.total) return SAGE_ERR_WORKSPACE;
+  const size_t qbytes = size_t(d.B * d.Hq * d.Nq * d.D) * 2, kvbytes = size_t(d.B * d.Hkv * d.Nk * d.D) * 2;
+  if (overlaps(o, qbytes, q, qbytes) || overlaps(o, qbytes, k, kvbytes) || overlaps(o, qbytes, v, kvbytes) ||
+      overlaps(o, qbytes, workspace, L.total))
+    return SAGE_ERR_INVALID_ARGUMENT;
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  sage::QuantQKArgs qa{};
+  qa.q = q;
+  qa.k = k;
+  qa.qgeo = geom(d, d.Hq, d.Nq);
+  qa.kgeo = geom(d, d.Hkv, d.Nk);
+  qa.B = int(d.B), qa.Hq = int(d.Hq), qa.Hkv = int(d.Hkv), qa.Nq = int(d.Nq), qa.Nk = int(d.Nk), qa.D = int(d.D);
+  qa.bf16 = d.bf16;
+  qa.q_codes = at<int8_t>(workspace, L.q_codes);
+  qa.q_scale = at<float>(workspace, L.q_scale);
+  qa.k_codes = at<int8_t>(workspace, L.k_codes);
+  qa.k_scale = at<float>(workspace, L.k_scale);
+  qa.k_mean = at<float>(workspace, L.k_mean);
+  qa.ksum_part = at<double>(workspace, L.ksum);
+  hipError_t e = sage::launch_quant_qk(qa, hs);
+  if (e != hipSuccess) return SAGE_ERR_HIP;
+
+  sage::QuantVArgs va{};
+  va.v = v;
+  va.vgeo = geom(d, d.Hkv, d.Nk);
+  va.B = int(d.B), va.Hkv = int(d.Hkv), va.Nk = int(d.Nk), va.D = int(d.D);
+  va.n_pad = int(round_up(d.Nk, sage::kVPad));
+  va.bf16 = d.bf16;
+  va.fp8 = fp8;
+  va.out = at<void>(workspace, L.vt);
+  va.v_scale = at<float>(workspace, L.v_scale);
+  va.v_inv = at<float>(workspace, L.v_inv);
+  va.vmax_part = at<float>(workspace, L.vmax);
+  e = sage::launch_quant_v(va, hs);
+  if (e != hipSuccess) return SAGE_ERR_HIP;
+
+  sage::AttnArgs aa{};
+  aa.q8 = qa.q_codes;
+  aa.q_scale = qa.q_scale;
+  aa.k8 = qa.k_codes;
+  aa.k_scale = qa.k_scale;
+  aa.vt = va.out;
+  aa.v_scale = va.v_scale;
+  aa.o = o;
+  aa.ogeo = geom(d, d.Hq, d.Nq);
+  aa.B = int(d.B), aa.Hq = int(d.Hq), aa.Hkv = int(d.Hkv), aa.Nq = int(d.Nq), aa.Nk = int(d.Nk), aa.D = int(d.D);
+  aa.n_pad = va.n_pad;
+  aa.nbq = int(cdiv(d.Nq, sage::kBlkQ));
+  aa.nbk = int(cdiv(d.Nk, sage::kBlkK));
+  aa.scale_log2 = sm_scale * sage::kLog2E;
+  aa.causal = is_causal != 0;
+  aa.bf16 = d.bf16;
+  aa.fp8 = fp8;
+  return from_hip(sage::launch_attn(aa, hs));
+}
+
+sage_status sage_debug_qk_i32(const sage_shape* s, const int8_t* q_codes, const int8_t* k_codes, int32_t* s_out,
+                              void* stream) {
+  Dims d;
+  sage_status st = check_shape(s, &d);
+  if (st != SAGE_OK) return st;
+  if (d.B == 0 || d.Nq == 0 || d.Nk == 0) return SAGE_OK;
+  if (!q_codes || !k_codes || !s_out) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(s_out, 4)) return SAGE_ERR_INVALID_ARGUMENT;
+  sage::DebugQKArgs a{};
+  a.q8 = q_codes;
+  a.k8 = k_codes;
+  a.s_out = s_out;
+  a.B = int(d.B), a.Hq = int(d.Hq), a.Hkv = int(d.Hkv), a.Nq = int(d.Nq), a.Nk = int(d.Nk), a.D = int(d.D);
+  return from_hip(sage::launch_debug_qk(a, static_cast<hipStream_t>(stream)));
+}
+
+const char* sage_status_string(sage_status st) {
+  switch (st) {
+    case SAGE_OK: return "SAGE_OK";
+    case SAGE_ERR_INVALID_ARGUMENT: return "SAGE_ERR_INVALID_ARGUMENT: invalid pointer, size, alignment or enum";
+    case SAGE_ERR_UNSUPPORTED: return "SAGE_ERR_UNSUPPORTED: head_dim must be 64 or 128; causal needs seq_q == seq_k";
+    case SAGE_ERR_WORKSPACE: return "SAGE_ERR_WORKSPACE: workspace smaller than the size query reports";
+    case SAGE_ERR_HIP: return "SAGE_ERR_HIP: the HIP runtime rejected a launch";
+  }
+  return "unknown sage_status";
+}
+
+}  // extern "C"

@@ -1,0 +1,69 @@
+// Internal (C++) interface between the C-ABI front end and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sage {
+
+// Element strides of a [B, H, N, d] tensor in either user layout
+// (HND: token stride d; NHD: token stride H*d). The channel stride is 1.
+struct TensorGeom {
+  int64_t batch_stride;
+  int64_t head_stride;
+  int64_t tok_stride;
+};
+
+struct QuantQKArgs {
+  const void* q;
+  const void* k;
+  TensorGeom qgeo, kgeo;
+  int B, Hq, Hkv, Nq, Nk, D;
+  bool bf16;
+  int8_t* q_codes;
+  float* q_scale;
+  int8_t* k_codes;
+  float* k_scale;
+  float* k_mean;
+  double* ksum_part;   // [B*Hkv][ceil(Nk/256)][D]
+};
+
+struct QuantVArgs {
+  const void* v;
+  TensorGeom vgeo;
+  int B, Hkv, Nk, n_pad, D;
+  bool bf16, fp8;
+  void* out;           // FP8: e4m3 codes [B*Hkv][D][n_pad]; else 16-bit V^T [B*Hkv][D][n_pad]
+  float* v_scale;      // FP8 only
+  float* v_inv;        // FP8 only (448 / a_v)
+  float* vmax_part;    // FP8 only: [B*Hkv][ceil(Nk/256)][D]
+};
+
+struct AttnArgs {
+  const int8_t* q8;     // [B*Hq][Nq][D]
+  const float* q_scale; // [B*Hq][nbq]
+  const int8_t* k8;     // [B*Hkv][Nk][D]
+  const float* k_scale; // [B*Hkv][nbk]
+  const void* vt;       // [B*Hkv][D][n_pad]: e4m3 codes or 16-bit V^T
+  const float* v_scale; // [B*Hkv][D] (FP8 only)
+  void* o;
+  TensorGeom ogeo;
+  int B, Hq, Hkv, Nq, Nk, n_pad, D;
+  int nbq, nbk;
+  float scale_log2;     // sm_scale * log2(e)
+  bool causal, bf16, fp8;
+};
+
+struct DebugQKArgs {
+  const int8_t* q8;
+  const int8_t* k8;
+  int32_t* s_out;       // [B*Hq][Nq][Nk]
+  int B, Hq, Hkv, Nq, Nk, D;
+};
+
+hipError_t launch_quant_qk(const QuantQKArgs& a, hipStream_t st);
+hipError_t launch_quant_v(const QuantVArgs& a, hipStream_t st);
+hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
+hipError_t launch_debug_qk(const DebugQKArgs& a, hipStream_t st);
+
+}  // namespace sage

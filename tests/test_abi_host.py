@@ -1,0 +1,162 @@
+"""Host-side checks of the C ABI (CPU only, no GPU needed).
+
+The library loads on a machine without a GPU, exports every function the header
+declares, and rejects every invalid request on the host with the documented
+status before making any HIP call (fake device addresses are therefore safe
+here: validation never dereferences them).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import quantized_attention_channel_amd as sage
+from oracle import sage_ref
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sage.h")
+
+FAKE = 0x7F0000000000          # a 256-byte aligned address that is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sage_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("sage_quant_qk", "sage_quant_v", "sage_attn_fwd", "sage_workspace_bytes",
+              "sage_block_sizes", "sage_status_string", "sage_debug_qk_i32"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", sage.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (sage_[a-z0-9_]+)$", out, flags=re.M))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    for n in declared_functions():
+        getattr(sage.lib, n)                        # dlsym succeeds
+
+
+def test_binding_covers_the_header():
+    assert set(declared_functions()) == set(sage._SIGNATURES)
+
+
+def test_block_sizes_match_the_oracle_readings():
+    for d in (64, 128):
+        assert sage.sage_block_sizes(d) == (sage_ref.BLK_Q, sage_ref.BLK_K, sage_ref.BKV[d])
+    with pytest.raises(sage.SageError) as e:
+        sage.sage_block_sizes(96)
+    assert e.value.status == sage.SAGE_ERR_UNSUPPORTED
+    assert sage.lib.sage_block_sizes(64, None, None, None) == sage.SAGE_OK
+
+
+def test_status_strings():
+    for st in range(5):
+        assert sage.lib.sage_status_string(st)
+    assert b"unknown" in sage.lib.sage_status_string(99)
+
+
+def test_v_codes_stride():
+    assert sage.sage_v_codes_stride(0) == 0
+    assert sage.sage_v_codes_stride(1) == 64
+    assert sage.sage_v_codes_stride(64) == 64
+    assert sage.sage_v_codes_stride(65) == 128
+
+
+def _shape(**kw):
+    base = dict(B=2, Hq=4, Hkv=2, Nq=300, Nk=300, d=128, layout="HND")
+    base.update(kw)
+    return sage.make_shape(base["B"], base["Hq"], base["Hkv"], base["Nq"], base["Nk"], base["d"], base["layout"])
+
+
+def test_workspace_size_grows_with_the_problem():
+    s = _shape()
+    w8, w16 = sage.sage_workspace_bytes(s, "fp8"), sage.sage_workspace_bytes(s, "fp16")
+    codes = 2 * 4 * 300 * 128 + 2 * 2 * 300 * 128
+    assert w8 >= codes + 2 * 2 * 128 * 320 and w16 >= codes + 2 * 2 * 128 * 320 * 2
+    assert w8 % 256 == 0 and w16 % 256 == 0
+    assert sage.sage_workspace_bytes(_shape(Nq=600, Nk=600), "fp8") > w8
+    assert sage.lib.sage_workspace_bytes(None, 1) == 0
+    assert sage.lib.sage_workspace_bytes(ctypes.byref(s), 7) == 0
+    assert sage.lib.sage_workspace_bytes(ctypes.byref(_shape(d=96)), 1) == 0
+
+
+def _attn(shape, q=FAKE, k=FAKE + 2 ** 30, v=FAKE + 2 ** 31, o=FAKE + 3 * 2 ** 30, causal=0, scale=0.1,
+          pv=1, ws=FAKE + 2 ** 33, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = sage.lib.sage_workspace_bytes(ctypes.byref(shape), pv) if shape is not None else 0
+    sp = None if shape is None else ctypes.byref(shape)
+    return sage.lib.sage_attn_fwd(sp, q, k, v, o, causal, scale, pv, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,kw,want", [
+    ("null shape", dict(shape=None), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("Hq % Hkv", dict(shape=_shape(Hq=3, Hkv=2)), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("bad layout", dict(shape=sage.SageShape(1, 1, 1, 8, 8, 64, 5, 0)), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("bad dtype", dict(shape=sage.SageShape(1, 1, 1, 8, 8, 64, 0, 9)), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("negative seq", dict(shape=_shape(Nq=-1)), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("too long", dict(shape=_shape(Nq=(1 << 20) + 1, Nk=(1 << 20) + 1)), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("head dim 96", dict(shape=_shape(d=96)), sage.SAGE_ERR_UNSUPPORTED),
+    ("causal Nq != Nk", dict(shape=_shape(Nq=100, Nk=300), causal=1), sage.SAGE_ERR_UNSUPPORTED),
+    ("causal flag 2", dict(shape=_shape(), causal=2), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("sm_scale nan", dict(shape=_shape(), scale=float("nan")), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("sm_scale 0", dict(shape=_shape(), scale=0.0), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("sm_scale inf", dict(shape=_shape(), scale=float("inf")), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("bad pv", dict(shape=_shape(), pv=3), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("null q", dict(shape=_shape(), q=None), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("null o", dict(shape=_shape(), o=None), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("null workspace", dict(shape=_shape(), ws=None), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("misaligned q", dict(shape=_shape(), q=FAKE + 8), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("misaligned ws", dict(shape=_shape(), ws=FAKE + 2 ** 33 + 64), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("small workspace", dict(shape=_shape(), ws_bytes=1024), sage.SAGE_ERR_WORKSPACE),
+    ("o aliases q", dict(shape=_shape(), o=FAKE + 4096), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("o aliases workspace", dict(shape=_shape(), o=FAKE + 2 ** 33 + 256), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("no keys", dict(shape=_shape(Nk=0)), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("no queries is a no-op", dict(shape=_shape(Nq=0), q=None, o=None), sage.SAGE_OK),
+    ("empty batch is a no-op", dict(shape=_shape(B=0)), sage.SAGE_OK),
+])
+def test_attn_fwd_validation(case, kw, want):
+    assert _attn(**kw) == want, case
+
+
+def test_quant_entry_points_validate():
+    s = _shape()
+    sp = ctypes.byref(s)
+    ws = FAKE + 2 ** 33
+    ok_ws = sage.lib.sage_quant_qk_workspace_bytes(sp)
+    assert ok_ws > 0
+    # null outputs, misalignment, small workspace
+    assert sage.lib.sage_quant_qk(sp, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, ws, ok_ws, None) == \
+        sage.SAGE_ERR_INVALID_ARGUMENT
+    assert sage.lib.sage_quant_qk(sp, FAKE, FAKE, FAKE, FAKE + 2, FAKE, FAKE, FAKE, ws, ok_ws, None) == \
+        sage.SAGE_ERR_INVALID_ARGUMENT
+    assert sage.lib.sage_quant_qk(sp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, 16, None) == \
+        sage.SAGE_ERR_WORKSPACE
+    vws = sage.lib.sage_quant_v_workspace_bytes(sp)
+    assert vws > 0
+    assert sage.lib.sage_quant_v(sp, FAKE, None, FAKE, ws, vws, None) == sage.SAGE_ERR_INVALID_ARGUMENT
+    assert sage.lib.sage_quant_v(sp, FAKE, FAKE, FAKE, ws, 16, None) == sage.SAGE_ERR_WORKSPACE
+    assert sage.lib.sage_quant_v(ctypes.byref(_shape(d=32)), FAKE, FAKE, FAKE, ws, vws, None) == \
+        sage.SAGE_ERR_UNSUPPORTED
+    assert sage.lib.sage_debug_qk_i32(sp, None, FAKE, FAKE, None) == sage.SAGE_ERR_INVALID_ARGUMENT
+    assert sage.lib.sage_debug_qk_i32(sp, FAKE + 1, FAKE, FAKE, None) == sage.SAGE_ERR_INVALID_ARGUMENT
+
+
+def test_python_wrapper_rejects_unsupported_sdpa_arguments():
+    import torch
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.float16)
+    with pytest.raises(NotImplementedError):
+        sage.sageattn(q, q, q, attn_mask=torch.ones(4, 4))
+    with pytest.raises(NotImplementedError):
+        sage.sageattn(q, q, q, dropout_p=0.1)
+    with pytest.raises(TypeError):
+        sage.sageattn(q, q, q, bogus=1)
+    with pytest.raises(ValueError):                       # CPU tensors never reach the library
+        sage.sageattn(q, q, q)

@@ -1,0 +1,233 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+* Integer and code stages are bit-exact: K channel means, Q/K INT8 codes and
+  scales, V e4m3 codes (including padding) and scales, INT32 QK^T from the
+  attention kernel's own matrix-core tile code.
+* The float output meets the method's bar against the oracle (cosine >= 0.9999,
+  sum|o-r|/sum|r| <= 1e-3) and against fp64 exact attention (cosine >= 0.999;
+  on the outlier workload the per-block INT8 reading bounds the method itself
+  near 0.998, so that case is held to the method's own bound).
+* Small cases run the oracle on every row; the five full-size workloads run the
+  HIP path in the configuration the benchmark times and compare sampled rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import exact, sage_ref
+from tests.parity_util import COS_EXACT, COS_ORACLE, RL1_ORACLE, cos, rel_l1, say, worst_head_cos
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+if torch.cuda.is_available():
+    import quantized_attention_channel_amd as sage
+
+
+def _cpu(x):
+    return x.detach().cpu()
+
+
+def _np_inputs(q, k, v, layout):
+    return tuple(sage_ref.as_hnd(t.float().numpy(), layout) for t in (q, k, v))
+
+
+def _gpu(*ts):
+    return tuple(t.cuda() for t in ts)
+
+
+# ------------------------------------------------------------------ quantisation stages
+QUANT_CASES = [
+    W.TINY,
+    W.TINY.with_(B=2, Hq=4, Hkv=2, N=333, d=128, dtype="bf16", layout="NHD"),
+    W.TINY.with_(B=1, Hq=3, Hkv=3, N=1, d=64),
+    W.TINY.with_(B=2, Hq=2, Hkv=1, N=1000, d=64, dtype="bf16", k_off_var=50.0),
+    W.MID_OUTLIER.with_(B=1, Hq=2, Hkv=2, N=777),
+]
+
+
+@pytest.mark.parametrize("w", QUANT_CASES, ids=[f"{w.B}x{w.Hq}x{w.N}x{w.d}{w.dtype}{w.layout}" for w in QUANT_CASES])
+def test_quant_qk_bit_exact(w):
+    say("quant_qk", w)
+    q, k, v = W.generate(w)
+    got = sage.sage_quant_qk(*_gpu(q, k), tensor_layout=w.layout)
+    torch.cuda.synchronize()
+    qn, kn, _ = _np_inputs(q, k, v, w.layout)
+    ref = sage_ref.quant_qk(qn, kn)
+    assert np.array_equal(_cpu(got["k_mean"]).numpy(), ref["k_mean"])
+    assert np.array_equal(_cpu(got["q_scale"]).numpy(), ref["q_scale"])
+    assert np.array_equal(_cpu(got["k_scale"]).numpy(), ref["k_scale"])
+    assert np.array_equal(_cpu(got["q_codes"]).numpy(), ref["q8"])
+    assert np.array_equal(_cpu(got["k_codes"]).numpy(), ref["k8"])
+
+
+@pytest.mark.parametrize("w", QUANT_CASES, ids=[f"{w.B}x{w.Hq}x{w.N}x{w.d}{w.dtype}{w.layout}" for w in QUANT_CASES])
+def test_quant_v_bit_exact(w):
+    say("quant_v", w)
+    q, k, v = W.generate(w)
+    codes, scale = sage.sage_quant_v(v.cuda(), tensor_layout=w.layout)
+    torch.cuda.synchronize()
+    _, _, vn = _np_inputs(q, k, v, w.layout)
+    rc, rs = sage_ref.quant_v_fp8(vn)
+    codes = _cpu(codes).numpy()
+    assert np.array_equal(_cpu(scale).numpy(), rs)
+    assert np.array_equal(codes[..., :w.N], rc)
+    assert not codes[..., w.N:].any()                  # padding keys are zero codes
+
+
+def test_fp8_conversion_ties_and_extremes():
+    """V built so that V * (448 / a_v) hits e4m3 rounding midpoints exactly."""
+    from oracle.fp8_e4m3 import e4m3_decode
+    vals = e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = (vals[1:] + vals[:-1]) / 2                  # exact in fp16 (<= 5 significant bits)
+    col = np.concatenate([[448.0], vals, mids, -mids, [-0.0]])
+    n = len(col)
+    v = torch.from_numpy(np.stack([col, col[::-1].copy()], axis=1)).to(torch.float16)  # [n, 2]
+    v = torch.cat([v, torch.zeros(n, 62, dtype=torch.float16)], dim=1).reshape(1, 1, n, 64)
+    say("fp8 ties", n)
+    codes, scale = sage.sage_quant_v(v.cuda())
+    torch.cuda.synchronize()
+    rc, rs = sage_ref.quant_v_fp8(v.float().numpy())
+    assert float(rs[0, 0, 0]) == 1.0                   # 448 / 448: codes are the values' own encodes
+    assert np.array_equal(_cpu(codes).numpy()[..., :n], rc)
+
+
+def test_debug_qk_int32_bit_exact():
+    rng = np.random.default_rng(5)
+    for (B, Hq, Hkv, Nq, Nk, d) in [(1, 2, 1, 130, 70, 64), (2, 2, 2, 129, 200, 128), (1, 1, 1, 5, 1, 128)]:
+        say("debug_qk", B, Hq, Hkv, Nq, Nk, d)
+        q8 = rng.integers(-127, 128, (B, Hq, Nq, d)).astype(np.int8)
+        k8 = rng.integers(-127, 128, (B, Hkv, Nk, d)).astype(np.int8)
+        q8[0, 0, 0] = 127
+        k8[0, 0, 0] = -127
+        s = sage.sage_debug_qk_i32(torch.from_numpy(q8).cuda(), torch.from_numpy(k8).cuda())
+        torch.cuda.synchronize()
+        s = _cpu(s).numpy()
+        G = Hq // Hkv
+        for b in range(B):
+            for h in range(Hq):
+                assert np.array_equal(s[b, h], sage_ref.qk_int32(q8[b, h], k8[b, h // G]))
+        assert s[0, 0, 0, 0] == -d * 127 * 127
+
+
+# ------------------------------------------------------------------ float output, every row
+SMALL_CASES = [
+    (W.TINY, "fp16"),                                                     # the tiny workload itself
+    (W.TINY, "fp8"),
+    (W.TINY.with_(B=2, Hq=4, Hkv=2, N=333, d=128, dtype="bf16", layout="NHD", causal=True), "fp8"),
+    (W.TINY.with_(B=2, Hq=4, Hkv=2, N=333, d=128, dtype="bf16", layout="NHD", causal=True), "fp16"),
+    (W.TINY.with_(B=1, Hq=4, Hkv=1, N=1000, d=64, causal=True), "fp8"),
+    (W.TINY.with_(B=1, Hq=2, Hkv=2, N=1000, d=128, causal=False), "fp16"),
+    (W.TINY.with_(B=1, Hq=2, Hkv=2, N=65, d=128, causal=True), "fp8"),
+    (W.TINY.with_(B=1, Hq=1, Hkv=1, N=1, d=64), "fp8"),
+    (W.TINY.with_(B=1, Hq=1, Hkv=1, N=1, d=128, causal=True), "fp16"),
+    (W.MID_OUTLIER.with_(B=1, Hq=2, Hkv=2, N=512), "fp8"),
+]
+
+
+@pytest.mark.parametrize("w,pv", SMALL_CASES,
+                         ids=[f"{w.B}x{w.Hq}/{w.Hkv}x{w.N}x{w.d}{w.dtype}{w.layout}{'c' if w.causal else ''}-{pv}"
+                              for w, pv in SMALL_CASES])
+def test_attention_small_all_rows(w, pv):
+    say("attn small", w, pv)
+    q, k, v = W.generate(w)
+    o = sage.sage_attn_fwd(*_gpu(q, k, v), is_causal=w.causal, sm_scale=w.sm_scale, pv_dtype=pv,
+                           tensor_layout=w.layout)
+    torch.cuda.synchronize()
+    got = sage_ref.as_hnd(o.float().cpu().numpy(), w.layout)
+    qn, kn, vn = _np_inputs(q, k, v, w.layout)
+    ref = sage_ref.sage_attention(qn, kn, vn, dtype=w.dtype, is_causal=w.causal, sm_scale=w.sm_scale, pv=pv)
+    ex = exact.exact_attention(qn, kn, vn, is_causal=w.causal, sm_scale=w.sm_scale)
+    c, r, ce = cos(got, ref), rel_l1(got, ref), cos(got, ex)
+    say(f"   cos={c:.7f} rel_l1={r:.2e} cos_exact={ce:.6f} worst_head={worst_head_cos(got, ref):.7f}")
+    assert np.isfinite(got).all()
+    assert c >= COS_ORACLE and r <= RL1_ORACLE
+    assert ce >= (0.9975 if w.outliers else COS_EXACT)
+
+
+def test_attention_zero_q_is_uniform():
+    """Closed form: Q = 0 gives uniform weights; the output is the mean of V over
+    visible keys (dequantised V in FP8 mode)."""
+    w = W.TINY.with_(B=1, Hq=2, Hkv=2, N=200, d=128)
+    q, k, v = W.generate(w)
+    q = torch.zeros_like(q)
+    for pv in ("fp16", "fp8"):
+        for causal in (False, True):
+            say("zero q", pv, causal)
+            o = sage.sage_attn_fwd(*_gpu(q, k, v), is_causal=causal, pv_dtype=pv)
+            torch.cuda.synchronize()
+            ref = sage_ref.sage_attention(q.float().numpy(), k.float().numpy(), v.float().numpy(), dtype="fp16",
+                                          is_causal=causal, sm_scale=w.sm_scale, pv=pv)
+            got = o.float().cpu().numpy()
+            assert cos(got, ref) >= 0.999999 and rel_l1(got, ref) <= 1e-4
+
+
+def test_attention_is_deterministic_and_layout_invariant():
+    w = W.TINY.with_(B=2, Hq=4, Hkv=2, N=300, d=128, dtype="bf16")
+    q, k, v = _gpu(*W.generate(w))
+    say("determinism")
+    a = sage.sage_attn_fwd(q, k, v, is_causal=True, pv_dtype="fp8")
+    b = sage.sage_attn_fwd(q, k, v, is_causal=True, pv_dtype="fp8")
+    qn, kn, vn = (t.transpose(1, 2).contiguous() for t in (q, k, v))
+    c = sage.sage_attn_fwd(qn, kn, vn, is_causal=True, pv_dtype="fp8", tensor_layout="NHD")
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert torch.equal(a, c.transpose(1, 2))
+
+
+def test_empty_query_is_a_noop():
+    q = torch.zeros(1, 2, 0, 64, dtype=torch.float16, device="cuda")
+    k = torch.randn(1, 2, 5, 64, dtype=torch.float16, device="cuda")
+    o = sage.sage_attn_fwd(q, k, k)
+    torch.cuda.synchronize()
+    assert o.shape == q.shape
+
+
+# ------------------------------------------------------------------ the five workloads at full size
+FULL = [
+    (W.TINY, "fp16", None),
+    (W.MID_OUTLIER, "fp8", 24),
+    (W.GQA_CAUSAL, "fp8", 24),
+    (W.LONG_D64, "fp16", 24),
+    (W.LONG_D64, "fp8", 24),
+    (W.PEAK, "fp8", 16),
+    (W.PEAK.with_(causal=True), "fp8", 16),
+]
+
+
+@pytest.mark.parametrize("w,pv,nrows", FULL,
+                         ids=[f"{w.name}-{pv}{'-causal' if w.causal else ''}" for w, pv, _ in FULL])
+def test_workload_full_size(w, pv, nrows):
+    say("full workload", w.name, pv, "causal" if w.causal else "")
+    q, k, v = W.generate(w)
+    qg, kg, vg = _gpu(q, k, v)
+    o = sage.sage_attn_fwd(qg, kg, vg, is_causal=w.causal, sm_scale=w.sm_scale, pv_dtype=pv,
+                           tensor_layout=w.layout)
+    quant = sage.sage_quant_qk(qg, kg, tensor_layout=w.layout)
+    vcodes, vscale = sage.sage_quant_v(vg, tensor_layout=w.layout)
+    torch.cuda.synchronize()
+    del qg, kg, vg
+    qn, kn, vn = _np_inputs(q, k, v, w.layout)
+    parts = sage_ref.quant_qk(qn, kn)
+    # integer stages in full
+    assert np.array_equal(_cpu(quant["k_mean"]).numpy(), parts["k_mean"])
+    assert np.array_equal(_cpu(quant["q_scale"]).numpy(), parts["q_scale"])
+    assert np.array_equal(_cpu(quant["k_scale"]).numpy(), parts["k_scale"])
+    assert np.array_equal(_cpu(quant["q_codes"]).numpy(), parts["q8"])
+    assert np.array_equal(_cpu(quant["k_codes"]).numpy(), parts["k8"])
+    if pv == "fp8":
+        parts["v8"], parts["v_scale"] = sage_ref.quant_v_fp8(vn)
+        assert np.array_equal(_cpu(vscale).numpy(), parts["v_scale"])
+        assert np.array_equal(_cpu(vcodes).numpy()[..., :w.N], parts["v8"])
+    # float output on sampled rows (row i depends on Q's block of i and all of K, V)
+    rows = None if nrows is None else np.array(W.sample_rows(w.N, nrows, sage_ref.BLK_Q))
+    got = sage_ref.as_hnd(o.float().cpu().numpy(), w.layout)
+    got = got if rows is None else got[:, :, rows]
+    ref = sage_ref.sage_attention(qn, kn, vn, dtype=w.dtype, is_causal=w.causal, sm_scale=w.sm_scale, pv=pv,
+                                  rows=rows, parts=parts)
+    ex = exact.exact_attention(qn, kn, vn, is_causal=w.causal, sm_scale=w.sm_scale, rows=rows)
+    c, r, ce = cos(got, ref), rel_l1(got, ref), cos(got, ex)
+    say(f"   cos={c:.7f} rel_l1={r:.2e} cos_exact={ce:.6f} worst_head={worst_head_cos(got, ref):.7f}")
+    assert np.isfinite(got).all()
+    assert c >= COS_ORACLE and r <= RL1_ORACLE
+    assert ce >= (0.9975 if w.outliers else COS_EXACT)
