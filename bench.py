@@ -1,0 +1,283 @@
+#!/usr/bin/env python3
+"""Attention TOPS of the quantised-attention forward hot path on one MI355X.
+
+A *step* is one pass of the whole hot path over one batch of seeded synthetic
+input already resident in HBM: K channel statistics and smoothing, per-block
+INT8 Q/K, per-channel e4m3 V, and the fused attention kernel (INT8 QK^T,
+dequantisation, online softmax, P to e4m3, PV with two-level accumulation,
+epilogue). It is issued through the C ABI as sage_quant_qk + sage_quant_v +
+sage_attn_fwd_codes -- exactly the kernels sage_attn_fwd enqueues -- so that
+HIP events can bracket the attention kernel inside every timed step.
+
+value        = 4*B*H*N^2*d (halved for causal) / wall time per step   [TOPS]
+roofline     = the attention kernel alone: the same counted operations / its
+               mean event-timed duration, against the dense INT8/FP8 MFMA peak
+cpu_baseline = the CPU oracle on a bounded sample of the same workload.
+
+Default workload: B=1, H=32, N=32768, d=128, fp16, non-causal, PV in e4m3 (the
+long-sequence peak workload); the causal variant is reported alongside.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+import workloads as W  # noqa: E402
+
+METRIC = "attention TOPS (4·B·H·N²·d/t) at N=32K d=128 + % of INT8/FP8 MFMA peak"
+PEAK_TOPS = 5000.0            # MI355X dense INT8 and dense FP8 MFMA peak (5.0 POP/s each)
+PEAK_HBM_GBS = 8000.0
+ALIASES = {"tiny": W.TINY, "mid": W.MID_OUTLIER, "gqa": W.GQA_CAUSAL, "long": W.LONG_D64, "peak": W.PEAK}
+KERNEL_SOURCES = ["quantized_attention_channel_amd/csrc/attn_kernel.hip",
+                  "quantized_attention_channel_amd/csrc/sage_device.h"]
+COUNTERS_MD = os.path.join(ROOT, "profiles", "attn_fwd_peak_counters.md")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counted_ops(w: W.Workload) -> float:
+    return w.attention_ops()
+
+
+class Plan:
+    """Preallocated buffers and the three C-ABI calls of one step."""
+
+    def __init__(self, w: W.Workload, pv: str, q, k, v):
+        import quantized_attention_channel_amd as sage
+        self.sage, self.w, self.pv = sage, w, pv
+        self.shape = sage.shape_of(q, k, w.layout)
+        s = self.shape
+        blk_q, blk_k, _ = sage.sage_block_sizes(w.d)
+        dev = q.device
+        npad = sage.sage_v_codes_stride(w.N)
+        self.q, self.k, self.v = q, k, v
+        self.o = torch.empty_like(q)
+        self.q8 = torch.empty((w.B, w.Hq, w.N, w.d), dtype=torch.int8, device=dev)
+        self.sq = torch.empty((w.B, w.Hq, -(-w.N // blk_q)), dtype=torch.float32, device=dev)
+        self.k8 = torch.empty((w.B, w.Hkv, w.N, w.d), dtype=torch.int8, device=dev)
+        self.sk = torch.empty((w.B, w.Hkv, -(-w.N // blk_k)), dtype=torch.float32, device=dev)
+        self.mu = torch.empty((w.B, w.Hkv, w.d), dtype=torch.float32, device=dev)
+        if pv == "fp8":
+            self.vp = torch.empty((w.B, w.Hkv, w.d, npad), dtype=torch.uint8, device=dev)
+            self.sv = torch.empty((w.B, w.Hkv, w.d), dtype=torch.float32, device=dev)
+        else:
+            self.vp = torch.empty((w.B, w.Hkv, w.d, npad), dtype=q.dtype, device=dev)
+            self.sv = None
+        lib = sage.lib
+        nws = max(lib.sage_quant_qk_workspace_bytes(ctypes.byref(s)), lib.sage_quant_v_workspace_bytes(ctypes.byref(s)))
+        self.ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
+        self.full_ws = torch.empty(max(sage.sage_workspace_bytes(s, pv), 256), dtype=torch.uint8, device=dev)
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        P = sage._ptr
+        self.args_qk = (ctypes.byref(s), P(q), P(k), P(self.q8), P(self.sq), P(self.k8), P(self.sk), P(self.mu),
+                        P(self.ws), self.ws.numel(), self.stream)
+        self.args_v = (ctypes.byref(s), P(v), P(self.vp), P(self.sv), P(self.ws), self.ws.numel(), self.stream)
+        self.args_vt = (ctypes.byref(s), P(v), P(self.vp), self.stream)
+        self.args_attn = (ctypes.byref(s), P(self.q8), P(self.sq), P(self.k8), P(self.sk), P(self.vp), P(self.sv),
+                          P(self.o), int(w.causal), float(w.sm_scale), sage.PV_DTYPES[pv], self.stream)
+        self.args_full = (ctypes.byref(s), P(q), P(k), P(v), P(self.o), int(w.causal), float(w.sm_scale),
+                          sage.PV_DTYPES[pv], P(self.full_ws), self.full_ws.numel(), self.stream)
+
+    def quant(self):
+        lib, chk = self.sage.lib, self.sage._check
+        chk(lib.sage_quant_qk(*self.args_qk), "sage_quant_qk")
+        if self.pv == "fp8":
+            chk(lib.sage_quant_v(*self.args_v), "sage_quant_v")
+        else:
+            chk(lib.sage_transpose_v(*self.args_vt), "sage_transpose_v")
+
+    def attention(self):
+        self.sage._check(self.sage.lib.sage_attn_fwd_codes(*self.args_attn), "sage_attn_fwd_codes")
+
+    def fused_entry(self):
+        self.sage._check(self.sage.lib.sage_attn_fwd(*self.args_full), "sage_attn_fwd")
+
+
+def time_steps(plan: Plan, steps: int, warmup: int):
+    for _ in range(warmup):
+        plan.quant()
+        plan.attention()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1, e2 in ev:
+        e0.record()
+        plan.quant()
+        e1.record()
+        plan.attention()
+        e2.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    quant_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / steps
+    attn_ms = sum(b.elapsed_time(c) for _, b, c in ev) / steps
+    gpu_ms = sum(a.elapsed_time(c) for a, _, c in ev) / steps
+    return wall * 1e3, gpu_ms, quant_ms, attn_ms
+
+
+def time_fused_entry(plan: Plan, steps: int):
+    plan.fused_entry()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        plan.fused_entry()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps * 1e3
+
+
+def counters_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, or None when it is missing or the kernel sources changed since."""
+    if not os.path.exists(COUNTERS_MD):
+        return None, None
+    text = open(COUNTERS_MD).read()
+    def grab(key):
+        m = re.search(rf"^{key}:\s*([0-9a-fA-F.e+-]+)\s*$", text, flags=re.M)
+        return m.group(1) if m else None
+    sha = grab("kernel_source_sha256")
+    vals = [grab(k) for k in ("fetch_kib_per_dispatch", "write_kib_per_dispatch", "copy_fetch_factor",
+                              "copy_write_factor")]
+    if sha != kernel_source_hash() or any(v is None for v in vals):
+        return None, sha
+    fetch, write, ff, fw = (float(v) for v in vals)
+    return (fetch * ff + write * fw) * 1024.0, sha
+
+
+def cpu_baseline(w: W.Workload, pv: str, rows: int):
+    """The oracle, as it stands, on a bounded sample: batch 0 / head 0 of the
+    workload, its Q/K/V quantisation in full and `rows` query rows of attention."""
+    import numpy as np
+    from oracle import sage_ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    one = w.with_(B=1, Hq=1, Hkv=1)
+    q, k, v = W.generate(one)
+    qn, kn, vn = (t.float().numpy() for t in (q, k, v))
+    sel = np.linspace(0, w.N - 1, rows).round().astype(np.int64)
+    t0 = time.perf_counter()
+    sage_ref.sage_attention(qn, kn, vn, dtype=w.dtype, is_causal=w.causal, sm_scale=w.sm_scale, pv=pv,
+                            layout=w.layout, rows=np.unique(sel))
+    dt = time.perf_counter() - t0
+    if w.causal:
+        ops = float(sum(4.0 * (int(i) + 1) * w.d for i in np.unique(sel)))
+    else:
+        ops = 4.0 * len(np.unique(sel)) * w.N * w.d
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": int(threads), "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": (f"batch 0, head 0 of {w.B * w.Hq}: Q/K/V quantisation of that head in full "
+                       f"(N={w.N}) plus {len(np.unique(sel))} of {w.N} query rows of attention; "
+                       f"TOPS counted as 4*rows*N*d{' (causal: visible keys only)' if w.causal else ''}")}
+
+
+def copy_calibration():
+    """A plain device copy of known size, for scaling HBM byte counters."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
+
+
+def measure(w: W.Workload, pv: str, steps: int, warmup: int):
+    q, k, v = W.generate(w, device="cuda")
+    plan = Plan(w, pv, q, k, v)
+    wall_ms, gpu_ms, quant_ms, attn_ms = time_steps(plan, steps, warmup)
+    fused_ms = time_fused_entry(plan, max(3, steps // 4))
+    ops = counted_ops(w)
+    return dict(wall_ms=wall_ms, gpu_ms=gpu_ms, quant_ms=quant_ms, attn_ms=attn_ms, fused_ms=fused_ms,
+                tops=ops / (wall_ms * 1e-3) / 1e12, attn_tops=ops / (attn_ms * 1e-3) / 1e12,
+                quant_bytes=3.0 * (w.B * w.Hq * w.N * w.d + 2 * w.B * w.Hkv * w.N * w.d))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="peak", help="peak|tiny|mid|gqa|long or a full workload name")
+    ap.add_argument("--pv", default=None, help="fp8|fp16 (default: the workload's)")
+    ap.add_argument("--causal", type=int, default=None, help="override the workload's causal flag")
+    ap.add_argument("--no-variants", action="store_true", help="skip the causal variant of the peak workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=8192)
+    ap.add_argument("--copy-calibration", action="store_true", help="run only a 1 GiB device copy")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the quantised attention "
+              "path here is a single-GPU kernel; see the sharding notes in the design document)",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    w = ALIASES.get(args.workload) or W.ALL[args.workload]
+    if args.causal is not None:
+        w = w.with_(causal=bool(args.causal))
+    pv = args.pv or w.pv
+
+    r = measure(w, pv, args.steps, args.warmup)
+    traffic, counters_sha = counters_traffic()
+    roof = {"bound": "mfma", "achieved": round(r["attn_tops"], 2), "peak": PEAK_TOPS, "unit": "TFLOP/s",
+            "frac": round(r["attn_tops"] / PEAK_TOPS, 4), "traffic": traffic,
+            "kernel": "attn_fwd_kernel", "ops_per_launch": counted_ops(w),
+            "mean_launch_ms": round(r["attn_ms"], 4)}
+    out = {
+        "metric": METRIC, "value": round(r["tops"], 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(r["wall_ms"], 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8+fp8_e4m3" if pv == "fp8" else f"int8+{w.dtype}",
+        "data": "synthetic: seeded normal Q/K/V, per-channel K offsets (workloads.py)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                   "causal": w.causal, "pv": pv, "layout": w.layout, "input_dtype": w.dtype},
+        "mfma_peak_frac": round(r["tops"] / PEAK_TOPS, 4),
+        "roofline": roof,
+        "breakdown_ms": {"gpu_step": round(r["gpu_ms"], 4), "quant": round(r["quant_ms"], 4),
+                         "attention": round(r["attn_ms"], 4), "sage_attn_fwd_single_call": round(r["fused_ms"], 4)},
+        "quant_hbm": {"algorithmic_bytes": r["quant_bytes"],
+                      "GBps": round(r["quant_bytes"] / (r["quant_ms"] * 1e-3) / 1e9, 1),
+                      "frac_of_8TBps": round(r["quant_bytes"] / (r["quant_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+    }
+    if w is W.PEAK and not args.no_variants:
+        wc = w.with_(causal=True)
+        rc = measure(wc, pv, args.steps, args.warmup)
+        out["variants"] = {"causal": {"value": round(rc["tops"], 2), "ms_per_step": round(rc["wall_ms"], 4),
+                                      "attention_tops": round(rc["attn_tops"], 2),
+                                      "attention_frac": round(rc["attn_tops"] / PEAK_TOPS, 4),
+                                      "attention_ms": round(rc["attn_ms"], 4)}}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, pv, args.cpu_rows)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

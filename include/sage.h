@@ -131,6 +131,22 @@ sage_status sage_attn_fwd(const sage_shape* s, const void* q, const void* k, con
                           void* o, int32_t is_causal, float sm_scale, int32_t pv_dtype,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* FP16-PV preparation of V: the 16-bit values transposed to
+ *   v_t [B,Hkv,d,sage_v_codes_stride(Nk)] (keys contiguous per channel, padding keys 0),
+ * the layout the PV product reads in FP16/BF16 mode. */
+sage_status sage_transpose_v(const sage_shape* s, const void* v, void* v_t, void* stream);
+
+/* The fused attention kernel alone, from precomputed codes (for callers that
+ * quantise once and reuse K/V codes, and to time the kernel by itself):
+ *   q_codes/q_scale/k_codes/k_scale  as written by sage_quant_qk
+ *   v_prepared  FP8: e4m3 codes from sage_quant_v;  FP16: v_t from sage_transpose_v
+ *   v_scale     FP8: from sage_quant_v;  FP16: ignored (may be NULL)
+ * o, is_causal, sm_scale, pv_dtype as for sage_attn_fwd. Needs no workspace. */
+sage_status sage_attn_fwd_codes(const sage_shape* s, const int8_t* q_codes, const float* q_scale,
+                                const int8_t* k_codes, const float* k_scale, const void* v_prepared,
+                                const float* v_scale, void* o, int32_t is_causal, float sm_scale,
+                                int32_t pv_dtype, void* stream);
+
 /* Test hook: the INT32 QK^T of the attention kernel's own matrix-core tile code,
  * for canonical-order codes as produced by sage_quant_qk.
  *   s_out [B,Hq,Nq,Nk] int32, s_out[b,h,i,j] = sum_c q_codes[b,h,i,c] * k_codes[b,h/G,j,c]. */

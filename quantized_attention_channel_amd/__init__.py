@@ -7,7 +7,8 @@ the binding raises.
 
 Entry points (same names as the C ABI):
   sage_block_sizes, sage_v_codes_stride, sage_workspace_bytes,
-  sage_quant_qk, sage_quant_v, sage_attn_fwd, sage_debug_qk_i32.
+  sage_quant_qk, sage_quant_v, sage_transpose_v, sage_attn_fwd,
+  sage_attn_fwd_codes, sage_debug_qk_i32.
 User-facing wrapper:
   sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None,
            pv_dtype="fp8") -- the call shape the SageAttention pages show
@@ -43,6 +44,9 @@ _SIGNATURES = {
     "sage_quant_v": (ctypes.c_int, [_c_shape_p, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "sage_attn_fwd": (ctypes.c_int, [_c_shape_p, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_float,
                                      ctypes.c_int32, _vp, ctypes.c_size_t, _vp]),
+    "sage_transpose_v": (ctypes.c_int, [_c_shape_p, _vp, _vp, _vp]),
+    "sage_attn_fwd_codes": (ctypes.c_int, [_c_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32,
+                                           ctypes.c_float, ctypes.c_int32, _vp]),
     "sage_debug_qk_i32": (ctypes.c_int, [_c_shape_p, _vp, _vp, _vp, _vp]),
     "sage_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
@@ -175,6 +179,29 @@ def sage_quant_v(v: torch.Tensor, tensor_layout: str = "HND"):
     return codes, scale
 
 
+def sage_transpose_v(v: torch.Tensor, tensor_layout: str = "HND") -> torch.Tensor:
+    """16-bit V transposed to [B,Hkv,d,Nk_pad] (the FP16-PV operand layout)."""
+    _check_inputs(v)
+    s = shape_of(v, v, tensor_layout)
+    vt = torch.empty((s.batch, s.heads_kv, s.head_dim, sage_v_codes_stride(s.seq_k)), dtype=v.dtype,
+                     device=v.device)
+    _check(lib.sage_transpose_v(_ref(s), _ptr(v), _ptr(vt), _stream(v.device)), "sage_transpose_v")
+    return vt
+
+
+def sage_attn_fwd_codes(shape: SageShape, q_codes, q_scale, k_codes, k_scale, v_prepared, v_scale, o, *,
+                        is_causal: bool = False, sm_scale: Optional[float] = None, pv_dtype: str = "fp8"):
+    """The fused attention kernel alone, from the outputs of sage_quant_qk and
+    sage_quant_v (FP8) or sage_transpose_v (FP16). Writes into ``o``."""
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(shape.head_dim)
+    _check(lib.sage_attn_fwd_codes(_ref(shape), _ptr(q_codes), _ptr(q_scale), _ptr(k_codes), _ptr(k_scale),
+                                   _ptr(v_prepared), _ptr(v_scale), _ptr(o), int(bool(is_causal)),
+                                   float(sm_scale), PV_DTYPES[pv_dtype], _stream(o.device)),
+           "sage_attn_fwd_codes")
+    return o
+
+
 def sage_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, is_causal: bool = False,
                   sm_scale: Optional[float] = None, pv_dtype: str = "fp8", tensor_layout: str = "HND",
                   out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -229,6 +256,7 @@ def sageattn(q, k, v, tensor_layout: str = "HND", is_causal: bool = False, sm_sc
                          sm_scale=sm_scale, pv_dtype=pv_dtype, tensor_layout=tensor_layout)
 
 
-__all__ = ["sageattn", "sage_attn_fwd", "sage_quant_qk", "sage_quant_v", "sage_debug_qk_i32",
+__all__ = ["sageattn", "sage_attn_fwd", "sage_attn_fwd_codes", "sage_quant_qk", "sage_quant_v",
+           "sage_transpose_v", "sage_debug_qk_i32",
            "sage_block_sizes", "sage_v_codes_stride", "sage_workspace_bytes", "make_shape", "shape_of",
            "SageError", "SageShape", "lib", "LIB_PATH"]

@@ -263,7 +263,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     const float inv_l = 1.0f / pair_sum(l_run);
     uint16_t* orow = reinterpret_cast<uint16_t*>(a.o) + (int64_t)b * a.ogeo.batch_stride +
                      (int64_t)h * a.ogeo.head_stride + (int64_t)qi * a.ogeo.tok_stride;
-    const float* vs = a.v_scale + (int64_t)bhk * D;
+    const float* vs = FP8 ? a.v_scale + (int64_t)bhk * D : nullptr;
 #pragma unroll
     for (int cb = 0; cb < NT; ++cb) {
 #pragma unroll

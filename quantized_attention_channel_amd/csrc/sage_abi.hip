@@ -275,6 +275,68 @@ sage_status sage_attn_fwd(const sage_shape* s, const void* q, const void* k, con
   return from_hip(sage::launch_attn(aa, hs));
 }
 
+sage_status sage_transpose_v(const sage_shape* s, const void* v, void* v_t, void* stream) {
+  Dims d;
+  sage_status st = check_shape(s, &d);
+  if (st != SAGE_OK) return st;
+  if (d.B == 0 || d.Nk == 0) return SAGE_OK;
+  if (!v || !v_t || !aligned(v, 16) || !aligned(v_t, 16)) return SAGE_ERR_INVALID_ARGUMENT;
+  sage::QuantVArgs a{};
+  a.v = v;
+  a.vgeo = geom(d, d.Hkv, d.Nk);
+  a.B = int(d.B), a.Hkv = int(d.Hkv), a.Nk = int(d.Nk), a.D = int(d.D);
+  a.n_pad = int(round_up(d.Nk, sage::kVPad));
+  a.bf16 = d.bf16;
+  a.fp8 = false;
+  a.out = v_t;
+  return from_hip(sage::launch_quant_v(a, static_cast<hipStream_t>(stream)));
+}
+
+sage_status sage_attn_fwd_codes(const sage_shape* s, const int8_t* q_codes, const float* q_scale,
+                                const int8_t* k_codes, const float* k_scale, const void* v_prepared,
+                                const float* v_scale, void* o, int32_t is_causal, float sm_scale,
+                                int32_t pv_dtype, void* stream) {
+  Dims d;
+  sage_status st = check_shape(s, &d);
+  if (st != SAGE_OK) return st;
+  if (pv_dtype != SAGE_PV_FP16 && pv_dtype != SAGE_PV_FP8_E4M3) return SAGE_ERR_INVALID_ARGUMENT;
+  if (is_causal != 0 && is_causal != 1) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (d.B == 0 || d.Nq == 0) return SAGE_OK;
+  if (d.Nk == 0) return SAGE_ERR_INVALID_ARGUMENT;
+  if (is_causal && d.Nq != d.Nk) return SAGE_ERR_UNSUPPORTED;
+  const bool fp8 = pv_dtype == SAGE_PV_FP8_E4M3;
+  if (!q_codes || !q_scale || !k_codes || !k_scale || !v_prepared || !o || (fp8 && !v_scale))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(v_prepared, 16) || !aligned(o, 16) ||
+      !aligned(q_scale, 4) || !aligned(k_scale, 4) || (fp8 && !aligned(v_scale, 4)))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  const size_t obytes = size_t(d.B * d.Hq * d.Nq * d.D) * 2;
+  const int64_t npad = round_up(d.Nk, sage::kVPad);
+  if (overlaps(o, obytes, q_codes, size_t(d.B * d.Hq * d.Nq * d.D)) ||
+      overlaps(o, obytes, k_codes, size_t(d.B * d.Hkv * d.Nk * d.D)) ||
+      overlaps(o, obytes, v_prepared, size_t(d.B * d.Hkv * d.D * npad) * (fp8 ? 1 : 2)))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  sage::AttnArgs aa{};
+  aa.q8 = q_codes;
+  aa.q_scale = q_scale;
+  aa.k8 = k_codes;
+  aa.k_scale = k_scale;
+  aa.vt = v_prepared;
+  aa.v_scale = v_scale;
+  aa.o = o;
+  aa.ogeo = geom(d, d.Hq, d.Nq);
+  aa.B = int(d.B), aa.Hq = int(d.Hq), aa.Hkv = int(d.Hkv), aa.Nq = int(d.Nq), aa.Nk = int(d.Nk), aa.D = int(d.D);
+  aa.n_pad = int(npad);
+  aa.nbq = int(cdiv(d.Nq, sage::kBlkQ));
+  aa.nbk = int(cdiv(d.Nk, sage::kBlkK));
+  aa.scale_log2 = sm_scale * sage::kLog2E;
+  aa.causal = is_causal != 0;
+  aa.bf16 = d.bf16;
+  aa.fp8 = fp8;
+  return from_hip(sage::launch_attn(aa, static_cast<hipStream_t>(stream)));
+}
+
 sage_status sage_debug_qk_i32(const sage_shape* s, const int8_t* q_codes, const int8_t* k_codes, int32_t* s_out,
                               void* stream) {
   Dims d;
