@@ -84,7 +84,7 @@ typedef struct sage_shape {
  * Returns SAGE_ERR_UNSUPPORTED for other head dims; null outputs are skipped. */
 sage_status sage_block_sizes(int32_t head_dim, int32_t* blk_q, int32_t* blk_k, int32_t* bkv);
 
-/* Nk rounded up to the padded key count of transposed V codes (multiple of 64). */
+/* Nk rounded up to the padded key count of transposed V codes (a multiple of BKV = 128). */
 int64_t sage_v_codes_stride(int32_t seq_k);
 
 /* Workspace bytes sage_quant_qk needs for `s` (K channel-sum partials). */

@@ -59,7 +59,7 @@ INT8_MAX = 127.0
 
 BLK_Q = 128        # [R7]
 BLK_K = 64         # [R7]
-BKV = {64: 64, 128: 64}   # [R14] KV tile per head dim
+BKV = {64: 128, 128: 128}   # [R14] KV tile per head dim
 
 
 def as_hnd(x: np.ndarray, layout: str) -> np.ndarray:

@@ -24,7 +24,8 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsage.so")
+# SAGE_LIB_PATH selects another build of the same library (same ABI); default: in-tree.
+LIB_PATH = os.environ.get("SAGE_LIB_PATH") or os.path.join(_HERE, "libsage.so")
 
 SAGE_OK, SAGE_ERR_INVALID_ARGUMENT, SAGE_ERR_UNSUPPORTED, SAGE_ERR_WORKSPACE, SAGE_ERR_HIP = range(5)
 LAYOUTS = {"HND": 0, "NHD": 1}

@@ -13,6 +13,7 @@ typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -20,8 +21,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // Method constants (quantisation blocks and the online-softmax KV tile).
 constexpr int kBlkQ = 128;   // query tokens per INT8 scale
 constexpr int kBlkK = 64;    // key tokens per INT8 scale
-constexpr int kBkv = 64;     // keys per online-softmax tile
-constexpr int kVPad = 64;    // transposed-V rows are padded to a multiple of this
+constexpr int kBkv = 128;    // keys per online-softmax tile
+constexpr int kVPad = 128;   // transposed-V rows are padded to a multiple of the tile
 constexpr float kE4m3Max = 448.0f;
 constexpr float kLog2E = 1.4426950408889634f;
 constexpr float kLog2E4m3Max = 8.807354922057604f;  // log2(448)

@@ -65,9 +65,9 @@ def test_status_strings():
 
 def test_v_codes_stride():
     assert sage.sage_v_codes_stride(0) == 0
-    assert sage.sage_v_codes_stride(1) == 64
-    assert sage.sage_v_codes_stride(64) == 64
-    assert sage.sage_v_codes_stride(65) == 128
+    assert sage.sage_v_codes_stride(1) == 128
+    assert sage.sage_v_codes_stride(128) == 128
+    assert sage.sage_v_codes_stride(129) == 256
 
 
 def _shape(**kw):
@@ -80,7 +80,7 @@ def test_workspace_size_grows_with_the_problem():
     s = _shape()
     w8, w16 = sage.sage_workspace_bytes(s, "fp8"), sage.sage_workspace_bytes(s, "fp16")
     codes = 2 * 4 * 300 * 128 + 2 * 2 * 300 * 128
-    assert w8 >= codes + 2 * 2 * 128 * 320 and w16 >= codes + 2 * 2 * 128 * 320 * 2
+    assert w8 >= codes + 2 * 2 * 128 * 384 and w16 >= codes + 2 * 2 * 128 * 384 * 2
     assert w8 % 256 == 0 and w16 % 256 == 0
     assert sage.sage_workspace_bytes(_shape(Nq=600, Nk=600), "fp8") > w8
     assert sage.lib.sage_workspace_bytes(None, 1) == 0
