@@ -36,14 +36,18 @@ Readings where the pages are silent (each also listed in the design notes):
   [R10] sm_scale and log2(e) enter through the dequantisation factor
        c = fp32(s_q * s_k * sm_scale * log2 e); scores live in the log2 domain.
   [R11] causal masking is top-left aligned (key j > query i is masked).
-  [R12] P goes to e4m3 as e4m3(fp32(448 * P~)); the 1/448 is undone in the
-       epilogue together with s_v.
+  [R12] P goes to e4m3 as e4m3(fp32(448 * P~)); the factor 448 cancels against
+       the row sum (R16), s_v is applied in the epilogue.
   [R13] in FP16-PV mode P is rounded to the input dtype (fp16 or bf16) and
        multiplied with the unquantised V.
   [R14] the online softmax walks KV tiles of BKV keys from key 0 upward; BKV
        is part of the method's definition (P codes depend on the running max).
   [R15] level-1 accumulation spans one KV tile; level 2 is O = alpha*O + R.
-  [R16] the row sum l accumulates the unquantised fp32 P~.
+  [R16] the row sum l accumulates the P values that enter the PV product (the
+       e4m3 values of 448 * P~ in FP8 mode, the fp16/bf16-rounded P~ in FP16
+       mode), so the output is normalised by the weights actually applied;
+       against fp64 exact attention this is equal to or slightly better than
+       summing the unquantised P~.
 """
 from __future__ import annotations
 
@@ -180,8 +184,9 @@ def online_softmax_pv(s2: np.ndarray, vals: np.ndarray, *, bkv: int, p_codec, wo
     Per tile t, in ascending order:
       m_new = max(m_old, max_j s2);  alpha = exp2(m_old - m_new)  (0 on the first tile)
       P~    = exp2(s2 - m_new)
-      l     = alpha * l + sum_j P~                     [R16]
-      R     = codec(P~) . vals_tile                    (level 1: fresh per tile)
+      P     = codec(P~)                                (the values entering PV)
+      l     = alpha * l + sum_j P                      [R16]
+      R     = P . vals_tile                            (level 1: fresh per tile)
       O     = alpha * O + R                            (level 2)
     Returns (O [R,dv] float64, l [R] float64) -- not yet normalised.
     """
@@ -200,8 +205,8 @@ def online_softmax_pv(s2: np.ndarray, vals: np.ndarray, *, bkv: int, p_codec, wo
             p = np.exp2((st - m_safe[:, None]).astype(work_dtype)).astype(work_dtype)
         p = np.where(live[:, None], p, 0).astype(work_dtype)
         alpha = np.where(live, alpha, 0.0).astype(np.float64)
-        l = alpha * l + p.astype(np.float64).sum(axis=1)
         pq = p.astype(np.float64) if p_codec is None else p_codec(p)
+        l = alpha * l + pq.sum(axis=1)                # [R16]
         r = pq @ vals[t0:t0 + bkv]                    # level 1 (exact for e4m3 x e4m3)
         o = alpha[:, None] * o + r                    # level 2
         m = m_new
@@ -282,7 +287,7 @@ def sage_attention(q, k, v, *, dtype: str, is_causal: bool, sm_scale: float, pv:
                 vals = v[b, g].astype(np.float64)
             o, l = online_softmax_pv(s2, vals, bkv=bkv, p_codec=codec, work_dtype=np.float32)
             if pv == "fp8":                                                     # epilogue
-                o = o * (parts["v_scale"][b, g].astype(np.float64) / E4M3_MAX)[None, :]
+                o = o * parts["v_scale"][b, g].astype(np.float64)[None, :]
             out[b, h] = o / l[:, None]
     if return_fp64:
         return out

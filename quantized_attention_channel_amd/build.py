@@ -45,7 +45,9 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1)) as ex:
         outs = list(ex.map(_run, cmds))
     tmp = LIB + ".tmp"
-    outs.append(_run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]))
+    # -z defs: a symbol left undefined (e.g. a kernel stub the host pass did not
+    # emit) fails the link here instead of the first dlopen
+    outs.append(_run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,-z,defs", "-o", tmp, *objs]))
     os.replace(tmp, LIB)
     if verbose:
         for o in outs:

@@ -35,21 +35,35 @@ constexpr int kBlocks = kBkv / 32; // 32-key S^T blocks per tile
 static_assert(kBkv == 2 * kBlkK, "a tile spans two K quantisation blocks");
 
 // --------------------------------------------------------------- LDS layouts
-// K tile: [128 keys][D bytes]; 16-byte chunks XOR-swizzled per row so that the
-// 8 rows read by 8 consecutive lanes land in 8 different bank groups.
-__device__ __forceinline__ int key_swz(int row) { return (row & 3) | (((row >> 4) & 1) << 2); }
+// gfx950 serves a 16-byte-per-lane LDS read 16 lanes at a time from 64 banks
+// (256 bytes per cycle); a read is conflict-free when every group of 16
+// consecutive lanes covers the 16 distinct 16-byte slots of a 256-byte span.
+// Each layout XOR-swizzles the 16-byte chunk index with bits of the row so the
+// operand reads of the kernel below meet that rule.
+//
+// K tile: [128 keys][D bytes]. A lane group reads 16 rows key_perm(0..15)
+// (+16) of one chunk column; the swizzle uses the row bits that vary among them.
+template <int D>
+__device__ __forceinline__ int key_swz(int row) {
+  if constexpr (D == 128) return ((row >> 1) & 3) | (((row >> 4) & 1) << 2);   // 8 chunks per row
+  else return ((row >> 2) & 1) | (((row >> 4) & 1) << 1);                      // 4 chunks per row
+}
 template <int D>
 __device__ __forceinline__ int k_lds_off(int row, int chunk) {
-  return row * D + ((chunk ^ (key_swz(row) & (D / 16 - 1))) << 4);
+  return row * D + ((chunk ^ key_swz<D>(row)) << 4);
 }
 // A row m of a 32-key block reads key key_perm(m); the S^T result then holds
 // keys 16*g .. 16*g+15 of the block in lane group g, in element order.
 __device__ __forceinline__ int key_perm(int m) { return ((m >> 2) & 1) * 16 + (m >> 3) * 4 + (m & 3); }
-// V^T tile: [D channels][128 keys] of 1 (e4m3) or 2 (fp16/bf16) bytes per key.
+// V^T tile: [D channels][128 keys] of 1 (e4m3: 8 chunks per row) or 2
+// (fp16/bf16: 16 chunks per row) bytes per key; a lane group reads 16
+// consecutive rows of one chunk column.
+template <bool FP8>
+__device__ __forceinline__ int v_swz(int row) { return FP8 ? ((row >> 1) & 7) : (row & 15); }
 template <bool FP8>
 __device__ __forceinline__ int v_lds_off(int row, int chunk) {
   constexpr int rowb = FP8 ? kBkv : 2 * kBkv;
-  return row * rowb + ((chunk ^ (row & 7)) << 4);
+  return row * rowb + ((chunk ^ v_swz<FP8>(row)) << 4);
 }
 
 __device__ __forceinline__ i32x4 lds16(const void* p) { return *reinterpret_cast<const i32x4*>(p); }
@@ -57,36 +71,46 @@ __device__ __forceinline__ i32x4 lds16(const void* p) { return *reinterpret_cast
 // --------------------------------------------------------------- tile staging
 // Direct global -> LDS loads (no staging registers): in each wave-wide load,
 // lane L writes 16 bytes at LDS slot base + 16 * L, so every lane fetches the
-// global chunk that the swizzled layout puts in its slot. Rows past Nk read as
-// zeros through the buffer range check.
+// global chunk that the swizzled layout puts in its slot. Per-lane offsets do
+// not depend on the tile; the tile offset goes in the scalar offset. Rows past
+// Nk read as zeros through the buffer range check.
 template <int D, bool FP8>
 struct TileStage {
   static constexpr int kVRowB = kBkv * (FP8 ? 1 : 2);
   static constexpr int kKLoads = kBkv * D / 16 / 256;      // wave-wide loads per wave
   static constexpr int kVLoads = D * kVRowB / 16 / 256;
+  static constexpr int kEb = FP8 ? 1 : 2;
 
-  // sk/sv: the LDS tile buffers; rv covers this head's V^T rows [D][n_pad].
-  static __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int n_pad,
-                                               int k0, int8_t* sk, uint8_t* sv, int wave, int lane) {
-    constexpr int kcpr = D / 16;                            // 16-byte chunks per K row
+  static __device__ __forceinline__ void init(uint32_t* koff, uint32_t* voff, int wave, int lane, int n_pad) {
+    constexpr int kcpr = D / 16;                          // 16-byte chunks per K row
 #pragma unroll
     for (int i = 0; i < kKLoads; ++i) {
       const int slot = (i * 4 + wave) * 64 + lane;
       const int row = slot / kcpr, pchunk = slot % kcpr;
-      const int gchunk = pchunk ^ (key_swz(row) & (kcpr - 1));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(sk + (i * 4 + wave) * 1024),
-                                              16, (uint32_t)(k0 + row) * D + gchunk * 16, 0, 0, 0);
+      koff[i] = (uint32_t)row * D + ((pchunk ^ key_swz<D>(row)) << 4);
     }
-    constexpr int vcpr = kVRowB / 16;                       // 16-byte chunks per V^T row
-    constexpr int eb = FP8 ? 1 : 2;
+    constexpr int vcpr = kVRowB / 16;                     // 16-byte chunks per V^T row
 #pragma unroll
     for (int i = 0; i < kVLoads; ++i) {
       const int slot = (i * 4 + wave) * 64 + lane;
       const int row = slot / vcpr, pchunk = slot % vcpr;
-      const int gchunk = pchunk ^ (row & 7);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(sv + (i * 4 + wave) * 1024),
-                                              16, ((uint32_t)row * n_pad + k0) * eb + gchunk * 16, 0, 0, 0);
+      voff[i] = (uint32_t)row * n_pad * kEb + ((pchunk ^ v_swz<FP8>(row)) << 4);
     }
+  }
+  static __device__ __forceinline__ void issue_k(__amdgpu_buffer_rsrc_t rk, const uint32_t* koff, int wave, int k0,
+                                                 int8_t* sk) {
+#pragma unroll
+    for (int i = 0; i < kKLoads; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(sk + (i * 4 + wave) * 1024),
+                                              16, koff[i], k0 * D, 0, 0);
+  }
+  // rv covers this head's V^T rows [D][n_pad]
+  static __device__ __forceinline__ void issue_v(__amdgpu_buffer_rsrc_t rv, const uint32_t* voff, int wave, int k0,
+                                                 uint8_t* sv) {
+#pragma unroll
+    for (int i = 0; i < kVLoads; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(sv + (i * 4 + wave) * 1024),
+                                              16, voff[i], k0 * kEb, 0, 0);
   }
 };
 
@@ -158,7 +182,6 @@ __device__ __forceinline__ void attend_tile(const int8_t* sk, const uint8_t* sv,
   const float bias = (FP8 ? kLog2E4m3Max : 0.0f) - m_new;   // P8 = e4m3(448 * P~) via the exponent
 
   // P~ overwrites the scores in place (as fp32 bit patterns).
-  float lsum = 0.0f;
 #pragma unroll
   for (int b = 0; b < kBlocks; ++b) {
     const float c = b < 2 ? c0 : c1;
@@ -167,10 +190,8 @@ __device__ __forceinline__ void attend_tile(const int8_t* sk, const uint8_t* sv,
       float x = fast_exp2(__builtin_fmaf((float)s[b][r], c, bias));
       if (MASK && s[b][r] == INT_MIN) x = 0.0f;
       s[b][r] = __builtin_bit_cast(int, x);
-      lsum += x;
     }
   }
-  st.l = alpha * st.l + lsum;
   st.m = m_new;
   // (copy the element out first: a bit-cast applied to a vector-element
   //  expression reads the vector's first element)
@@ -188,6 +209,17 @@ __device__ __forceinline__ void attend_tile(const int8_t* sk, const uint8_t* sv,
         int y = __builtin_amdgcn_cvt_pk_fp8_f32(p(2 * u + 1, 4 * w), p(2 * u + 1, 4 * w + 1), 0, false);
         pk[u][4 + w] = __builtin_amdgcn_cvt_pk_fp8_f32(p(2 * u + 1, 4 * w + 2), p(2 * u + 1, 4 * w + 3), y, true);
       }
+    // Row sum of the quantised P (the values the PV product consumes): with an
+    // all-ones A operand every row of the product is the sum over the tile's
+    // keys, so each lane receives its query's complete sum.
+    {
+      constexpr int kOnes = 0x38383838;                 // four e4m3 1.0
+      const i32x8 ones = {kOnes, kOnes, kOnes, kOnes, kOnes, kOnes, kOnes, kOnes};
+      f32x16 ls = mfma_fp8(ones, pk[0], f32x16{});
+      ls = mfma_fp8(ones, pk[1], ls);
+      st.l = __builtin_fmaf(alpha, st.l, ls[0]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int cb = 0; cb < NT; ++cb) {
       const int row = cb * 32 + n;
@@ -214,6 +246,14 @@ __device__ __forceinline__ void attend_tile(const int8_t* sk, const uint8_t* sv,
         ph[2 * b][e] = (HS)p(b, e);
         ph[2 * b + 1][e] = (HS)p(b, 8 + e);
       }
+    // Row sum of the rounded P (the values the PV product consumes), two per
+    // dot instruction; each lane holds its half of the keys.
+    float lsum = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 2 * kBlocks; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) lsum = dot2_ones(ph[u][e], ph[u][e + 1], lsum);
+    st.l = __builtin_fmaf(alpha, st.l, lsum);
 #pragma unroll
     for (int cb = 0; cb < NT; ++cb) {
       const int row = cb * 32 + n;
@@ -280,7 +320,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   const auto rv = make_rsrc(reinterpret_cast<const uint8_t*>(a.vt) + (int64_t)bhk * D * a.n_pad * eb,
                             (uint32_t)(D * a.n_pad * eb));
 
-  Stage::issue(rk, rv, a.n_pad, 0, s_k0, s_v0, wave, lane);
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t koff[Stage::kKLoads], voff[Stage::kVLoads];
+  Stage::init(koff, voff, wv, lane, a.n_pad);
+  Stage::issue_k(rk, koff, wv, 0, s_k0);
+  Stage::issue_v(rv, voff, wv, 0, s_v0);
   wait_tile_loads();
   __syncthreads();
 
@@ -297,7 +341,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
     const float c1 = cq * kscale[min(2 * kt + 1, a.nbk - 1)];   // past Nk: masked anyway
     // always prefetch (the last tile reloads itself into the idle buffer) so the
     // wait-count bookkeeping sees one path
-    Stage::issue(rk, rv, a.n_pad, min(kt + 1, n_kt - 1) * kBkv, nk_buf, nv_buf, wave, lane);
+    Stage::issue_k(rk, koff, wv, min(kt + 1, n_kt - 1) * kBkv, nk_buf);
+    Stage::issue_v(rv, voff, wv, min(kt + 1, n_kt - 1) * kBkv, nv_buf);
     if (kt < n_kt_wave) {
       const int k0 = kt * kBkv;
       const bool need_mask = (k0 + kBkv > a.Nk) || (CAUSAL && k0 + kBkv - 1 > q0w);
@@ -316,7 +361,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
 
   // Epilogue: normalise, undo the V scale, round, store in the caller's layout.
   if (qi < a.Nq) {
-    const float inv_l = 1.0f / pair_sum(st.l);
+    // (the FP8 path's row sum is already complete in both lanes of a query)
+    const float inv_l = 1.0f / (FP8 ? st.l : pair_sum(st.l));
     uint16_t* orow = reinterpret_cast<uint16_t*>(a.o) + (int64_t)b * a.ogeo.batch_stride +
                      (int64_t)h * a.ogeo.head_stride + (int64_t)qi * a.ogeo.tok_stride;
     const float* vs = FP8 ? a.v_scale + (int64_t)bhk * D : nullptr;

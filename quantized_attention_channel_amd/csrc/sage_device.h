@@ -88,4 +88,14 @@ __device__ __forceinline__ float wave_max(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// acc + a + b for two 16-bit floats, one packed dot instruction (products with 1.0 are exact).
+__device__ __forceinline__ float dot2_ones(_Float16 a, _Float16 b, float acc) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2(h2{a, b}, h2{(_Float16)1.0f, (_Float16)1.0f}, acc, false);
+}
+__device__ __forceinline__ float dot2_ones(__bf16 a, __bf16 b, float acc) {
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(b2{a, b}, b2{(__bf16)1.0f, (__bf16)1.0f}, acc, false);
+}
+
 }  // namespace sage

@@ -103,6 +103,38 @@ def test_identical_keys_give_uniform_attention(pv):
     assert np.allclose(o, np.broadcast_to(want, o.shape), rtol=1e-12, atol=1e-14)
 
 
+def _worked_fp8_case():
+    import math
+    d = 64
+    b = np.float32(np.float16(0.25 * 8 / math.log2(math.e)))     # S2 = +-b*log2(e)/8 ~ 0.25
+    q = np.zeros((1, 1, 1, d), np.float32)
+    q[0, 0, 0, 0] = b
+    k = np.zeros((1, 1, 2, d), np.float32)
+    k[0, 0, 0, 0], k[0, 0, 1, 0] = 1.0, -1.0
+    v = np.zeros((1, 1, 2, d), np.float32)
+    v[0, 0, 0, :2] = [1.0, 0.25]
+    v[0, 0, 1, :2] = [0.5, -1.0]
+    return q, k, v
+
+
+def test_p_quantisation_worked_example():
+    """P's e4m3 rounding and the row sum of the values entering PV, by hand
+    (tests/golden/p_quant_worked.txt)."""
+    import os
+    rows = []
+    with open(os.path.join(os.path.dirname(__file__), "golden", "p_quant_worked.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                rows.append([float(t) for t in line.split()])
+    q, k, v = _worked_fp8_case()
+    o = sage_ref.sage_attention(q, k, v, dtype="fp16", is_causal=False, sm_scale=0.125, pv="fp8",
+                                return_fp64=True)[0, 0, 0]
+    for ch, num, den in rows:
+        assert abs(o[int(ch)] - num / den) <= 1e-6      # fp32 accumulation; other readings differ by >1e-3
+    assert np.all(o[2:] == 0)
+
+
 # --------------------------------------------------------------------------- structure
 @pytest.mark.parametrize("pv", ["fp16", "fp8"])
 def test_gqa_equals_repeated_heads(pv):
@@ -178,12 +210,15 @@ def test_planted_mistakes_are_caught(monkeypatch):
         m.setattr(sage_ref, "k_channel_mean",
                   lambda k: (orig_mean(k).astype(np.float64) * k.shape[2] / (k.shape[2] + 1)).astype(np.float32))
         assert _fails(tq.test_k_mean_is_exact_sum_correctly_divided)
-    # 4. P scaled by 240 (the FNUZ maximum) instead of 448
+    # 4. P scaled by 240 (the FNUZ maximum) instead of 448; P not quantised at all
     with monkeypatch.context() as m:
         from oracle.fp8_e4m3 import e4m3_round
         m.setattr(sage_ref, "_p_codec_fp8",
                   lambda p: e4m3_round((p.astype(np.float32) * np.float32(240)).astype(np.float32)))
-        assert _fails(lambda: test_zero_q_gives_mean_of_values("fp8", False))
+        assert _fails(test_p_quantisation_worked_example)
+    with monkeypatch.context() as m:
+        m.setattr(sage_ref, "_p_codec_fp8", lambda p: p.astype(np.float64) * 448.0)
+        assert _fails(test_p_quantisation_worked_example)
     # 5. log2(e) dropped from the dequantisation factor (natural-log scores fed to exp2)
     orig_dq = sage_ref.dequant_factor
     with monkeypatch.context() as m:
