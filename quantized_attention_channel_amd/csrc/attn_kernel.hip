@@ -80,37 +80,36 @@ struct TileStage {
   static constexpr int kKLoads = kBkv * D / 16 / 256;      // wave-wide loads per wave
   static constexpr int kVLoads = D * kVRowB / 16 / 256;
   static constexpr int kEb = FP8 ? 1 : 2;
+  // Load round i covers LDS bytes [4096 i, 4096 (i+1)) of a tile: K rows
+  // 4096/D apart, V^T rows 4096/kVRowB apart. Both swizzles read only row
+  // bits below those strides, so round i's global offsets are round 0's plus
+  // a constant, which goes in the scalar offset: one VGPR per tensor.
+  static constexpr int kKRowsPerRound = 4096 / D;
+  static constexpr int kVRowsPerRound = 4096 / kVRowB;
+  static_assert(D == 64 || D == 128, "head dims");
+  static_assert(kKRowsPerRound >= 32 && kVRowsPerRound >= 16, "swizzle bits stay below the round stride");
 
-  static __device__ __forceinline__ void init(uint32_t* koff, uint32_t* voff, int wave, int lane, int n_pad) {
-    constexpr int kcpr = D / 16;                          // 16-byte chunks per K row
-#pragma unroll
-    for (int i = 0; i < kKLoads; ++i) {
-      const int slot = (i * 4 + wave) * 64 + lane;
-      const int row = slot / kcpr, pchunk = slot % kcpr;
-      koff[i] = (uint32_t)row * D + ((pchunk ^ key_swz<D>(row)) << 4);
-    }
-    constexpr int vcpr = kVRowB / 16;                     // 16-byte chunks per V^T row
-#pragma unroll
-    for (int i = 0; i < kVLoads; ++i) {
-      const int slot = (i * 4 + wave) * 64 + lane;
-      const int row = slot / vcpr, pchunk = slot % vcpr;
-      voff[i] = (uint32_t)row * n_pad * kEb + ((pchunk ^ v_swz<FP8>(row)) << 4);
-    }
+  static __device__ __forceinline__ void init(uint32_t& koff, uint32_t& voff, int wave, int lane, int n_pad) {
+    const int slot = wave * 64 + lane;                    // round 0
+    const int krow = slot / (D / 16), kchunk = slot % (D / 16);
+    koff = (uint32_t)krow * D + ((kchunk ^ key_swz<D>(krow)) << 4);
+    const int vrow = slot / (kVRowB / 16), vchunk = slot % (kVRowB / 16);
+    voff = (uint32_t)vrow * n_pad * kEb + ((vchunk ^ v_swz<FP8>(vrow)) << 4);
   }
-  static __device__ __forceinline__ void issue_k(__amdgpu_buffer_rsrc_t rk, const uint32_t* koff, int wave, int k0,
+  static __device__ __forceinline__ void issue_k(__amdgpu_buffer_rsrc_t rk, uint32_t koff, int wave, int k0,
                                                  int8_t* sk) {
 #pragma unroll
     for (int i = 0; i < kKLoads; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(sk + (i * 4 + wave) * 1024),
-                                              16, koff[i], k0 * D, 0, 0);
+                                              16, koff, k0 * D + i * 4096, 0, 0);
   }
   // rv covers this head's V^T rows [D][n_pad]
-  static __device__ __forceinline__ void issue_v(__amdgpu_buffer_rsrc_t rv, const uint32_t* voff, int wave, int k0,
-                                                 uint8_t* sv) {
+  static __device__ __forceinline__ void issue_v(__amdgpu_buffer_rsrc_t rv, uint32_t voff, int wave, int k0,
+                                                 int n_pad, uint8_t* sv) {
 #pragma unroll
     for (int i = 0; i < kVLoads; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(sv + (i * 4 + wave) * 1024),
-                                              16, voff[i], k0 * kEb, 0, 0);
+                                              16, voff, (k0 + i * kVRowsPerRound * n_pad) * kEb, 0, 0);
   }
 };
 
@@ -119,17 +118,20 @@ template <int D>
 __device__ __forceinline__ void qk_tile(const int8_t* sk, const i32x4* qreg, int lane, i32x16* s) {
   const int g = lane >> 5, m = lane & 31;
   const int r0 = key_perm(m);
+  // All K operands are read before the first MFMA, so the LDS latency is paid
+  // once per tile rather than once per operand batch.
+  i32x4 ka[D / 32][kBlocks];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int b = 0; b < kBlocks; ++b) ka[t][b] = lds16(sk + k_lds_off<D>(32 * b + r0, 2 * t + g));
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int b = 0; b < kBlocks; ++b) s[b] = i32x16{};
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t) {
+  for (int t = 0; t < D / 32; ++t)
 #pragma unroll
-    for (int b = 0; b < kBlocks; ++b) {
-      const i32x4 ka = lds16(sk + k_lds_off<D>(32 * b + r0, 2 * t + g));
-      s[b] = mfma_i8(ka, qreg[t], s[b]);
-    }
-    if (t % 2 == 1) __builtin_amdgcn_sched_barrier(0);   // at most 8 K operands in flight
-  }
+    for (int b = 0; b < kBlocks; ++b) s[b] = mfma_i8(ka[t][b], qreg[t], s[b]);
 }
 
 template <int D>
@@ -198,6 +200,20 @@ __device__ __forceinline__ void attend_tile(const int8_t* sk, const uint8_t* sv,
   auto p = [&](int b, int r) { const int bits = s[b][r]; return __builtin_bit_cast(float, bits); };
 
   if constexpr (FP8) {
+    // V^T operands of 32-channel block cb: rows cb*32 + n, 16-byte chunks
+    // 4u + g and 4u + 2 + g for key half u. Read one block ahead of its MFMAs.
+    auto load_v = [&](int cb, i32x8* va) {
+      const int row = cb * 32 + n;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const i32x4 lo = lds16(sv + v_lds_off<true>(row, 4 * u + g));
+        const i32x4 hi = lds16(sv + v_lds_off<true>(row, 4 * u + 2 + g));
+        va[u] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+    };
+    i32x8 va[NT][2];
+    load_v(0, va[0]);
+    __builtin_amdgcn_sched_barrier(0);          // keep these reads ahead of the packing below
     // two 64-key halves: bytes 0..15 = block 2u, bytes 16..31 = block 2u+1
     i32x8 pk[2];
 #pragma unroll
@@ -219,18 +235,12 @@ __device__ __forceinline__ void attend_tile(const int8_t* sk, const uint8_t* sv,
       ls = mfma_fp8(ones, pk[1], ls);
       st.l = __builtin_fmaf(alpha, st.l, ls[0]);
     }
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int cb = 0; cb < NT; ++cb) {
-      const int row = cb * 32 + n;
+      if (cb + 1 < NT) load_v(cb + 1, va[cb + 1]);
       f32x16 r = f32x16{};
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const i32x4 lo = lds16(sv + v_lds_off<true>(row, 4 * u + g));
-        const i32x4 hi = lds16(sv + v_lds_off<true>(row, 4 * u + 2 + g));
-        const i32x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        r = mfma_fp8(va, pk[u], r);                                   // level 1
-      }
+      for (int u = 0; u < 2; ++u) r = mfma_fp8(va[cb][u], pk[u], r);  // level 1
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int e = 0; e < 16; ++e) st.o[cb][e] = __builtin_fmaf(alpha, st.o[cb][e], r[e]);   // level 2
@@ -279,10 +289,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   using Stage = TileStage<D, FP8>;
   // Two tile buffers as distinct objects so the compiler can tell the tile
   // being computed from the one being loaded.
-  __shared__ __attribute__((aligned(1024))) int8_t s_k0[kBkv * D];
-  __shared__ __attribute__((aligned(1024))) int8_t s_k1[kBkv * D];
-  __shared__ __attribute__((aligned(1024))) uint8_t s_v0[D * Stage::kVRowB];
-  __shared__ __attribute__((aligned(1024))) uint8_t s_v1[D * Stage::kVRowB];
+  constexpr int kKBytes = kBkv * D, kVBytes = D * Stage::kVRowB;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kKBytes + 2 * kVBytes];
+  int8_t* const s_k0 = reinterpret_cast<int8_t*>(smem);
+  int8_t* const s_k1 = reinterpret_cast<int8_t*>(smem + kKBytes);
+  uint8_t* const s_v0 = smem + 2 * kKBytes;
+  uint8_t* const s_v1 = smem + 2 * kKBytes + kVBytes;
 
   // Work decomposition. Work-groups are dealt round-robin to the 8 XCDs; give
   // each XCD a contiguous range of (head, q-tile) work so the work-groups that
@@ -321,10 +333,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
                             (uint32_t)(D * a.n_pad * eb));
 
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  uint32_t koff[Stage::kKLoads], voff[Stage::kVLoads];
+  uint32_t koff, voff;
   Stage::init(koff, voff, wv, lane, a.n_pad);
   Stage::issue_k(rk, koff, wv, 0, s_k0);
-  Stage::issue_v(rv, voff, wv, 0, s_v0);
+  Stage::issue_v(rv, voff, wv, 0, a.n_pad, s_v0);
   wait_tile_loads();
   __syncthreads();
 
@@ -335,14 +347,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   st.l = 0.0f;
 
   // One tile: prefetch the next tile into the other buffer, compute this one.
+  // K scales run one tile ahead: a scalar load shares the LDS wait counter, so a
+  // load issued in the tile that uses it would stall the first operand wait.
+  float ks0 = kscale[0], ks1 = kscale[min(1, a.nbk - 1)];
   auto step = [&](int kt, const int8_t* sk, const uint8_t* sv, int8_t* nk_buf, uint8_t* nv_buf) {
-    // scales first: their loads must not queue behind the tile prefetch
-    const float c0 = cq * kscale[min(2 * kt, a.nbk - 1)];
-    const float c1 = cq * kscale[min(2 * kt + 1, a.nbk - 1)];   // past Nk: masked anyway
+    const float c0 = cq * ks0;
+    const float c1 = cq * ks1;                     // past Nk: masked anyway
+    ks0 = kscale[min(2 * kt + 2, a.nbk - 1)];
+    ks1 = kscale[min(2 * kt + 3, a.nbk - 1)];
     // always prefetch (the last tile reloads itself into the idle buffer) so the
     // wait-count bookkeeping sees one path
     Stage::issue_k(rk, koff, wv, min(kt + 1, n_kt - 1) * kBkv, nk_buf);
-    Stage::issue_v(rv, voff, wv, min(kt + 1, n_kt - 1) * kBkv, nv_buf);
+    Stage::issue_v(rv, voff, wv, min(kt + 1, n_kt - 1) * kBkv, a.n_pad, nv_buf);
     if (kt < n_kt_wave) {
       const int k0 = kt * kBkv;
       const bool need_mask = (k0 + kBkv > a.Nk) || (CAUSAL && k0 + kBkv - 1 > q0w);
