@@ -74,20 +74,20 @@ __device__ __forceinline__ i32x4 lds16(const void* p) { return *reinterpret_cast
 // global chunk that the swizzled layout puts in its slot. Per-lane offsets do
 // not depend on the tile; the tile offset goes in the scalar offset. Rows past
 // Nk read as zeros through the buffer range check.
-template <int D, bool FP8>
+template <int D, bool FP8, int NW>
 struct TileStage {
   static constexpr int kVRowB = kBkv * (FP8 ? 1 : 2);
-  static constexpr int kKLoads = kBkv * D / 16 / 256;      // wave-wide loads per wave
-  static constexpr int kVLoads = D * kVRowB / 16 / 256;
+  static constexpr int kRound = NW * 1024;                // LDS bytes per wave-wide load round
+  static constexpr int kKLoads = kBkv * D / kRound;       // load rounds per tile
+  static constexpr int kVLoads = D * kVRowB / kRound;
   static constexpr int kEb = FP8 ? 1 : 2;
-  // Load round i covers LDS bytes [4096 i, 4096 (i+1)) of a tile: K rows
-  // 4096/D apart, V^T rows 4096/kVRowB apart. Both swizzles read only row
+  // Round i covers LDS bytes [kRound i, kRound (i+1)) of a tile: K rows
+  // kRound/D apart, V^T rows kRound/kVRowB apart. Both swizzles read only row
   // bits below those strides, so round i's global offsets are round 0's plus
   // a constant, which goes in the scalar offset: one VGPR per tensor.
-  static constexpr int kKRowsPerRound = 4096 / D;
-  static constexpr int kVRowsPerRound = 4096 / kVRowB;
-  static_assert(D == 64 || D == 128, "head dims");
-  static_assert(kKRowsPerRound >= 32 && kVRowsPerRound >= 16, "swizzle bits stay below the round stride");
+  static constexpr int kVRowsPerRound = kRound / kVRowB;
+  static_assert(kKLoads >= 1 && kVLoads >= 1, "every wave loads");
+  static_assert(kRound / D >= 32 && kVRowsPerRound >= 16, "swizzle bits stay below the round stride");
 
   static __device__ __forceinline__ void init(uint32_t& koff, uint32_t& voff, int wave, int lane, int n_pad) {
     const int slot = wave * 64 + lane;                    // round 0
@@ -100,15 +100,15 @@ struct TileStage {
                                                  int8_t* sk) {
 #pragma unroll
     for (int i = 0; i < kKLoads; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(sk + (i * 4 + wave) * 1024),
-                                              16, koff, k0 * D + i * 4096, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(sk + (i * NW + wave) * 1024),
+                                              16, koff, k0 * D + i * kRound, 0, 0);
   }
   // rv covers this head's V^T rows [D][n_pad]
   static __device__ __forceinline__ void issue_v(__amdgpu_buffer_rsrc_t rv, uint32_t voff, int wave, int k0,
                                                  int n_pad, uint8_t* sv) {
 #pragma unroll
     for (int i = 0; i < kVLoads; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(sv + (i * 4 + wave) * 1024),
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(sv + (i * NW + wave) * 1024),
                                               16, voff, (k0 + i * kVRowsPerRound * n_pad) * kEb, 0, 0);
   }
 };
@@ -118,20 +118,17 @@ template <int D>
 __device__ __forceinline__ void qk_tile(const int8_t* sk, const i32x4* qreg, int lane, i32x16* s) {
   const int g = lane >> 5, m = lane & 31;
   const int r0 = key_perm(m);
-  // All K operands are read before the first MFMA, so the LDS latency is paid
-  // once per tile rather than once per operand batch.
-  i32x4 ka[D / 32][kBlocks];
-#pragma unroll
-  for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-    for (int b = 0; b < kBlocks; ++b) ka[t][b] = lds16(sk + k_lds_off<D>(32 * b + r0, 2 * t + g));
-  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int b = 0; b < kBlocks; ++b) s[b] = i32x16{};
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t)
+  for (int t = 0; t < D / 32; ++t) {
 #pragma unroll
-    for (int b = 0; b < kBlocks; ++b) s[b] = mfma_i8(ka[t][b], qreg[t], s[b]);
+    for (int b = 0; b < kBlocks; ++b) {
+      const i32x4 ka = lds16(sk + k_lds_off<D>(32 * b + r0, 2 * t + g));
+      s[b] = mfma_i8(ka, qreg[t], s[b]);
+    }
+    if (t % 2 == 1) __builtin_amdgcn_sched_barrier(0);   // at most 8 K operands in flight
+  }
 }
 
 template <int D>
@@ -149,23 +146,46 @@ struct RowState {
   float l;
 };
 
-// One KV tile for one wave: QK^T, (masking), online softmax, P quantisation, PV.
-template <int D, bool FP8, bool CAUSAL, bool MASK, typename T>
-__device__ __forceinline__ void attend_tile(const int8_t* sk, const uint8_t* sv, const i32x4* qreg, int lane,
-                                            int k0, int qi, int nk, float c0, float c1, RowState<D>& st) {
-  constexpr int NT = D / 32;
-  const int g = lane >> 5, n = lane & 31;
-  i32x16 s[kBlocks];
-  qk_tile<D>(sk, qreg, lane, s);
+template <typename T>
+using Half8 = typename std::conditional<std::is_same<T, BF16>::value, bf16x8, f16x8>::type;
 
+// Pins a value in registers at this point: it must be computed before here and
+// cannot be sunk past it. Used to keep each phase's work inside its phase (the
+// barriers order memory only). Emits no instruction.
+template <typename V>
+__device__ __forceinline__ void pin(V& x) { asm volatile("" : "+v"(x)); }
+
+// P of one tile as the PV product consumes it, with the tile's rescale factor.
+template <bool FP8, typename T>
+struct PTile;
+template <typename T>
+struct PTile<true, T> {
+  i32x8 pk[2];       // e4m3 codes of 448 P~; pk[u]: key half u (bytes 0..15 block 2u, 16..31 block 2u+1)
+  float alpha;
+};
+template <typename T>
+struct PTile<false, T> {
+  Half8<T> ph[2 * kBlocks];   // ph[2b + h]: block b, keys 16g + 8h + 0..7
+  float alpha;
+  float lsum;                 // this lane's sum of the rounded P
+};
+
+// Softmax phase of one KV tile for one wave (vector ALU work only): mask,
+// online softmax in the log2 domain, P quantisation. s (S^T of the tile) is
+// consumed; the running max is updated; the P operand and alpha go to pt.
+template <int D, bool FP8, bool CAUSAL, bool MASK, typename T>
+__device__ __forceinline__ void softmax_phase(i32x16* s, int lane, int k0, int qi, int nk, float c0, float c1,
+                                              float& m, PTile<FP8, T>& pt) {
+  const int g = lane >> 5;
   if (MASK) {
+    // key k0 + 32b + 16g + r is visible iff 32b + r < lim (one per-lane bound
+    // against compile-time constants)
+    const int lim = (CAUSAL ? min(nk, qi + 1) : nk) - k0 - 16 * g;
 #pragma unroll
     for (int b = 0; b < kBlocks; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = k0 + 32 * b + 16 * g + r;
-        if (key >= nk || (CAUSAL && key > qi)) s[b][r] = INT_MIN;
-      }
+      for (int r = 0; r < 16; ++r)
+        if (32 * b + r >= lim) s[b][r] = INT_MIN;
   }
   // Row maximum: integer max per K quantisation block (3-input max tree), then scaled.
   int mx0 = max(s[0][0], s[1][0]), mx1 = max(s[2][0], s[3][0]);
@@ -179,8 +199,9 @@ __device__ __forceinline__ void attend_tile(const int8_t* sk, const uint8_t* sv,
     if (mx0 == INT_MIN) t0 = -INFINITY;
     if (mx1 == INT_MIN) t1 = -INFINITY;
   }
-  const float m_new = fmaxf(st.m, pair_max(fmaxf(t0, t1)));
-  const float alpha = fast_exp2(st.m - m_new);
+  const float m_new = fmaxf(m, pair_max(fmaxf(t0, t1)));
+  pt.alpha = fast_exp2(m - m_new);
+  m = m_new;
   const float bias = (FP8 ? kLog2E4m3Max : 0.0f) - m_new;   // P8 = e4m3(448 * P~) via the exponent
 
   // P~ overwrites the scores in place (as fp32 bit patterns).
@@ -194,11 +215,57 @@ __device__ __forceinline__ void attend_tile(const int8_t* sk, const uint8_t* sv,
       s[b][r] = __builtin_bit_cast(int, x);
     }
   }
-  st.m = m_new;
   // (copy the element out first: a bit-cast applied to a vector-element
   //  expression reads the vector's first element)
   auto p = [&](int b, int r) { const int bits = s[b][r]; return __builtin_bit_cast(float, bits); };
+  if constexpr (FP8) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        int x = __builtin_amdgcn_cvt_pk_fp8_f32(p(2 * u, 4 * w), p(2 * u, 4 * w + 1), 0, false);
+        pt.pk[u][w] = __builtin_amdgcn_cvt_pk_fp8_f32(p(2 * u, 4 * w + 2), p(2 * u, 4 * w + 3), x, true);
+        int y = __builtin_amdgcn_cvt_pk_fp8_f32(p(2 * u + 1, 4 * w), p(2 * u + 1, 4 * w + 1), 0, false);
+        pt.pk[u][4 + w] = __builtin_amdgcn_cvt_pk_fp8_f32(p(2 * u + 1, 4 * w + 2), p(2 * u + 1, 4 * w + 3), y, true);
+      }
+  } else {
+    using HS = typename std::conditional<std::is_same<T, BF16>::value, __bf16, _Float16>::type;
+#pragma unroll
+    for (int b = 0; b < kBlocks; ++b)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pt.ph[2 * b][e] = (HS)p(b, e);
+        pt.ph[2 * b + 1][e] = (HS)p(b, 8 + e);
+      }
+    // Row sum of the rounded P (the values the PV product consumes), two per
+    // dot instruction; each lane holds its half of the keys.
+    float lsum = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 2 * kBlocks; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) lsum = dot2_ones(pt.ph[u][e], pt.ph[u][e + 1], lsum);
+    pt.lsum = lsum;
+  }
+  if constexpr (FP8) {
+    pin(pt.pk[0]);
+    pin(pt.pk[1]);
+  } else {
+#pragma unroll
+    for (int u = 0; u < 2 * kBlocks; ++u) pin(pt.ph[u]);
+    pin(pt.lsum);
+  }
+  pin(pt.alpha);
+  pin(m);
+}
 
+// PV phase of one KV tile for one wave (matrix-core work): the row sum of the
+// quantised P, R = V^T P^T into a fresh accumulator (level 1), O = alpha O + R
+// (level 2).
+template <int D, bool FP8, typename T>
+__device__ __forceinline__ void pv_phase(const uint8_t* sv, int lane, const PTile<FP8, T>& pt, RowState<D>& st) {
+  constexpr int NT = D / 32;
+  const int g = lane >> 5, n = lane & 31;
+  const float alpha = pt.alpha;
   if constexpr (FP8) {
     // V^T operands of 32-channel block cb: rows cb*32 + n, 16-byte chunks
     // 4u + g and 4u + 2 + g for key half u. Read one block ahead of its MFMAs.
@@ -213,26 +280,14 @@ __device__ __forceinline__ void attend_tile(const int8_t* sk, const uint8_t* sv,
     };
     i32x8 va[NT][2];
     load_v(0, va[0]);
-    __builtin_amdgcn_sched_barrier(0);          // keep these reads ahead of the packing below
-    // two 64-key halves: bytes 0..15 = block 2u, bytes 16..31 = block 2u+1
-    i32x8 pk[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        int x = __builtin_amdgcn_cvt_pk_fp8_f32(p(2 * u, 4 * w), p(2 * u, 4 * w + 1), 0, false);
-        pk[u][w] = __builtin_amdgcn_cvt_pk_fp8_f32(p(2 * u, 4 * w + 2), p(2 * u, 4 * w + 3), x, true);
-        int y = __builtin_amdgcn_cvt_pk_fp8_f32(p(2 * u + 1, 4 * w), p(2 * u + 1, 4 * w + 1), 0, false);
-        pk[u][4 + w] = __builtin_amdgcn_cvt_pk_fp8_f32(p(2 * u + 1, 4 * w + 2), p(2 * u + 1, 4 * w + 3), y, true);
-      }
     // Row sum of the quantised P (the values the PV product consumes): with an
     // all-ones A operand every row of the product is the sum over the tile's
     // keys, so each lane receives its query's complete sum.
     {
       constexpr int kOnes = 0x38383838;                 // four e4m3 1.0
       const i32x8 ones = {kOnes, kOnes, kOnes, kOnes, kOnes, kOnes, kOnes, kOnes};
-      f32x16 ls = mfma_fp8(ones, pk[0], f32x16{});
-      ls = mfma_fp8(ones, pk[1], ls);
+      f32x16 ls = mfma_fp8(ones, pt.pk[0], f32x16{});
+      ls = mfma_fp8(ones, pt.pk[1], ls);
       st.l = __builtin_fmaf(alpha, st.l, ls[0]);
     }
 #pragma unroll
@@ -240,30 +295,13 @@ __device__ __forceinline__ void attend_tile(const int8_t* sk, const uint8_t* sv,
       if (cb + 1 < NT) load_v(cb + 1, va[cb + 1]);
       f32x16 r = f32x16{};
 #pragma unroll
-      for (int u = 0; u < 2; ++u) r = mfma_fp8(va[cb][u], pk[u], r);  // level 1
-      __builtin_amdgcn_sched_barrier(0);
+      for (int u = 0; u < 2; ++u) r = mfma_fp8(va[cb][u], pt.pk[u], r);  // level 1
 #pragma unroll
       for (int e = 0; e < 16; ++e) st.o[cb][e] = __builtin_fmaf(alpha, st.o[cb][e], r[e]);   // level 2
     }
   } else {
-    using H8 = typename std::conditional<std::is_same<T, BF16>::value, bf16x8, f16x8>::type;
-    using HS = typename std::conditional<std::is_same<T, BF16>::value, __bf16, _Float16>::type;
-    H8 ph[2 * kBlocks];            // ph[2b + h] = block b, keys 16g + 8h + 0..7
-#pragma unroll
-    for (int b = 0; b < kBlocks; ++b)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        ph[2 * b][e] = (HS)p(b, e);
-        ph[2 * b + 1][e] = (HS)p(b, 8 + e);
-      }
-    // Row sum of the rounded P (the values the PV product consumes), two per
-    // dot instruction; each lane holds its half of the keys.
-    float lsum = 0.0f;
-#pragma unroll
-    for (int u = 0; u < 2 * kBlocks; ++u)
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) lsum = dot2_ones(ph[u][e], ph[u][e + 1], lsum);
-    st.l = __builtin_fmaf(alpha, st.l, lsum);
+    using H8 = Half8<T>;
+    st.l = __builtin_fmaf(alpha, st.l, pt.lsum);
 #pragma unroll
     for (int cb = 0; cb < NT; ++cb) {
       const int row = cb * 32 + n;
@@ -272,73 +310,90 @@ __device__ __forceinline__ void attend_tile(const int8_t* sk, const uint8_t* sv,
       for (int u = 0; u < 2 * kBlocks; ++u) {
         // keys 32*(u/2) + 16g + 8*(u%2) + 0..7 -> 16-byte chunk 4*(u/2) + 2g + (u%2)
         const i32x4 raw = lds16(sv + v_lds_off<false>(row, 4 * (u >> 1) + 2 * g + (u & 1)));
-        r = mfma_half(__builtin_bit_cast(H8, raw), ph[u], r);          // level 1
+        r = mfma_half(__builtin_bit_cast(H8, raw), pt.ph[u], r);          // level 1
       }
 #pragma unroll
       for (int e = 0; e < 16; ++e) st.o[cb][e] = __builtin_fmaf(alpha, st.o[cb][e], r[e]);   // level 2
     }
   }
+#pragma unroll
+  for (int cb = 0; cb < NT; ++cb) pin(st.o[cb]);
+  pin(st.l);
 }
 
 // --------------------------------------------------------------- the kernel
-__device__ __forceinline__ void wait_tile_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// One work-group = 8 waves = two groups of four, each group one 128-query tile
+// (one Q quantisation block) of the same (batch, head); each wave owns 32
+// queries. The groups share the K/V tiles in LDS and run half a tile apart
+// ("ping-pong"): while one group is in its matrix phase (PV of the previous
+// tile, then QK^T of this one) the other is in its vector phase (softmax of its
+// current tile), so on every SIMD one wave keeps the matrix cores busy while
+// the other issues vector instructions. Every phase ends at a work-group
+// barrier.
+//
+// Global phase p: group 0 runs X(t) at p = 2t and Y(t) at p = 2t + 1; group 1
+// runs one phase later. X(t) = PV(t-1) + QK^T(t), Y(t) = softmax(t). K(t) is
+// read in phases 2t and 2t+1, V(t-1) in the same two phases. At the start of
+// phase 2t all waves issue the loads of K(t+1) and V(t) into the buffers that
+// K(t-1) and V(t-2) left; they must land by the end of phase 2t+1.
+constexpr int kWaves = 8;
+
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+__device__ __forceinline__ void wait_loads_barrier() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int D, bool FP8, bool CAUSAL, typename T>
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   constexpr int NT = D / 32;
-  using Stage = TileStage<D, FP8>;
-  // Two tile buffers as distinct objects so the compiler can tell the tile
-  // being computed from the one being loaded.
+  using Stage = TileStage<D, FP8, kWaves>;
   constexpr int kKBytes = kBkv * D, kVBytes = D * Stage::kVRowB;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kKBytes + 2 * kVBytes];
-  int8_t* const s_k0 = reinterpret_cast<int8_t*>(smem);
-  int8_t* const s_k1 = reinterpret_cast<int8_t*>(smem + kKBytes);
-  uint8_t* const s_v0 = smem + 2 * kKBytes;
-  uint8_t* const s_v1 = smem + 2 * kKBytes + kVBytes;
 
   // Work decomposition. Work-groups are dealt round-robin to the 8 XCDs; give
-  // each XCD a contiguous range of (head, q-tile) work so the work-groups that
+  // each XCD a contiguous range of (head, query) work so the work-groups that
   // share an XCD's L2 stream the same head's K/V tiles.
-  const int n_qt = (a.Nq + kBq - 1) / kBq;
-  const int total = n_qt * a.B * a.Hq;
+  const int n_qp = (a.Nq + 2 * kBq - 1) / (2 * kBq);
+  const int total = n_qp * a.B * a.Hq;
   int id = blockIdx.x;
   if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
-  const int bh = id / n_qt;
-  int qt = id % n_qt;
-  if (CAUSAL) qt = n_qt - 1 - qt;            // longest rows first
+  const int bh = id / n_qp;
+  int qp = id % n_qp;
+  if (CAUSAL) qp = n_qp - 1 - qp;            // longest rows first
   const int b = bh / a.Hq, h = bh % a.Hq;
   const int bhk = b * a.Hkv + h / (a.Hq / a.Hkv);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);
   const int g = lane >> 5;
-  const int q0w = qt * kBq + wave * 32;
+  const int qt = 2 * qp + grp;                 // this group's 128-query tile
+  const int q0w = qt * kBq + (wave & 3) * 32;
   const int qi = q0w + (lane & 31);
 
   i32x4 qreg[NT];
   load_q_operand<D>(a.q8 + (int64_t)bh * a.Nq * D, a.Nq, qi, g, qreg);
-  const float cq = a.q_scale[(int64_t)bh * a.nbq + qt] * a.scale_log2;
-  // k scales through the constant address space: uniform scalar loads that do
-  // not queue behind the tile prefetch in the vector-memory counter
+  const bool grp_live = qt * kBq < a.Nq;
+  const float cq = grp_live ? a.q_scale[(int64_t)bh * a.nbq + qt] * a.scale_log2 : 0.0f;
   const __attribute__((address_space(4))) float* kscale =
       (const __attribute__((address_space(4))) float*)(a.k_scale + (int64_t)bhk * a.nbk);
 
-  const int kv_end = CAUSAL ? min(a.Nk, (qt + 1) * kBq) : a.Nk;
-  const int n_kt = (kv_end + kBkv - 1) / kBkv;
-  // tiles this wave computes (waves entirely past Nq only help stage tiles)
-  const int n_kt_wave = q0w >= a.Nq ? 0 : CAUSAL ? (min(a.Nk, q0w + 32) + kBkv - 1) / kBkv : n_kt;
+  // KV tiles this group attends to, and the work-group's (the longer of the two).
+  // Only a group's last tile can need masking: it holds the ragged end of the
+  // keys and, with causal masking (Nq == Nk, query tile == KV tile), the diagonal.
+  auto tiles_for = [&](int q_tile) {
+    const int kv_end = CAUSAL ? min(a.Nk, (q_tile + 1) * kBq) : a.Nk;
+    return (kv_end + kBkv - 1) / kBkv;
+  };
+  const int n_g = grp_live ? tiles_for(qt) : 0;
+  const int n_wg = ((2 * qp + 1) * kBq < a.Nq) ? tiles_for(2 * qp + 1) : tiles_for(2 * qp);
 
   constexpr int eb = FP8 ? 1 : 2;
   const auto rk = make_rsrc(a.k8 + (int64_t)bhk * a.Nk * D, (uint32_t)a.Nk * D);
   const auto rv = make_rsrc(reinterpret_cast<const uint8_t*>(a.vt) + (int64_t)bhk * D * a.n_pad * eb,
                             (uint32_t)(D * a.n_pad * eb));
-
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   uint32_t koff, voff;
   Stage::init(koff, voff, wv, lane, a.n_pad);
-  Stage::issue_k(rk, koff, wv, 0, s_k0);
-  Stage::issue_v(rv, voff, wv, 0, a.n_pad, s_v0);
-  wait_tile_loads();
-  __syncthreads();
+  Stage::issue_k(rk, koff, wv, 0, reinterpret_cast<int8_t*>(smem));
+  wait_loads_barrier();
 
   RowState<D> st;
 #pragma unroll
@@ -346,34 +401,128 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   st.m = -INFINITY;
   st.l = 0.0f;
 
-  // One tile: prefetch the next tile into the other buffer, compute this one.
-  // K scales run one tile ahead: a scalar load shares the LDS wait counter, so a
-  // load issued in the tile that uses it would stall the first operand wait.
-  float ks0 = kscale[0], ks1 = kscale[min(1, a.nbk - 1)];
-  auto step = [&](int kt, const int8_t* sk, const uint8_t* sv, int8_t* nk_buf, uint8_t* nv_buf) {
-    const float c0 = cq * ks0;
-    const float c1 = cq * ks1;                     // past Nk: masked anyway
-    ks0 = kscale[min(2 * kt + 2, a.nbk - 1)];
-    ks1 = kscale[min(2 * kt + 3, a.nbk - 1)];
-    // always prefetch (the last tile reloads itself into the idle buffer) so the
-    // wait-count bookkeeping sees one path
-    Stage::issue_k(rk, koff, wv, min(kt + 1, n_kt - 1) * kBkv, nk_buf);
-    Stage::issue_v(rv, voff, wv, min(kt + 1, n_kt - 1) * kBkv, a.n_pad, nv_buf);
-    if (kt < n_kt_wave) {
-      const int k0 = kt * kBkv;
-      const bool need_mask = (k0 + kBkv > a.Nk) || (CAUSAL && k0 + kBkv - 1 > q0w);
-      if (need_mask)
-        attend_tile<D, FP8, CAUSAL, true, T>(sk, sv, qreg, lane, k0, qi, a.Nk, c0, c1, st);
-      else
-        attend_tile<D, FP8, CAUSAL, false, T>(sk, sv, qreg, lane, k0, qi, a.Nk, c0, c1, st);
-    }
-    wait_tile_loads();
-    __syncthreads();
+  // Buffers by tile parity, as compile-time offsets: the compiler can then tell
+  // the buffer being loaded from the one being read, and does not wait for a
+  // prefetch before an unrelated LDS read.
+  using Even = std::integral_constant<int, 0>;
+  using Odd = std::integral_constant<int, 1>;
+  i32x16 s[kBlocks];
+  PTile<FP8, T> pt;
+
+  // Phase pair t = global phases 2t and 2t+1, P = t & 1. Every pair starts with
+  // all waves issuing the loads of K(t+1) and V(t) (into the buffers K(t-1) and
+  // V(t-2) left) and ends with their wait; a plain barrier splits the pair.
+  auto loads = [&](auto par, int t) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;
+    if (t + 1 < n_wg) Stage::issue_k(rk, koff, wv, (t + 1) * kBkv, reinterpret_cast<int8_t*>(smem + (1 - P) * kKBytes));
+    if (t < n_wg) Stage::issue_v(rv, voff, wv, t * kBkv, a.n_pad, smem + 2 * kKBytes + P * kVBytes);
   };
-  for (int kt = 0; kt < n_kt; kt += 2) {
-    step(kt, s_k0, s_v0, s_k1, s_v1);
-    if (kt + 1 < n_kt) step(kt + 1, s_k1, s_v1, s_k0, s_v0);
+  auto loads_rt = [&](int t) __attribute__((always_inline)) {   // idle pairs: no LDS reads to order against
+    if (t & 1) loads(Odd{}, t); else loads(Even{}, t);
+  };
+  // X(t): PV(t-1) with V in buffer 1-P, then QK^T(t) with K in buffer P.
+  auto x_bufs = [&](const uint8_t* v_prv, const int8_t* k_cur, bool do_pv, bool do_qk) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
+    if (do_pv) pv_phase<D, FP8, T>(v_prv, lane, pt, st);
+    __builtin_amdgcn_sched_barrier(0);         // P and the V operands die before the K operands load
+    if (do_qk) qk_tile<D>(k_cur, qreg, lane, s);
+  };
+  auto x_phase = [&](auto par, int t, bool do_pv, bool do_qk) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;
+    x_bufs(smem + 2 * kKBytes + (1 - P) * kVBytes, reinterpret_cast<const int8_t*>(smem + P * kKBytes), do_pv, do_qk);
+  };
+  // The same with the parity known only at run time (the last pairs of a
+  // group): the compiler then cannot separate these reads from the prefetch in
+  // flight and waits for it first, which costs a load latency once or twice
+  // per work-group.
+  auto x_phase_rt = [&](int t, bool do_pv, bool do_qk) __attribute__((always_inline)) {
+    const int P = t & 1;
+    x_bufs(smem + 2 * kKBytes + (1 - P) * kVBytes, reinterpret_cast<const int8_t*>(smem + P * kKBytes), do_pv, do_qk);
+  };
+  // Y(t): softmax of tile t (registers only).
+  auto y_phase = [&](int t, auto masked) __attribute__((always_inline)) {
+    const float c0 = cq * kscale[min(2 * t, a.nbk - 1)];
+    const float c1 = cq * kscale[min(2 * t + 1, a.nbk - 1)];   // past Nk: masked anyway
+    __builtin_amdgcn_s_setprio(0);
+    softmax_phase<D, FP8, CAUSAL, decltype(masked)::value, T>(s, lane, t * kBkv, qi, a.Nk, c0, c1, st.m, pt);
+  };
+  using Masked = std::true_type;
+  using Full = std::false_type;
+  const int n = n_g;
+
+  if (grp == 0) {
+    // group 0, pair t: X(t) | Y(t)
+    if (n > 0) {
+      loads(Even{}, 0);
+      x_phase(Even{}, 0, false, true);
+      barrier_only();
+      if (n == 1) y_phase(0, Masked{}); else y_phase(0, Full{});
+      wait_loads_barrier();
+      auto steady = [&](auto par, int t) __attribute__((always_inline)) {
+        loads(par, t);
+        x_phase(par, t, true, true);
+        barrier_only();
+        y_phase(t, Full{});
+        wait_loads_barrier();
+      };
+      int t = 1;
+      for (; t + 1 <= n - 2; t += 2) {
+        steady(Odd{}, t);
+        steady(Even{}, t + 1);
+      }
+      if (t <= n - 2) { steady(Odd{}, t); ++t; }
+      // t == n - 1 (when n >= 2): masked last tile, then PV(n - 1) at pair n
+      if (n >= 2) {
+        loads_rt(n - 1);
+        x_phase_rt(n - 1, true, true);
+        barrier_only();
+        y_phase(n - 1, Masked{});
+        wait_loads_barrier();
+      }
+      loads_rt(n);
+      x_phase_rt(n, true, false);
+      barrier_only();
+      wait_loads_barrier();
+    }
+    for (int t = n + (n > 0 ? 1 : 0); t <= n_wg; ++t) {
+      loads_rt(t);
+      barrier_only();
+      wait_loads_barrier();
+    }
+  } else {
+    // group 1, pair t: Y(t-1) | X(t)
+    if (n > 0) {
+      loads(Even{}, 0);
+      barrier_only();
+      x_phase(Even{}, 0, false, true);
+      wait_loads_barrier();
+      auto steady = [&](auto par, int t) __attribute__((always_inline)) {
+        loads(par, t);
+        y_phase(t - 1, Full{});
+        barrier_only();
+        x_phase(par, t, true, true);
+        wait_loads_barrier();
+      };
+      int t = 1;
+      for (; t + 1 <= n - 1; t += 2) {
+        steady(Odd{}, t);
+        steady(Even{}, t + 1);
+      }
+      if (t <= n - 1) { steady(Odd{}, t); ++t; }
+      // t == n: masked last tile's softmax, then PV(n - 1)
+      loads_rt(n);
+      y_phase(n - 1, Masked{});
+      barrier_only();
+      x_phase_rt(n, true, false);
+      wait_loads_barrier();
+    }
+    for (int t = n + (n > 0 ? 1 : 0); t <= n_wg; ++t) {
+      loads_rt(t);
+      barrier_only();
+      wait_loads_barrier();
+    }
   }
+  __builtin_amdgcn_s_setprio(0);
 
   // Epilogue: normalise, undo the V scale, round, store in the caller's layout.
   if (qi < a.Nq) {
@@ -442,9 +591,9 @@ __global__ __launch_bounds__(256) void debug_qk_kernel(DebugQKArgs a) {
 // --------------------------------------------------------------- launchers
 template <int D, bool FP8, bool CAUSAL, typename T>
 static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t st) {
-  const int n_qt = (a.Nq + kBq - 1) / kBq;
-  const int grid = n_qt * a.B * a.Hq;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, FP8, CAUSAL, T>), dim3(grid), dim3(256), 0, st, a);
+  const int n_qp = (a.Nq + 2 * kBq - 1) / (2 * kBq);
+  const int grid = n_qp * a.B * a.Hq;
+  hipLaunchKernelGGL((attn_fwd_kernel<D, FP8, CAUSAL, T>), dim3(grid), dim3(64 * kWaves), 0, st, a);
   return hipGetLastError();
 }
 
