@@ -182,18 +182,25 @@ __device__ __forceinline__ void softmax_phase(i32x16* s, int lane, int k0, int q
     // against compile-time constants)
     const int lim = (CAUSAL ? min(nk, qi + 1) : nk) - k0 - 16 * g;
 #pragma unroll
-    for (int b = 0; b < kBlocks; ++b)
+    for (int bb = 0; bb < kBlocks; ++bb)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (32 * b + r >= lim) s[b][r] = INT_MIN;
+        if (32 * bb + r >= lim) s[bb][r] = INT_MIN;
   }
-  // Row maximum: integer max per K quantisation block (3-input max tree), then scaled.
-  int mx0 = max(s[0][0], s[1][0]), mx1 = max(s[2][0], s[3][0]);
+  // Row maximum per K quantisation block: four chains of one 3-input integer
+  // max per two scores (the pins keep the compiler from rebalancing them into
+  // a tree of 2-input maxima), then scaled.
+  auto si = [&](int bb, int r) { const int v = s[bb][r]; return v; };
+  int mc[kBlocks] = {si(0, 0), si(1, 0), si(2, 0), si(3, 0)};
 #pragma unroll
-  for (int r = 1; r < 16; ++r) {
-    mx0 = max(mx0, max(s[0][r], s[1][r]));
-    mx1 = max(mx1, max(s[2][r], s[3][r]));
-  }
+  for (int r = 1; r < 15; r += 2)
+#pragma unroll
+    for (int bb = 0; bb < kBlocks; ++bb) {
+      mc[bb] = max(mc[bb], max(si(bb, r), si(bb, r + 1)));
+      pin(mc[bb]);
+    }
+  const int mx0 = max(max(mc[0], si(0, 15)), max(mc[1], si(1, 15)));
+  const int mx1 = max(max(mc[2], si(2, 15)), max(mc[3], si(3, 15)));
   float t0 = (float)mx0 * c0, t1 = (float)mx1 * c1;
   if (MASK) {
     if (mx0 == INT_MIN) t0 = -INFINITY;
@@ -206,26 +213,32 @@ __device__ __forceinline__ void softmax_phase(i32x16* s, int lane, int k0, int q
 
   // P~ overwrites the scores in place (as fp32 bit patterns).
 #pragma unroll
-  for (int b = 0; b < kBlocks; ++b) {
-    const float c = b < 2 ? c0 : c1;
+  for (int bb = 0; bb < kBlocks; ++bb) {
+    const float c = bb < 2 ? c0 : c1;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float x = fast_exp2(__builtin_fmaf((float)s[b][r], c, bias));
-      if (MASK && s[b][r] == INT_MIN) x = 0.0f;
-      s[b][r] = __builtin_bit_cast(int, x);
+      const int sv = si(bb, r);
+      float x = fast_exp2(__builtin_fmaf((float)sv, c, bias));
+      if (MASK && sv == INT_MIN) x = 0.0f;
+      s[bb][r] = __builtin_bit_cast(int, x);
     }
   }
   // (copy the element out first: a bit-cast applied to a vector-element
   //  expression reads the vector's first element)
-  auto p = [&](int b, int r) { const int bits = s[b][r]; return __builtin_bit_cast(float, bits); };
+  auto p = [&](int bb, int r) { const int bits = s[bb][r]; return __builtin_bit_cast(float, bits); };
+  // The first conversion of each pair writes the low half and keeps the high
+  // half of its third operand, which the second conversion overwrites: any
+  // value serves, and reusing an input's register avoids initialising one.
+  auto bits = [&](int bb, int r) { const int v = s[bb][r]; return v; };
   if constexpr (FP8) {
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        int x = __builtin_amdgcn_cvt_pk_fp8_f32(p(2 * u, 4 * w), p(2 * u, 4 * w + 1), 0, false);
+        int x = __builtin_amdgcn_cvt_pk_fp8_f32(p(2 * u, 4 * w), p(2 * u, 4 * w + 1), bits(2 * u, 4 * w), false);
         pt.pk[u][w] = __builtin_amdgcn_cvt_pk_fp8_f32(p(2 * u, 4 * w + 2), p(2 * u, 4 * w + 3), x, true);
-        int y = __builtin_amdgcn_cvt_pk_fp8_f32(p(2 * u + 1, 4 * w), p(2 * u + 1, 4 * w + 1), 0, false);
+        int y = __builtin_amdgcn_cvt_pk_fp8_f32(p(2 * u + 1, 4 * w), p(2 * u + 1, 4 * w + 1), bits(2 * u + 1, 4 * w),
+                                                false);
         pt.pk[u][4 + w] = __builtin_amdgcn_cvt_pk_fp8_f32(p(2 * u + 1, 4 * w + 2), p(2 * u + 1, 4 * w + 3), y, true);
       }
   } else {
