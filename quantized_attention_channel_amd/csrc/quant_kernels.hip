@@ -40,7 +40,8 @@ __global__ __launch_bounds__(256) void channel_stats_kernel(
   float vm[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) { ks[e] = 0.0; vm[e] = 0.0f; }
-  for (int t = t_begin + r0; t < t_end; t += RPI) {
+#pragma unroll 4
+  for (int t = t_begin + r0; t < t_end; t += RPI) {   // (unrolled: several loads in flight)
     const int64_t off = base + (int64_t)t * geo.tok_stride;
     if (WITH_K) {
       i32x4 raw = *reinterpret_cast<const i32x4*>(k + off);
@@ -88,16 +89,30 @@ __global__ __launch_bounds__(D) void channel_finalize_kernel(
     float* __restrict__ k_mean, float* __restrict__ v_scale, float* __restrict__ v_inv) {
   const int bh = blockIdx.x, c = threadIdx.x;
   const int64_t p = (int64_t)bh * chunks * D + c;
+  // Eight independent accumulators keep eight loads in flight (a single chain
+  // would wait one memory latency per chunk); they are combined in a fixed
+  // order, so the result does not depend on timing.
+  constexpr int U = 8;
   if (WITH_K) {
-    double s = 0.0;
-    for (int i = 0; i < chunks; ++i) s += ksum_part[p + (int64_t)i * D];
-    k_mean[bh * D + c] = (float)(s / (double)N);
+    double s[U] = {};
+    int i = 0;
+    for (; i + U <= chunks; i += U)
+#pragma unroll
+      for (int u = 0; u < U; ++u) s[u] += ksum_part[p + (int64_t)(i + u) * D];
+    for (; i < chunks; ++i) s[0] += ksum_part[p + (int64_t)i * D];
+    const double total = ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
+    k_mean[bh * D + c] = (float)(total / (double)N);
   }
   if (WITH_V) {
-    float a = 0.0f;
-    for (int i = 0; i < chunks; ++i) a = fmaxf(a, vmax_part[p + (int64_t)i * D]);
-    v_scale[bh * D + c] = a / kE4m3Max;
-    v_inv[bh * D + c] = a > 0.0f ? kE4m3Max / a : 0.0f;
+    float a[U] = {};
+    int i = 0;
+    for (; i + U <= chunks; i += U)
+#pragma unroll
+      for (int u = 0; u < U; ++u) a[u] = fmaxf(a[u], vmax_part[p + (int64_t)(i + u) * D]);
+    for (; i < chunks; ++i) a[0] = fmaxf(a[0], vmax_part[p + (int64_t)i * D]);
+    const float m = fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])), fmaxf(fmaxf(a[4], a[5]), fmaxf(a[6], a[7])));
+    v_scale[bh * D + c] = m / kE4m3Max;
+    v_inv[bh * D + c] = m > 0.0f ? kE4m3Max / m : 0.0f;
   }
 }
 
