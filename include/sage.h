@@ -54,7 +54,7 @@ extern "C" {
 typedef enum sage_status {
   SAGE_OK = 0,
   SAGE_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size, bad enum, aliasing output */
-  SAGE_ERR_UNSUPPORTED = 2,      /* valid request this build does not implement (head_dim, causal Nq != Nk) */
+  SAGE_ERR_UNSUPPORTED = 2,      /* valid request the library does not implement (head_dim, causal Nq != Nk) */
   SAGE_ERR_WORKSPACE = 3,        /* workspace smaller than the query function reports */
   SAGE_ERR_HIP = 4               /* the HIP runtime rejected a launch */
 } sage_status;

@@ -1,8 +1,10 @@
 // Fused quantised attention forward for gfx950.
 //
-// One work-group = 4 waves = 128 queries of one (batch, query head); each wave
-// owns 32 queries and walks the KV sequence in tiles of 128 keys, which all four
-// waves share through LDS (double-buffered, one barrier per tile).
+// One work-group = 8 waves = two groups of 4, each group one 128-query tile of
+// the same (batch, query head); each wave owns 32 queries and walks the KV
+// sequence in tiles of 128 keys, which all eight waves share through LDS
+// (double-buffered). The two groups run half a tile apart so that the matrix
+// work of one overlaps the vector work of the other (see the kernel below).
 //
 // Per wave and tile (SageAttention's hot loop: INT8 QK^T, online softmax, P in
 // FP8 or FP16, PV with two-level accumulation -- thu-ml/SageAttention repo card,
@@ -12,7 +14,7 @@
 //      query per lane: lane l holds query l % 32 and 16 keys of every block, so
 //      each row reduction is in-lane plus one exchange with lane l ^ 32.
 //   2. Dequantise with c = s_q * s_k * sm_scale * log2(e) (one scalar per 64-key
-//      K quantisation block; the work-group is one Q block), mask only on the
+//      K quantisation block; a group is one Q block), mask only on the
 //      causal diagonal / ragged tail tile, online softmax in the log2 domain.
 //   3. P -> e4m3 (scaled by 448 through the exponent) or fp16/bf16, packed
 //      straight from registers into the B operand of the PV product: the K rows
@@ -30,7 +32,7 @@
 
 namespace sage {
 
-constexpr int kBq = 128;           // queries per work-group == the Q quantisation block
+constexpr int kBq = 128;           // queries per group == the Q quantisation block
 constexpr int kBlocks = kBkv / 32; // 32-key S^T blocks per tile
 static_assert(kBkv == 2 * kBlkK, "a tile spans two K quantisation blocks");
 
@@ -77,20 +79,20 @@ __device__ __forceinline__ i32x4 lds16(const void* p) { return *reinterpret_cast
 template <int D, bool FP8, int NW>
 struct TileStage {
   static constexpr int kVRowB = kBkv * (FP8 ? 1 : 2);
-  static constexpr int kRound = NW * 1024;                // LDS bytes per wave-wide load round
-  static constexpr int kKLoads = kBkv * D / kRound;       // load rounds per tile
-  static constexpr int kVLoads = D * kVRowB / kRound;
+  static constexpr int kPass = NW * 1024;                // LDS bytes per wave-wide load pass
+  static constexpr int kKLoads = kBkv * D / kPass;       // load passes per tile
+  static constexpr int kVLoads = D * kVRowB / kPass;
   static constexpr int kEb = FP8 ? 1 : 2;
-  // Round i covers LDS bytes [kRound i, kRound (i+1)) of a tile: K rows
-  // kRound/D apart, V^T rows kRound/kVRowB apart. Both swizzles read only row
-  // bits below those strides, so round i's global offsets are round 0's plus
+  // Load pass i covers LDS bytes [kPass i, kPass (i+1)) of a tile: K rows
+  // kPass/D apart, V^T rows kPass/kVRowB apart. Both swizzles read only row
+  // bits below those strides, so pass i's global offsets are pass 0's plus
   // a constant, which goes in the scalar offset: one VGPR per tensor.
-  static constexpr int kVRowsPerRound = kRound / kVRowB;
+  static constexpr int kVRowsPerPass = kPass / kVRowB;
   static_assert(kKLoads >= 1 && kVLoads >= 1, "every wave loads");
-  static_assert(kRound / D >= 32 && kVRowsPerRound >= 16, "swizzle bits stay below the round stride");
+  static_assert(kPass / D >= 32 && kVRowsPerPass >= 16, "swizzle bits stay below the pass stride");
 
   static __device__ __forceinline__ void init(uint32_t& koff, uint32_t& voff, int wave, int lane, int n_pad) {
-    const int slot = wave * 64 + lane;                    // round 0
+    const int slot = wave * 64 + lane;                    // pass 0
     const int krow = slot / (D / 16), kchunk = slot % (D / 16);
     koff = (uint32_t)krow * D + ((kchunk ^ key_swz<D>(krow)) << 4);
     const int vrow = slot / (kVRowB / 16), vchunk = slot % (kVRowB / 16);
@@ -101,7 +103,7 @@ struct TileStage {
 #pragma unroll
     for (int i = 0; i < kKLoads; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(sk + (i * NW + wave) * 1024),
-                                              16, koff, k0 * D + i * kRound, 0, 0);
+                                              16, koff, k0 * D + i * kPass, 0, 0);
   }
   // rv covers this head's V^T rows [D][n_pad]
   static __device__ __forceinline__ void issue_v(__amdgpu_buffer_rsrc_t rv, uint32_t voff, int wave, int k0,
@@ -109,7 +111,7 @@ struct TileStage {
 #pragma unroll
     for (int i = 0; i < kVLoads; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(sv + (i * NW + wave) * 1024),
-                                              16, voff, (k0 + i * kVRowsPerRound * n_pad) * kEb, 0, 0);
+                                              16, voff, (k0 + i * kVRowsPerPass * n_pad) * kEb, 0, 0);
   }
 };
 
