@@ -231,3 +231,41 @@ def test_workload_full_size(w, pv, nrows):
     assert np.isfinite(got).all()
     assert c >= COS_ORACLE and r <= RL1_ORACLE
     assert ce >= (0.9975 if w.outliers else COS_EXACT)
+
+
+# ------------------------------------------------------------------ the longest sequence the ABI accepts
+@pytest.mark.parametrize("causal", [False, True], ids=["noncausal", "causal"])
+def test_maximum_sequence_length(causal):
+    """N = 2^20 keys and queries (the ABI's limit): integer stages in full,
+    float output on rows at both ends and in between (buffer offsets, tile
+    counts and grid at their largest)."""
+    n = 1 << 20
+    w = W.PEAK.with_(B=1, Hq=1, Hkv=1, N=n, causal=causal)
+    say("maximum length", n, "causal" if causal else "")
+    q, k, v = W.generate(w)
+    qg, kg, vg = _gpu(q, k, v)
+    o = sage.sage_attn_fwd(qg, kg, vg, is_causal=causal, sm_scale=w.sm_scale, pv_dtype="fp8")
+    quant = sage.sage_quant_qk(qg, kg)
+    vcodes, vscale = sage.sage_quant_v(vg)
+    torch.cuda.synchronize()
+    del qg, kg, vg
+    qn, kn, vn = _np_inputs(q, k, v, "HND")
+    parts = sage_ref.quant_qk(qn, kn)
+    assert np.array_equal(_cpu(quant["k_mean"]).numpy(), parts["k_mean"])
+    assert np.array_equal(_cpu(quant["q_scale"]).numpy(), parts["q_scale"])
+    assert np.array_equal(_cpu(quant["k_scale"]).numpy(), parts["k_scale"])
+    assert np.array_equal(_cpu(quant["q_codes"]).numpy(), parts["q8"])
+    assert np.array_equal(_cpu(quant["k_codes"]).numpy(), parts["k8"])
+    parts["v8"], parts["v_scale"] = sage_ref.quant_v_fp8(vn)
+    assert np.array_equal(_cpu(vscale).numpy(), parts["v_scale"])
+    assert np.array_equal(_cpu(vcodes).numpy()[..., :n], parts["v8"])
+    rows = np.array([0, 1, 127, 128, n // 2 + 77, n - 129, n - 1])
+    got = o.float().cpu().numpy()[:, :, rows]
+    ref = sage_ref.sage_attention(qn, kn, vn, dtype="fp16", is_causal=causal, sm_scale=w.sm_scale, pv="fp8",
+                                  rows=rows, parts=parts)
+    ex = exact.exact_attention(qn, kn, vn, is_causal=causal, sm_scale=w.sm_scale, rows=rows)
+    c, r, ce = cos(got, ref), rel_l1(got, ref), cos(got, ex)
+    say(f"   cos={c:.7f} rel_l1={r:.2e} cos_exact={ce:.6f}")
+    assert np.isfinite(got).all()
+    assert c >= COS_ORACLE and r <= RL1_ORACLE
+    assert ce >= COS_EXACT
