@@ -348,9 +348,10 @@ __device__ __forceinline__ void pv_phase(const uint8_t* sv, int lane, const PTil
 //
 // Global phase p: group 0 runs X(t) at p = 2t and Y(t) at p = 2t + 1; group 1
 // runs one phase later. X(t) = PV(t-1) + QK^T(t), Y(t) = softmax(t). K(t) is
-// read in phases 2t and 2t+1, V(t-1) in the same two phases. At the start of
-// phase 2t all waves issue the loads of K(t+1) and V(t) into the buffers that
-// K(t-1) and V(t-2) left; they must land by the end of phase 2t+1.
+// read in phases 2t and 2t+1, V(t-1) in the same two phases. In phase 2t
+// group 0 issues the loads of K(t+1) and V(t) into the buffers that K(t-1) and
+// V(t-2) left (after its matrix work in the steady pairs); they must land by
+// the end of phase 2t+1.
 constexpr int kWaves = 8;
 
 __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
@@ -407,6 +408,15 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   uint32_t koff, voff;
   Stage::init(koff, voff, wv, lane, a.n_pad);
+  // After the first tile, group 0's four waves load each pair's tiles, at the
+  // end of their matrix phase (before it in the last two pairs, where the
+  // buffer parity is known only at run time). That phase ends before group 1's
+  // softmax phase, so the wait for the address unit to take the loads falls
+  // into time group 0 would spend at the barrier, and no other wave issues
+  // loads.
+  using StageG = TileStage<D, FP8, 4>;
+  uint32_t koffg, voffg;
+  StageG::init(koffg, voffg, wv & 3, lane, a.n_pad);
   Stage::issue_k(rk, koff, wv, 0, reinterpret_cast<int8_t*>(smem));
   wait_loads_barrier();
 
@@ -424,13 +434,14 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   i32x16 s[kBlocks];
   PTile<FP8, T> pt;
 
-  // Phase pair t = global phases 2t and 2t+1, P = t & 1. Every pair starts with
-  // all waves issuing the loads of K(t+1) and V(t) (into the buffers K(t-1) and
-  // V(t-2) left) and ends with their wait; a plain barrier splits the pair.
+  // Phase pair t = global phases 2t and 2t+1, P = t & 1. In its first phase
+  // group 0 issues the loads of K(t+1) and V(t) (into the buffers K(t-1) and
+  // V(t-2) left); the pair ends with their wait, and a plain barrier splits it.
   auto loads = [&](auto par, int t) __attribute__((always_inline)) {
     constexpr int P = decltype(par)::value;
-    if (t + 1 < n_wg) Stage::issue_k(rk, koff, wv, (t + 1) * kBkv, reinterpret_cast<int8_t*>(smem + (1 - P) * kKBytes));
-    if (t < n_wg) Stage::issue_v(rv, voff, wv, t * kBkv, a.n_pad, smem + 2 * kKBytes + P * kVBytes);
+    if (t + 1 < n_wg)
+      StageG::issue_k(rk, koffg, wv & 3, (t + 1) * kBkv, reinterpret_cast<int8_t*>(smem + (1 - P) * kKBytes));
+    if (t < n_wg) StageG::issue_v(rv, voffg, wv & 3, t * kBkv, a.n_pad, smem + 2 * kKBytes + P * kVBytes);
   };
   auto loads_rt = [&](int t) __attribute__((always_inline)) {   // idle pairs: no LDS reads to order against
     if (t & 1) loads(Odd{}, t); else loads(Even{}, t);
@@ -468,14 +479,14 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   if (grp == 0) {
     // group 0, pair t: X(t) | Y(t)
     if (n > 0) {
-      loads(Even{}, 0);
       x_phase(Even{}, 0, false, true);
+      loads(Even{}, 0);
       barrier_only();
       if (n == 1) y_phase(0, Masked{}); else y_phase(0, Full{});
       wait_loads_barrier();
       auto steady = [&](auto par, int t) __attribute__((always_inline)) {
-        loads(par, t);
         x_phase(par, t, true, true);
+        loads(par, t);
         barrier_only();
         y_phase(t, Full{});
         wait_loads_barrier();
@@ -507,12 +518,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   } else {
     // group 1, pair t: Y(t-1) | X(t)
     if (n > 0) {
-      loads(Even{}, 0);
       barrier_only();
       x_phase(Even{}, 0, false, true);
       wait_loads_barrier();
       auto steady = [&](auto par, int t) __attribute__((always_inline)) {
-        loads(par, t);
         y_phase(t - 1, Full{});
         barrier_only();
         x_phase(par, t, true, true);
@@ -525,14 +534,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
       }
       if (t <= n - 1) { steady(Odd{}, t); ++t; }
       // t == n: masked last tile's softmax, then PV(n - 1)
-      loads_rt(n);
       y_phase(n - 1, Masked{});
       barrier_only();
       x_phase_rt(n, true, false);
       wait_loads_barrier();
     }
     for (int t = n + (n > 0 ? 1 : 0); t <= n_wg; ++t) {
-      loads_rt(t);
       barrier_only();
       wait_loads_barrier();
     }

@@ -9,7 +9,8 @@ pairs -- and checks for every tile count a launch can see:
 
 * both groups arrive at the same number of barriers, of the same kinds in the
   same order (a mismatch would hang the work-group);
-* both groups issue the loads of pair t in the same phase;
+* the loads of pair t are issued once, by group 0, in the pair's first phase
+  (after its matrix work in the steady pairs, before it in the last two);
 * every LDS read finds the tile it expects in its buffer, and no load in
   flight targets a buffer that is being read;
 * each group reads every K and V tile it attends to exactly once, in order.
@@ -37,9 +38,12 @@ def group_events(grp, n, n_wg):
         if qk:
             ev.append(('read_k', t))
 
-    def pair(t, first, second):
-        ev.append(('loads', t))
+    def pair(t, first, second, loads_after=False):
+        if grp == 0 and not loads_after:
+            ev.append(('loads', t))
         first()
+        if grp == 0 and loads_after:
+            ev.append(('loads', t))
         ev.append(bar)
         second()
         ev.append(barw)
@@ -47,14 +51,14 @@ def group_events(grp, n, n_wg):
     nothing = lambda: None
     if grp == 0:                                   # pair t: X(t) | Y(t)
         if n > 0:
-            pair(0, lambda: x(0, False, True), nothing)
+            pair(0, lambda: x(0, False, True), nothing, loads_after=True)
             t = 1
             while t + 1 <= n - 2:
                 for tt in (t, t + 1):
-                    pair(tt, lambda tt=tt: x(tt, True, True), nothing)
+                    pair(tt, lambda tt=tt: x(tt, True, True), nothing, loads_after=True)
                 t += 2
             if t <= n - 2:
-                pair(t, lambda: x(t, True, True), nothing)
+                pair(t, lambda: x(t, True, True), nothing, loads_after=True)
             if n >= 2:
                 pair(n - 1, lambda: x(n - 1, True, True), nothing)
             pair(n, lambda: x(n, True, False), nothing)
@@ -92,9 +96,12 @@ def check_work_group(nq, nk, causal, qp):
     kbuf = {0: 0, 1: None}                          # K(0) is staged before the first phase
     vbuf = {0: None, 1: None}
     pending = []
+    issued_all = []
     for p in range(len(kinds[0])):
         issued = [[e[1] for e in phases[g][p] if e[0] == 'loads'] for g in (0, 1)]
-        assert issued[0] == issued[1], "loads of a pair are issued in the same phase"
+        assert issued[1] == [], "group 1 issues no loads"
+        assert issued[0] == ([p // 2] if p % 2 == 0 else []), "pair t's loads in its first phase"
+        issued_all += issued[0]
         for t in issued[0]:
             if t + 1 < n_wg:
                 pending.append(('k', (t + 1) & 1, t + 1))
@@ -111,6 +118,7 @@ def check_work_group(nq, nk, causal, qp):
             for kind, b, t in pending:
                 (kbuf if kind == 'k' else vbuf)[b] = t
             pending = []
+    assert issued_all == list(range(n_wg + 1)), "every pair's loads are issued once"
     for g in (0, 1):
         assert [e[1] for e in evs[g] if e[0] == 'read_k'] == list(range(ns[g]))
         assert [e[1] for e in evs[g] if e[0] == 'read_v'] == list(range(ns[g]))
