@@ -91,10 +91,14 @@ struct TileStage {
   static_assert(kKLoads >= 1 && kVLoads >= 1, "every wave loads");
   static_assert(kPass / D >= 32 && kVRowsPerPass >= 16, "swizzle bits stay below the pass stride");
 
-  static __device__ __forceinline__ void init(uint32_t& koff, uint32_t& voff, int wave, int lane, int n_pad) {
+  static __device__ __forceinline__ uint32_t init_k(int wave, int lane) {
     const int slot = wave * 64 + lane;                    // pass 0
     const int krow = slot / (D / 16), kchunk = slot % (D / 16);
-    koff = (uint32_t)krow * D + ((kchunk ^ key_swz<D>(krow)) << 4);
+    return (uint32_t)krow * D + ((kchunk ^ key_swz<D>(krow)) << 4);
+  }
+  static __device__ __forceinline__ void init(uint32_t& koff, uint32_t& voff, int wave, int lane, int n_pad) {
+    const int slot = wave * 64 + lane;                    // pass 0
+    koff = init_k(wave, lane);
     const int vrow = slot / (kVRowB / 16), vchunk = slot % (kVRowB / 16);
     voff = (uint32_t)vrow * n_pad * kEb + ((vchunk ^ v_swz<FP8>(vrow)) << 4);
   }
@@ -406,8 +410,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   const auto rv = make_rsrc(reinterpret_cast<const uint8_t*>(a.vt) + (int64_t)bhk * D * a.n_pad * eb,
                             (uint32_t)(D * a.n_pad * eb));
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  uint32_t koff, voff;
-  Stage::init(koff, voff, wv, lane, a.n_pad);
+  // All eight waves load the first K tile.
+  const uint32_t koff = Stage::init_k(wv, lane);
   // After the first tile, group 0's four waves load each pair's tiles, at the
   // end of their matrix phase (before it in the last two pairs, where the
   // buffer parity is known only at run time). That phase ends before group 1's
@@ -443,7 +447,8 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
       StageG::issue_k(rk, koffg, wv & 3, (t + 1) * kBkv, reinterpret_cast<int8_t*>(smem + (1 - P) * kKBytes));
     if (t < n_wg) StageG::issue_v(rv, voffg, wv & 3, t * kBkv, a.n_pad, smem + 2 * kKBytes + P * kVBytes);
   };
-  auto loads_rt = [&](int t) __attribute__((always_inline)) {   // idle pairs: no LDS reads to order against
+  // (the last pairs and the idle pairs: runtime parity)
+  auto loads_rt = [&](int t) __attribute__((always_inline)) {
     if (t & 1) loads(Odd{}, t); else loads(Even{}, t);
   };
   // X(t): PV(t-1) with V in buffer 1-P, then QK^T(t) with K in buffer P.
