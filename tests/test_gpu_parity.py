@@ -145,6 +145,44 @@ def test_attention_small_all_rows(w, pv):
     assert ce >= (0.9975 if w.outliers else COS_EXACT)
 
 
+# Cross attention (non-causal, Nq != Nk): the key tiles a work-group walks depend
+# on Nk alone, the query tiles on Nq (ragged key tails, a single key, a single
+# query, a second query group with no rows, grouped-query heads).
+CROSS_CASES = [
+    (W.TINY.with_(B=1, Hq=2, Hkv=2, d=128), 300, 1000, "fp8"),
+    (W.TINY.with_(B=2, Hq=4, Hkv=2, d=64), 1000, 129, "fp16"),
+    (W.TINY.with_(B=1, Hq=4, Hkv=1, d=128, dtype="bf16", layout="NHD"), 129, 2000, "fp8"),
+    (W.TINY.with_(B=1, Hq=2, Hkv=2, d=64), 1, 700, "fp8"),
+    (W.TINY.with_(B=1, Hq=2, Hkv=2, d=128), 513, 1, "fp16"),
+    (W.TINY.with_(B=1, Hq=2, Hkv=2, d=128), 200, 333, "fp16"),
+]
+
+
+def _cut_tokens(t, n, layout):
+    return (t[:, :, :n] if layout == "HND" else t[:, :n]).contiguous()
+
+
+@pytest.mark.parametrize("w,nq,nk,pv", CROSS_CASES,
+                         ids=[f"{w.B}x{w.Hq}/{w.Hkv}xq{nq}k{nk}x{w.d}{w.dtype}{w.layout}-{pv}"
+                              for w, nq, nk, pv in CROSS_CASES])
+def test_cross_attention_all_rows(w, nq, nk, pv):
+    say("cross attn", w, nq, nk, pv)
+    q, k, v = W.generate(w.with_(N=max(nq, nk)))
+    q, k, v = _cut_tokens(q, nq, w.layout), _cut_tokens(k, nk, w.layout), _cut_tokens(v, nk, w.layout)
+    o = sage.sage_attn_fwd(*_gpu(q, k, v), is_causal=False, sm_scale=w.sm_scale, pv_dtype=pv, tensor_layout=w.layout)
+    torch.cuda.synchronize()
+    got = sage_ref.as_hnd(o.float().cpu().numpy(), w.layout)
+    assert got.shape == (w.B, w.Hq, nq, w.d)
+    qn, kn, vn = _np_inputs(q, k, v, w.layout)
+    ref = sage_ref.sage_attention(qn, kn, vn, dtype=w.dtype, is_causal=False, sm_scale=w.sm_scale, pv=pv)
+    ex = exact.exact_attention(qn, kn, vn, is_causal=False, sm_scale=w.sm_scale)
+    c, r, ce = cos(got, ref), rel_l1(got, ref), cos(got, ex)
+    say(f"   cos={c:.7f} rel_l1={r:.2e} cos_exact={ce:.6f}")
+    assert np.isfinite(got).all()
+    assert c >= COS_ORACLE and r <= RL1_ORACLE
+    assert ce >= COS_EXACT
+
+
 def test_attention_zero_q_is_uniform():
     """Closed form: Q = 0 gives uniform weights; the output is the mean of V over
     visible keys (dequantised V in FP8 mode)."""
