@@ -119,19 +119,31 @@ struct TileStage {
   }
 };
 
+// Scores as floats without a conversion instruction. For any INT8 codes
+// (-128 included) |S| <= D * 128 * 128 < 2^22 at D <= 128, so the integer
+// kScoreOffset + S is the fp32 bit pattern of the float kScoreOffsetF + S
+// exactly (floats in [2^23, 2^24] are the integers there), and one exact
+// subtraction gives float(S). The product chain adds the offset
+// for free when it starts from it instead of zero; the integer order of the
+// offset codes is that of S, so the row maximum still runs on integers.
+constexpr int kScoreOffset = 0x4B400000;
+constexpr float kScoreOffsetF = 12582912.0f;   // 1.5 * 2^23
+static_assert(128 * 128 * 128 < (1 << 22), "scores of the largest head dimension stay inside the offset binade");
+__device__ __forceinline__ float as_f32(int v) { return __builtin_bit_cast(float, v); }
+
 // S^T for the 128 keys of the staged tile against this wave's 32 queries.
+// Every product chain starts from c0: zero gives S itself, kScoreOffset in
+// every element gives the fp32 bit patterns of kScoreOffsetF + S.
 template <int D>
-__device__ __forceinline__ void qk_tile(const int8_t* sk, const i32x4* qreg, int lane, i32x16* s) {
+__device__ __forceinline__ void qk_tile(const int8_t* sk, const i32x4* qreg, int lane, i32x16* s, const i32x16& c0) {
   const int g = lane >> 5, m = lane & 31;
   const int r0 = key_perm(m);
-#pragma unroll
-  for (int b = 0; b < kBlocks; ++b) s[b] = i32x16{};
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) {
 #pragma unroll
     for (int b = 0; b < kBlocks; ++b) {
       const i32x4 ka = lds16(sk + k_lds_off<D>(32 * b + r0, 2 * t + g));
-      s[b] = mfma_i8(ka, qreg[t], s[b]);
+      s[b] = mfma_i8(ka, qreg[t], t == 0 ? c0 : s[b]);
     }
     if (t % 2 == 1) __builtin_amdgcn_sched_barrier(0);   // at most 8 K operands in flight
   }
@@ -207,7 +219,10 @@ __device__ __forceinline__ void softmax_phase(i32x16* s, int lane, int k0, int q
     }
   const int mx0 = max(max(mc[0], si(0, 15)), max(mc[1], si(1, 15)));
   const int mx1 = max(max(mc[2], si(2, 15)), max(mc[3], si(3, 15)));
-  float t0 = (float)mx0 * c0, t1 = (float)mx1 * c1;
+  // (FP8 P: the scores carry kScoreOffset; FP16 P keeps plain S and the
+  //  conversion, since the 16 registers of the offset block do not fit there)
+  auto sf = [&](int v) { return FP8 ? as_f32(v) - kScoreOffsetF : (float)v; };
+  float t0 = sf(mx0) * c0, t1 = sf(mx1) * c1;
   if (MASK) {
     if (mx0 == INT_MIN) t0 = -INFINITY;
     if (mx1 == INT_MIN) t1 = -INFINITY;
@@ -224,7 +239,7 @@ __device__ __forceinline__ void softmax_phase(i32x16* s, int lane, int k0, int q
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int sv = si(bb, r);
-      float x = fast_exp2(__builtin_fmaf((float)sv, c, bias));
+      float x = fast_exp2(__builtin_fmaf(sf(sv), c, bias));
       if (MASK && sv == INT_MIN) x = 0.0f;
       s[bb][r] = __builtin_bit_cast(int, x);
     }
@@ -437,6 +452,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   using Odd = std::integral_constant<int, 1>;
   i32x16 s[kBlocks];
   PTile<FP8, T> pt;
+  // The start value of every QK^T chain, kept in registers (opaque, so that
+  // it is not rebuilt per tile): the score offset for FP8 P, else zero.
+  i32x16 qk_init;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) qk_init[e] = FP8 ? kScoreOffset : 0;
+  if constexpr (FP8) pin(qk_init);
 
   // Phase pair t = global phases 2t and 2t+1, P = t & 1. In its first phase
   // group 0 issues the loads of K(t+1) and V(t) (into the buffers K(t-1) and
@@ -456,7 +477,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
     __builtin_amdgcn_s_setprio(1);
     if (do_pv) pv_phase<D, FP8, T>(v_prv, lane, pt, st);
     __builtin_amdgcn_sched_barrier(0);         // P and the V operands die before the K operands load
-    if (do_qk) qk_tile<D>(k_cur, qreg, lane, s);
+    if (do_qk) qk_tile<D>(k_cur, qreg, lane, s, qk_init);
   };
   auto x_phase = [&](auto par, int t, bool do_pv, bool do_qk) __attribute__((always_inline)) {
     constexpr int P = decltype(par)::value;
@@ -601,7 +622,7 @@ __global__ __launch_bounds__(256) void debug_qk_kernel(DebugQKArgs a) {
           buf_load16(rk, (uint32_t)(k0 + ci / (D / 16)) * D + (ci % (D / 16)) * 16);
     __syncthreads();
     i32x16 s[kBlocks];
-    qk_tile<D>(s_k, qreg, lane, s);
+    qk_tile<D>(s_k, qreg, lane, s, i32x16{});
     if (qi < a.Nq) {
       int32_t* row = a.s_out + ((int64_t)bh * a.Nq + qi) * a.Nk;
 #pragma unroll
