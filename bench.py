@@ -15,7 +15,8 @@ roofline     = the attention kernel alone: the same counted operations / its
 cpu_baseline = the CPU oracle on a bounded sample of the same workload.
 
 Default workload: B=1, H=32, N=32768, d=128, fp16, non-causal, PV in e4m3 (the
-long-sequence peak workload); the causal variant is reported alongside.
+long-sequence peak workload), per-block Q/K scales; the causal variant and the
+per-thread-scale variant are reported alongside.
 """
 from __future__ import annotations
 
@@ -61,12 +62,12 @@ def counted_ops(w: W.Workload) -> float:
 class Plan:
     """Preallocated buffers and the three C-ABI calls of one step."""
 
-    def __init__(self, w: W.Workload, pv: str, q, k, v):
+    def __init__(self, w: W.Workload, pv: str, q, k, v, qk_gran: str = "per_block"):
         import quantized_attention_channel_amd as sage
         self.sage, self.w, self.pv = sage, w, pv
-        self.shape = sage.shape_of(q, k, w.layout)
+        self.shape = sage.shape_of(q, k, w.layout, qk_gran)
         s = self.shape
-        blk_q, blk_k, _ = sage.sage_block_sizes(w.d)
+        blk_q, blk_k, _ = sage.sage_block_sizes(w.d, qk_gran)
         dev = q.device
         npad = sage.sage_v_codes_stride(w.N)
         self.q, self.k, self.v = q, k, v
@@ -162,7 +163,7 @@ def counters_traffic():
     return (fetch * ff + write * fw) * 1024.0, sha
 
 
-def cpu_baseline(w: W.Workload, pv: str, rows: int):
+def cpu_baseline(w: W.Workload, pv: str, rows: int, qk_gran: str = "per_block"):
     """The oracle, as it stands, on a bounded sample: batch 0 / head 0 of the
     workload, its Q/K/V quantisation in full and `rows` query rows of attention."""
     import numpy as np
@@ -177,8 +178,10 @@ def cpu_baseline(w: W.Workload, pv: str, rows: int):
     qn, kn, vn = (t.float().numpy() for t in (q, k, v))
     sel = np.linspace(0, w.N - 1, rows).round().astype(np.int64)
     t0 = time.perf_counter()
+    blk = ((sage_ref.PER_THREAD_BLK_Q, sage_ref.PER_THREAD_BLK_K) if qk_gran == "per_thread"
+           else (sage_ref.BLK_Q, sage_ref.BLK_K))
     sage_ref.sage_attention(qn, kn, vn, dtype=w.dtype, is_causal=w.causal, sm_scale=w.sm_scale, pv=pv,
-                            layout=w.layout, rows=np.unique(sel))
+                            layout=w.layout, rows=np.unique(sel), blk_q=blk[0], blk_k=blk[1])
     dt = time.perf_counter() - t0
     if w.causal:
         ops = float(sum(4.0 * (int(i) + 1) * w.d for i in np.unique(sel)))
@@ -202,9 +205,9 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
 
 
-def measure(w: W.Workload, pv: str, steps: int, warmup: int):
+def measure(w: W.Workload, pv: str, steps: int, warmup: int, qk_gran: str = "per_block"):
     q, k, v = W.generate(w, device="cuda")
-    plan = Plan(w, pv, q, k, v)
+    plan = Plan(w, pv, q, k, v, qk_gran)
     wall_ms, gpu_ms, quant_ms, attn_ms = time_steps(plan, steps, warmup)
     fused_ms = time_fused_entry(plan, max(3, steps // 4))
     ops = counted_ops(w)
@@ -221,7 +224,10 @@ def main():
     ap.add_argument("--workload", default="peak", help="peak|tiny|mid|gqa|long or a full workload name")
     ap.add_argument("--pv", default=None, help="fp8|fp16 (default: the workload's)")
     ap.add_argument("--causal", type=int, default=None, help="override the workload's causal flag")
-    ap.add_argument("--no-variants", action="store_true", help="skip the causal variant of the peak workload")
+    ap.add_argument("--qk-gran", default="per_block", choices=["per_block", "per_thread"],
+                    help="granularity of the Q/K INT8 scales")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the causal and per-thread variants of the peak workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=8192)
     ap.add_argument("--copy-calibration", action="store_true", help="run only a 1 GiB device copy")
@@ -244,11 +250,12 @@ def main():
         w = w.with_(causal=bool(args.causal))
     pv = args.pv or w.pv
 
-    r = measure(w, pv, args.steps, args.warmup)
+    r = measure(w, pv, args.steps, args.warmup, args.qk_gran)
     traffic, counters_sha = counters_traffic()
     roof = {"bound": "mfma", "achieved": round(r["attn_tops"], 2), "peak": PEAK_TOPS, "unit": "TFLOP/s",
             "frac": round(r["attn_tops"] / PEAK_TOPS, 4), "traffic": traffic,
-            "kernel": "attn_fwd_kernel", "ops_per_launch": counted_ops(w),
+            "kernel": "attn_fwd_fine_kernel" if args.qk_gran == "per_thread" else "attn_fwd_kernel",
+            "ops_per_launch": counted_ops(w),
             "mean_launch_ms": round(r["attn_ms"], 4)}
     out = {
         "metric": METRIC, "value": round(r["tops"], 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
@@ -256,7 +263,8 @@ def main():
         "vs_baseline": None, "dtype": "int8+fp8_e4m3" if pv == "fp8" else f"int8+{w.dtype}",
         "data": "synthetic: seeded normal Q/K/V, per-channel K offsets (workloads.py)",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
-                   "causal": w.causal, "pv": pv, "layout": w.layout, "input_dtype": w.dtype},
+                   "causal": w.causal, "pv": pv, "layout": w.layout, "input_dtype": w.dtype,
+                   "qk_gran": args.qk_gran},
         "mfma_peak_frac": round(r["tops"] / PEAK_TOPS, 4),
         "roofline": roof,
         "breakdown_ms": {"gpu_step": round(r["gpu_ms"], 4), "quant": round(r["quant_ms"], 4),
@@ -265,15 +273,16 @@ def main():
                       "GBps": round(r["quant_bytes"] / (r["quant_ms"] * 1e-3) / 1e9, 1),
                       "frac_of_8TBps": round(r["quant_bytes"] / (r["quant_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
     }
-    if w is W.PEAK and not args.no_variants:
-        wc = w.with_(causal=True)
-        rc = measure(wc, pv, args.steps, args.warmup)
-        out["variants"] = {"causal": {"value": round(rc["tops"], 2), "ms_per_step": round(rc["wall_ms"], 4),
-                                      "attention_tops": round(rc["attn_tops"], 2),
-                                      "attention_frac": round(rc["attn_tops"] / PEAK_TOPS, 4),
-                                      "attention_ms": round(rc["attn_ms"], 4)}}
+    if w is W.PEAK and args.qk_gran == "per_block" and not args.no_variants:
+        def variant(rv):
+            return {"value": round(rv["tops"], 2), "ms_per_step": round(rv["wall_ms"], 4),
+                    "attention_tops": round(rv["attn_tops"], 2),
+                    "attention_frac": round(rv["attn_tops"] / PEAK_TOPS, 4),
+                    "attention_ms": round(rv["attn_ms"], 4), "quant_ms": round(rv["quant_ms"], 4)}
+        out["variants"] = {"causal": variant(measure(w.with_(causal=True), pv, args.steps, args.warmup)),
+                           "per_thread": variant(measure(w, pv, args.steps, args.warmup, "per_thread"))}
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, pv, args.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline(w, pv, args.cpu_rows, args.qk_gran)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

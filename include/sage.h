@@ -64,6 +64,15 @@ typedef enum sage_dtype { SAGE_DTYPE_F16 = 0, SAGE_DTYPE_BF16 = 1 } sage_dtype;
 /* PV product precision (repo card "How it works": FP16 or FP8 for PV).
  * SAGE_PV_FP16 keeps P and V in the input dtype (fp16, or bf16 for bf16 inputs). */
 typedef enum sage_pv_dtype { SAGE_PV_FP16 = 0, SAGE_PV_FP8_E4M3 = 1 } sage_pv_dtype;
+/* Granularity of the Q and K INT8 scales (heatdrop.ai review, "The interesting
+ * bit": per-thread quantisation alongside the outlier smoothing).
+ *   SAGE_QK_PER_BLOCK   BLK_Q = 128 query tokens and BLK_K = 64 key tokens per scale.
+ *   SAGE_QK_PER_THREAD  one scale per group of tokens that a single lane of the
+ *                       attention kernel's matrix instructions holds: every
+ *                       query token alone (BLK_Q = 1) and every run of 16
+ *                       consecutive keys (BLK_K = 16).
+ * Zero is per-block, so a zero-initialised shape keeps the per-block scales. */
+typedef enum sage_qk_gran { SAGE_QK_PER_BLOCK = 0, SAGE_QK_PER_THREAD = 1 } sage_qk_gran;
 
 typedef struct sage_shape {
   int32_t batch;     /* B   */
@@ -74,15 +83,17 @@ typedef struct sage_shape {
   int32_t head_dim;  /* d   */
   int32_t layout;    /* sage_layout of q, k, v and o */
   int32_t dtype;     /* sage_dtype of q, k, v and o  */
+  int32_t qk_gran;   /* sage_qk_gran of the Q and K scales */
 } sage_shape;
 
-/* Quantisation block sizes and the online-softmax KV tile for `head_dim`.
- * BLK_Q query tokens / BLK_K key tokens share one INT8 scale (blocks start at
- * token 0, the last one may be short); the softmax walks KV tiles of BKV keys
- * from key 0 upward, so BKV is part of the result's definition (P's FP8 codes
- * depend on the running row max).
- * Returns SAGE_ERR_UNSUPPORTED for other head dims; null outputs are skipped. */
-sage_status sage_block_sizes(int32_t head_dim, int32_t* blk_q, int32_t* blk_k, int32_t* bkv);
+/* Quantisation block sizes and the online-softmax KV tile for `head_dim` and
+ * the sage_qk_gran `qk_gran`. BLK_Q query tokens / BLK_K key tokens share one
+ * INT8 scale (blocks start at token 0, the last one may be short); the softmax
+ * walks KV tiles of BKV keys from key 0 upward, so BKV is part of the result's
+ * definition (P's FP8 codes depend on the running row max).
+ * Returns SAGE_ERR_UNSUPPORTED for other head dims, SAGE_ERR_INVALID_ARGUMENT
+ * for an unknown granularity; null outputs are skipped. */
+sage_status sage_block_sizes(int32_t head_dim, int32_t qk_gran, int32_t* blk_q, int32_t* blk_k, int32_t* bkv);
 
 /* Nk rounded up to the padded key count of transposed V codes (a multiple of BKV = 128). */
 int64_t sage_v_codes_stride(int32_t seq_k);
@@ -96,7 +107,7 @@ size_t sage_quant_v_workspace_bytes(const sage_shape* s);
  * scales, reduction partials). Returns 0 for an invalid shape. */
 size_t sage_workspace_bytes(const sage_shape* s, int32_t pv_dtype);
 
-/* K smoothing + per-block INT8 quantisation of Q and K.
+/* K smoothing + INT8 quantisation of Q and K, per block of s->qk_gran.
  * (glossary 概要: K smoothed along the channel direction, then INT8;
  *  repo card "How it works": INT8 for QK^T.)
  *   k_mean [B,Hkv,d] fp32      mu = fp32((sum over all Nk tokens, in fp64) / Nk)

@@ -48,6 +48,12 @@ Readings where the pages are silent (each also listed in the design notes):
        mode), so the output is normalised by the weights actually applied;
        against fp64 exact attention this is equal to or slightly better than
        summing the unquantised P~.
+  [R20] per-thread quantisation (heatdrop.ai review, "The interesting bit",
+       names it next to the smoothing, without a definition) is read as the
+       finest grouping the GPU kernel's matrix-product lane layout gives at no
+       extra cost: every query token has its own scale (BLK_Q = 1) and every
+       run of 16 consecutive keys shares one (BLK_K = 16), blocks starting at
+       token 0. All the per-block rules above then apply per group.
 """
 from __future__ import annotations
 
@@ -63,6 +69,8 @@ INT8_MAX = 127.0
 
 BLK_Q = 128        # [R7]
 BLK_K = 64         # [R7]
+PER_THREAD_BLK_Q = 1     # [R20]
+PER_THREAD_BLK_K = 16    # [R20]
 BKV = {64: 128, 128: 128}   # [R14] KV tile per head dim
 
 

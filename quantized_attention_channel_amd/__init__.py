@@ -11,8 +11,10 @@ Entry points (same names as the C ABI):
   sage_attn_fwd_codes, sage_debug_qk_i32.
 User-facing wrapper:
   sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None,
-           pv_dtype="fp8") -- the call shape the SageAttention pages show
-  (cnnetsun.cn guide, basic usage; thu-ml/SageAttention repo card, "How to use").
+           pv_dtype="fp8", qk_quant_gran="per_block") -- the call shape the
+  SageAttention pages show (cnnetsun.cn guide, basic usage; thu-ml/SageAttention
+  repo card, "How to use"); qk_quant_gran="per_thread" selects the per-thread
+  Q/K scales (heatdrop.ai review, "The interesting bit").
 """
 from __future__ import annotations
 
@@ -31,12 +33,13 @@ SAGE_OK, SAGE_ERR_INVALID_ARGUMENT, SAGE_ERR_UNSUPPORTED, SAGE_ERR_WORKSPACE, SA
 LAYOUTS = {"HND": 0, "NHD": 1}
 DTYPES = {torch.float16: 0, torch.bfloat16: 1}
 PV_DTYPES = {"fp16": 0, "fp8": 1, "fp8_e4m3": 1}
+QK_GRANS = {"per_block": 0, "per_thread": 1}
 
 # Every function the header declares, with its ctypes signature.
 _c_shape_p = ctypes.c_void_p
 _vp = ctypes.c_void_p
 _SIGNATURES = {
-    "sage_block_sizes": (ctypes.c_int, [ctypes.c_int32, _vp, _vp, _vp]),
+    "sage_block_sizes": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp]),
     "sage_v_codes_stride": (ctypes.c_int64, [ctypes.c_int32]),
     "sage_quant_qk_workspace_bytes": (ctypes.c_size_t, [_c_shape_p]),
     "sage_quant_v_workspace_bytes": (ctypes.c_size_t, [_c_shape_p]),
@@ -55,7 +58,7 @@ _SIGNATURES = {
 
 class SageShape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("batch", "heads_q", "heads_kv", "seq_q", "seq_k", "head_dim", "layout", "dtype")]
+                ("batch", "heads_q", "heads_kv", "seq_q", "seq_k", "head_dim", "layout", "dtype", "qk_gran")]
 
 
 def _load():
@@ -92,11 +95,11 @@ def _stream(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def make_shape(B, Hq, Hkv, Nq, Nk, d, layout="HND", dtype=torch.float16) -> SageShape:
-    return SageShape(B, Hq, Hkv, Nq, Nk, d, LAYOUTS[layout], DTYPES[dtype])
+def make_shape(B, Hq, Hkv, Nq, Nk, d, layout="HND", dtype=torch.float16, qk_gran="per_block") -> SageShape:
+    return SageShape(B, Hq, Hkv, Nq, Nk, d, LAYOUTS[layout], DTYPES[dtype], QK_GRANS[qk_gran])
 
 
-def shape_of(q: torch.Tensor, k: torch.Tensor, layout: str) -> SageShape:
+def shape_of(q: torch.Tensor, k: torch.Tensor, layout: str, qk_gran: str = "per_block") -> SageShape:
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q, k, v must be 4-D")
     if layout == "HND":
@@ -109,7 +112,7 @@ def shape_of(q: torch.Tensor, k: torch.Tensor, layout: str) -> SageShape:
         raise ValueError(f"tensor_layout must be HND or NHD, got {layout!r}")
     if q.dtype not in DTYPES:
         raise TypeError(f"q/k/v must be float16 or bfloat16, got {q.dtype}")
-    return make_shape(B, Hq, Hkv, Nq, Nk, d, layout, q.dtype)
+    return make_shape(B, Hq, Hkv, Nq, Nk, d, layout, q.dtype, qk_gran)
 
 
 def _ref(s: SageShape):
@@ -117,10 +120,10 @@ def _ref(s: SageShape):
 
 
 # ------------------------------------------------------------------ queries
-def sage_block_sizes(head_dim: int):
+def sage_block_sizes(head_dim: int, qk_gran: str = "per_block"):
     bq, bk, bkv = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
-    _check(lib.sage_block_sizes(head_dim, ctypes.byref(bq), ctypes.byref(bk), ctypes.byref(bkv)),
-           "sage_block_sizes")
+    _check(lib.sage_block_sizes(head_dim, QK_GRANS[qk_gran], ctypes.byref(bq), ctypes.byref(bk),
+                                ctypes.byref(bkv)), "sage_block_sizes")
     return bq.value, bk.value, bkv.value
 
 
@@ -146,11 +149,11 @@ def _check_inputs(*ts):
 
 
 # ------------------------------------------------------------------ entry points
-def sage_quant_qk(q: torch.Tensor, k: torch.Tensor, tensor_layout: str = "HND"):
+def sage_quant_qk(q: torch.Tensor, k: torch.Tensor, tensor_layout: str = "HND", qk_gran: str = "per_block"):
     """Returns dict(q_codes, q_scale, k_codes, k_scale, k_mean) (canonical HND order)."""
     _check_inputs(q, k)
-    s = shape_of(q, k, tensor_layout)
-    blk_q, blk_k, _ = sage_block_sizes(s.head_dim)
+    s = shape_of(q, k, tensor_layout, qk_gran)
+    blk_q, blk_k, _ = sage_block_sizes(s.head_dim, qk_gran)
     dev = q.device
     out = dict(
         q_codes=torch.empty((s.batch, s.heads_q, s.seq_q, s.head_dim), dtype=torch.int8, device=dev),
@@ -205,9 +208,10 @@ def sage_attn_fwd_codes(shape: SageShape, q_codes, q_scale, k_codes, k_scale, v_
 
 def sage_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, is_causal: bool = False,
                   sm_scale: Optional[float] = None, pv_dtype: str = "fp8", tensor_layout: str = "HND",
-                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                  qk_gran: str = "per_block") -> torch.Tensor:
     _check_inputs(q, k, v)
-    s = shape_of(q, k, tensor_layout)
+    s = shape_of(q, k, tensor_layout, qk_gran)
     if tuple(v.shape) != tuple(k.shape) or v.dtype != q.dtype or k.dtype != q.dtype:
         raise ValueError("v must have k's shape and all inputs one dtype")
     if sm_scale is None:
@@ -235,7 +239,7 @@ def sage_debug_qk_i32(q_codes: torch.Tensor, k_codes: torch.Tensor) -> torch.Ten
 
 
 def sageattn(q, k, v, tensor_layout: str = "HND", is_causal: bool = False, sm_scale: Optional[float] = None,
-             pv_dtype: str = "fp8", **kwargs):
+             pv_dtype: str = "fp8", qk_quant_gran: str = "per_block", **kwargs):
     """Quantised attention with the scaled-dot-product-attention call shape.
 
     SDPA arguments this method does not implement are rejected rather than
@@ -253,11 +257,14 @@ def sageattn(q, k, v, tensor_layout: str = "HND", is_causal: bool = False, sm_sc
                 raise NotImplementedError("explicit attention masks are not supported")
     if kwargs:
         raise TypeError(f"unexpected arguments: {sorted(kwargs)}")
+    if qk_quant_gran not in QK_GRANS:
+        raise ValueError(f"qk_quant_gran must be one of {sorted(QK_GRANS)}, got {qk_quant_gran!r}")
     return sage_attn_fwd(q.contiguous(), k.contiguous(), v.contiguous(), is_causal=is_causal,
-                         sm_scale=sm_scale, pv_dtype=pv_dtype, tensor_layout=tensor_layout)
+                         sm_scale=sm_scale, pv_dtype=pv_dtype, tensor_layout=tensor_layout,
+                         qk_gran=qk_quant_gran)
 
 
 __all__ = ["sageattn", "sage_attn_fwd", "sage_attn_fwd_codes", "sage_quant_qk", "sage_quant_v",
            "sage_transpose_v", "sage_debug_qk_i32",
            "sage_block_sizes", "sage_v_codes_stride", "sage_workspace_bytes", "make_shape", "shape_of",
-           "SageError", "SageShape", "lib", "LIB_PATH"]
+           "SageError", "SageShape", "QK_GRANS", "lib", "LIB_PATH"]

@@ -13,9 +13,11 @@
 //      accumulation), as four 32-key blocks. Computing the transpose puts one
 //      query per lane: lane l holds query l % 32 and 16 keys of every block, so
 //      each row reduction is in-lane plus one exchange with lane l ^ 32.
-//   2. Dequantise with c = s_q * s_k * sm_scale * log2(e) (one scalar per 64-key
-//      K quantisation block; a group is one Q block), mask only on the
-//      causal diagonal / ragged tail tile, online softmax in the log2 domain.
+//   2. Dequantise with c = s_q * s_k * sm_scale * log2(e) (per-block scales:
+//      one factor per 64-key K block, a group being one Q block; per-thread
+//      scales: the lane's own query and each 16 keys the lane holds), mask only
+//      on the causal diagonal / ragged tail tile, online softmax in the log2
+//      domain.
 //   3. P -> e4m3 (scaled by 448 through the exponent) or fp16/bf16, packed
 //      straight from registers into the B operand of the PV product: the K rows
 //      of step 1 are permuted so that each lane's keys are contiguous, exactly
@@ -35,6 +37,7 @@ namespace sage {
 constexpr int kBq = 128;           // queries per group == the Q quantisation block
 constexpr int kBlocks = kBkv / 32; // 32-key S^T blocks per tile
 static_assert(kBkv == 2 * kBlkK, "a tile spans two K quantisation blocks");
+static_assert(kFineBlkK == 16 && kFineBlkQ == 1, "per-thread scales follow the lane layout of the products");
 
 // --------------------------------------------------------------- LDS layouts
 // gfx950 serves a 16-byte-per-lane LDS read 16 lanes at a time from 64 banks
@@ -191,8 +194,10 @@ struct PTile<false, T> {
 // Softmax phase of one KV tile for one wave (vector ALU work only): mask,
 // online softmax in the log2 domain, P quantisation. s (S^T of the tile) is
 // consumed; the running max is updated; the P operand and alpha go to pt.
-template <int D, bool FP8, bool CAUSAL, bool MASK, typename T>
-__device__ __forceinline__ void softmax_phase(i32x16* s, int lane, int k0, int qi, int nk, float c0, float c1,
+// c[bb]: this lane's dequantisation factor for 32-key block bb (per-block
+// scales: one per 64-key half of the tile; per-thread: one per lane half).
+template <int D, bool FP8, bool CAUSAL, bool MASK, bool FINE, typename T>
+__device__ __forceinline__ void softmax_phase(i32x16* s, int lane, int k0, int qi, int nk, const float (&c)[kBlocks],
                                               float& m, PTile<FP8, T>& pt) {
   const int g = lane >> 5;
   if (MASK) {
@@ -217,17 +222,30 @@ __device__ __forceinline__ void softmax_phase(i32x16* s, int lane, int k0, int q
       mc[bb] = max(mc[bb], max(si(bb, r), si(bb, r + 1)));
       pin(mc[bb]);
     }
-  const int mx0 = max(max(mc[0], si(0, 15)), max(mc[1], si(1, 15)));
-  const int mx1 = max(max(mc[2], si(2, 15)), max(mc[3], si(3, 15)));
   // (FP8 P: the scores carry kScoreOffset; FP16 P keeps plain S and the
   //  conversion, since the 16 registers of the offset block do not fit there)
   auto sf = [&](int v) { return FP8 ? as_f32(v) - kScoreOffsetF : (float)v; };
-  float t0 = sf(mx0) * c0, t1 = sf(mx1) * c1;
-  if (MASK) {
-    if (mx0 == INT_MIN) t0 = -INFINITY;
-    if (mx1 == INT_MIN) t1 = -INFINITY;
+  float m_tile;
+  if constexpr (FINE) {
+    float tb[kBlocks];
+#pragma unroll
+    for (int bb = 0; bb < kBlocks; ++bb) {
+      const int mxb = max(mc[bb], si(bb, 15));
+      tb[bb] = sf(mxb) * c[bb];
+      if (MASK && mxb == INT_MIN) tb[bb] = -INFINITY;
+    }
+    m_tile = fmaxf(fmaxf(tb[0], tb[1]), fmaxf(tb[2], tb[3]));
+  } else {
+    const int mx0 = max(max(mc[0], si(0, 15)), max(mc[1], si(1, 15)));
+    const int mx1 = max(max(mc[2], si(2, 15)), max(mc[3], si(3, 15)));
+    float t0 = sf(mx0) * c[0], t1 = sf(mx1) * c[2];
+    if (MASK) {
+      if (mx0 == INT_MIN) t0 = -INFINITY;
+      if (mx1 == INT_MIN) t1 = -INFINITY;
+    }
+    m_tile = fmaxf(t0, t1);
   }
-  const float m_new = fmaxf(m, pair_max(fmaxf(t0, t1)));
+  const float m_new = fmaxf(m, pair_max(m_tile));
   pt.alpha = fast_exp2(m - m_new);
   m = m_new;
   const float bias = (FP8 ? kLog2E4m3Max : 0.0f) - m_new;   // P8 = e4m3(448 * P~) via the exponent
@@ -235,11 +253,11 @@ __device__ __forceinline__ void softmax_phase(i32x16* s, int lane, int k0, int q
   // P~ overwrites the scores in place (as fp32 bit patterns).
 #pragma unroll
   for (int bb = 0; bb < kBlocks; ++bb) {
-    const float c = bb < 2 ? c0 : c1;
+    const float cb = FINE ? c[bb] : c[bb < 2 ? 0 : 2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int sv = si(bb, r);
-      float x = fast_exp2(__builtin_fmaf(sf(sv), c, bias));
+      float x = fast_exp2(__builtin_fmaf(sf(sv), cb, bias));
       if (MASK && sv == INT_MIN) x = 0.0f;
       s[bb][r] = __builtin_bit_cast(int, x);
     }
@@ -376,8 +394,8 @@ constexpr int kWaves = 8;
 __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
 __device__ __forceinline__ void wait_loads_barrier() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int D, bool FP8, bool CAUSAL, typename T>
-__global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
+template <int D, bool FP8, bool CAUSAL, typename T, bool FINE>
+__device__ __forceinline__ void attn_fwd_body(AttnArgs a) {
   constexpr int NT = D / 32;
   using Stage = TileStage<D, FP8, kWaves>;
   constexpr int kKBytes = kBkv * D, kVBytes = D * Stage::kVRowB;
@@ -406,7 +424,10 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   i32x4 qreg[NT];
   load_q_operand<D>(a.q8 + (int64_t)bh * a.Nq * D, a.Nq, qi, g, qreg);
   const bool grp_live = qt * kBq < a.Nq;
-  const float cq = grp_live ? a.q_scale[(int64_t)bh * a.nbq + qt] * a.scale_log2 : 0.0f;
+  // Q scale: the group's block, or (per-thread) the lane's own query.
+  float cq;
+  if constexpr (FINE) cq = qi < a.Nq ? a.q_scale[(int64_t)bh * a.nbq + qi] * a.scale_log2 : 0.0f;
+  else cq = grp_live ? a.q_scale[(int64_t)bh * a.nbq + qt] * a.scale_log2 : 0.0f;
   const __attribute__((address_space(4))) float* kscale =
       (const __attribute__((address_space(4))) float*)(a.k_scale + (int64_t)bhk * a.nbk);
 
@@ -493,10 +514,23 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   };
   // Y(t): softmax of tile t (registers only).
   auto y_phase = [&](int t, auto masked) __attribute__((always_inline)) {
-    const float c0 = cq * kscale[min(2 * t, a.nbk - 1)];
-    const float c1 = cq * kscale[min(2 * t + 1, a.nbk - 1)];   // past Nk: masked anyway
+    float c[kBlocks];
+    if constexpr (FINE) {
+      // lane half g holds keys 32bb + 16g + 0..15 of the tile: scale 8t + 2bb + g
+#pragma unroll
+      for (int bb = 0; bb < kBlocks; ++bb) {
+        const float ka = kscale[min(8 * t + 2 * bb, a.nbk - 1)];
+        const float kb = kscale[min(8 * t + 2 * bb + 1, a.nbk - 1)];   // past Nk: masked anyway
+        c[bb] = cq * (g ? kb : ka);
+      }
+    } else {
+      const float c0 = cq * kscale[min(2 * t, a.nbk - 1)];
+      const float c1 = cq * kscale[min(2 * t + 1, a.nbk - 1)];   // past Nk: masked anyway
+      c[0] = c[1] = c0;
+      c[2] = c[3] = c1;
+    }
     __builtin_amdgcn_s_setprio(0);
-    softmax_phase<D, FP8, CAUSAL, decltype(masked)::value, T>(s, lane, t * kBkv, qi, a.Nk, c0, c1, st.m, pt);
+    softmax_phase<D, FP8, CAUSAL, decltype(masked)::value, FINE, T>(s, lane, t * kBkv, qi, a.Nk, c, st.m, pt);
   };
   using Masked = std::true_type;
   using Full = std::false_type;
@@ -601,6 +635,18 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
   }
 }
 
+// Per-block Q/K scales.
+template <int D, bool FP8, bool CAUSAL, typename T>
+__global__ __launch_bounds__(512, 1) void attn_fwd_kernel(AttnArgs a) {
+  attn_fwd_body<D, FP8, CAUSAL, T, false>(a);
+}
+
+// Per-thread Q/K scales: one per query and one per 16 keys.
+template <int D, bool FP8, bool CAUSAL, typename T>
+__global__ __launch_bounds__(512, 1) void attn_fwd_fine_kernel(AttnArgs a) {
+  attn_fwd_body<D, FP8, CAUSAL, T, true>(a);
+}
+
 // INT32 S = Q8 K8^T through the same staging layout and matrix-core tile code.
 template <int D>
 __global__ __launch_bounds__(256) void debug_qk_kernel(DebugQKArgs a) {
@@ -641,7 +687,10 @@ template <int D, bool FP8, bool CAUSAL, typename T>
 static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t st) {
   const int n_qp = (a.Nq + 2 * kBq - 1) / (2 * kBq);
   const int grid = n_qp * a.B * a.Hq;
-  hipLaunchKernelGGL((attn_fwd_kernel<D, FP8, CAUSAL, T>), dim3(grid), dim3(64 * kWaves), 0, st, a);
+  if (a.fine)
+    hipLaunchKernelGGL((attn_fwd_fine_kernel<D, FP8, CAUSAL, T>), dim3(grid), dim3(64 * kWaves), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<D, FP8, CAUSAL, T>), dim3(grid), dim3(64 * kWaves), 0, st, a);
   return hipGetLastError();
 }
 

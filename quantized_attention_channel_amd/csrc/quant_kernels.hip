@@ -116,21 +116,31 @@ __global__ __launch_bounds__(D) void channel_finalize_kernel(
   }
 }
 
-// One work-group per (b, head, block of BLK tokens): optional smoothing
-// x - mu[c], block absmax, s = a/127, codes = rne(x * (127/a)).
+// INT8 quantisation per (b, head, block of BLK tokens): optional smoothing
+// x - mu[c], block absmax a, s = a/127, codes = rne(x * (127/a)).
+// Thread tid of pass `it` holds the 16-byte chunk (it*256 + tid) of the
+// work-group's token rows, so a block is G = BLK * D/8 consecutive chunks.
+// Blocks of G >= 256 chunks take one work-group each (reduction over the
+// whole group); smaller blocks share 64-token work-groups, and each pass
+// reduces its 256/G blocks over lane groups of G (in-wave butterflies up to
+// 64 lanes, one LDS exchange between waves above).
 template <typename T, int D, int BLK, bool SMOOTH>
 __global__ __launch_bounds__(256) void quant_int8_kernel(
     const uint16_t* __restrict__ x, TensorGeom geo, int H, int N, int nblk,
     const float* __restrict__ mean, int8_t* __restrict__ codes, float* __restrict__ scale) {
   constexpr int TPR = D / 8;
-  constexpr int ITER = BLK * TPR / 256;   // 16-byte chunks per thread
-  static_assert(ITER * 256 == BLK * TPR, "block must tile the work-group");
+  constexpr int G = BLK * TPR;                   // chunks per block
+  constexpr bool WHOLE = G >= 256;               // one block per work-group
+  constexpr int TOKS = WHOLE ? BLK : 64;         // token rows per work-group
+  constexpr int ITER = TOKS * TPR / 256;         // 16-byte chunks per thread
+  static_assert(ITER * 256 == TOKS * TPR, "token rows must tile the work-group");
+  static_assert(WHOLE ? G % 256 == 0 : 256 % G == 0, "blocks must tile the passes");
   __shared__ float red[4];
   const int tid = threadIdx.x;
   const int col = (tid % TPR) * 8;        // 256 % TPR == 0: fixed per thread
   const int bh = blockIdx.y;
   const int b = bh / H, h = bh % H;
-  const int t0 = blockIdx.x * BLK;
+  const int t0 = blockIdx.x * TOKS;
   const int64_t base = (int64_t)b * geo.batch_stride + (int64_t)h * geo.head_stride + col;
 
   float mu[8];
@@ -138,10 +148,11 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(
   for (int e = 0; e < 8; ++e) mu[e] = SMOOTH ? mean[bh * D + col + e] : 0.0f;
 
   float val[ITER][8];
-  float amax = 0.0f;
+  float amax[ITER];
 #pragma unroll
   for (int it = 0; it < ITER; ++it) {
     const int t = t0 + (it * 256 + tid) / TPR;
+    amax[it] = 0.0f;
     if (t < N) {
       i32x4 raw = *reinterpret_cast<const i32x4*>(x + base + (int64_t)t * geo.tok_stride);
 #pragma unroll
@@ -150,19 +161,45 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(
         float f = T::to_f32(bits);
         if (SMOOTH) f = f - mu[e];
         val[it][e] = f;
-        amax = fmaxf(amax, fabsf(f));
+        amax[it] = fmaxf(amax[it], fabsf(f));
       }
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) val[it][e] = 0.0f;
     }
   }
-  amax = wave_max(amax);
-  if ((tid & 63) == 0) red[tid >> 6] = amax;
-  __syncthreads();
-  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float inv = amax > 0.0f ? 127.0f / amax : 0.0f;
-  if (tid == 0) scale[(int64_t)bh * nblk + blockIdx.x] = amax / 127.0f;
+  float inv[ITER];
+  if constexpr (WHOLE) {
+    float a = 0.0f;
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) a = fmaxf(a, amax[it]);
+    a = wave_max(a);
+    if ((tid & 63) == 0) red[tid >> 6] = a;
+    __syncthreads();
+    a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    if (tid == 0) scale[(int64_t)bh * nblk + blockIdx.x] = a / 127.0f;
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) inv[it] = a > 0.0f ? 127.0f / a : 0.0f;
+  } else {
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      float a = amax[it];
+#pragma unroll
+      for (int o = 1; o < (G < 64 ? G : 64); o <<= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
+      if constexpr (G > 64) {
+        // the G/64 waves of each block exchange their maxima
+        if ((tid & 63) == 0) red[tid >> 6] = a;
+        __syncthreads();
+        const int w0 = (tid >> 6) & ~(G / 64 - 1);
+#pragma unroll
+        for (int w = 0; w < G / 64; ++w) a = fmaxf(a, red[w0 + w]);
+        __syncthreads();                 // red is rewritten by the next pass
+      }
+      const int blk = (t0 + (it * 256 + tid) / TPR) / BLK;
+      if (tid % G == 0 && blk < nblk) scale[(int64_t)bh * nblk + blk] = a / 127.0f;
+      inv[it] = a > 0.0f ? 127.0f / a : 0.0f;
+    }
+  }
 
   int8_t* out = codes + (int64_t)bh * N * D + col;
 #pragma unroll
@@ -172,13 +209,24 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(
       uint32_t w[2] = {0u, 0u};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float prod = val[it][e] * inv;
+        const float prod = val[it][e] * inv[it];
         const int q = (int)__builtin_rintf(prod);
         w[e / 4] |= ((uint32_t)(q & 0xff)) << (8 * (e & 3));
       }
       *reinterpret_cast<i32x2*>(out + (int64_t)t * D) = i32x2{(int)w[0], (int)w[1]};
     }
   }
+}
+
+// Launch of quant_int8_kernel over N tokens of B*H heads.
+template <typename T, int D, int BLK, bool SMOOTH>
+static void launch_quant_int8(const void* x, TensorGeom geo, int BH, int H, int N, const float* mean,
+                              int8_t* codes, float* scale, hipStream_t st) {
+  constexpr int TOKS = BLK * (D / 8) >= 256 ? BLK : 64;
+  const int nblk = (N + BLK - 1) / BLK;
+  const int wgs = (N + TOKS - 1) / TOKS;
+  hipLaunchKernelGGL((quant_int8_kernel<T, D, BLK, SMOOTH>), dim3(wgs, BH), dim3(256), 0, st,
+                     (const uint16_t*)x, geo, H, N, nblk, mean, codes, scale);
 }
 
 // One work-group per (b, kv-head, 64-token tile): V transposed to
@@ -253,15 +301,17 @@ static hipError_t launch_qk_t(const QuantQKArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((channel_finalize_kernel<D, true, false>), dim3(bhk), dim3(D), 0, st,
                        a.Nk, chunks, a.ksum_part, (const float*)nullptr, a.k_mean, (float*)nullptr,
                        (float*)nullptr);
-    const int nbk = (a.Nk + kBlkK - 1) / kBlkK;
-    hipLaunchKernelGGL((quant_int8_kernel<T, D, kBlkK, true>), dim3(nbk, bhk), dim3(256), 0, st,
-                       (const uint16_t*)a.k, a.kgeo, a.Hkv, a.Nk, nbk, a.k_mean, a.k_codes, a.k_scale);
+    if (a.fine)
+      launch_quant_int8<T, D, kFineBlkK, true>(a.k, a.kgeo, bhk, a.Hkv, a.Nk, a.k_mean, a.k_codes, a.k_scale, st);
+    else
+      launch_quant_int8<T, D, kBlkK, true>(a.k, a.kgeo, bhk, a.Hkv, a.Nk, a.k_mean, a.k_codes, a.k_scale, st);
   }
   if (a.Nq > 0) {
-    const int nbq = (a.Nq + kBlkQ - 1) / kBlkQ;
-    hipLaunchKernelGGL((quant_int8_kernel<T, D, kBlkQ, false>), dim3(nbq, a.B * a.Hq), dim3(256), 0, st,
-                       (const uint16_t*)a.q, a.qgeo, a.Hq, a.Nq, nbq, (const float*)nullptr, a.q_codes,
-                       a.q_scale);
+    const int bhq = a.B * a.Hq;
+    if (a.fine)
+      launch_quant_int8<T, D, kFineBlkQ, false>(a.q, a.qgeo, bhq, a.Hq, a.Nq, nullptr, a.q_codes, a.q_scale, st);
+    else
+      launch_quant_int8<T, D, kBlkQ, false>(a.q, a.qgeo, bhq, a.Hq, a.Nq, nullptr, a.q_codes, a.q_scale, st);
   }
   return hipGetLastError();
 }

@@ -20,7 +20,8 @@ constexpr int64_t kMaxSeq = int64_t(1) << 20;
 
 struct Dims {
   int64_t B, Hq, Hkv, Nq, Nk, D;
-  bool nhd, bf16;
+  int64_t blk_q, blk_k;   // tokens per INT8 scale
+  bool nhd, bf16, fine;
 };
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -32,6 +33,7 @@ sage_status check_shape(const sage_shape* s, Dims* d) {
   if (!s) return SAGE_ERR_INVALID_ARGUMENT;
   if (s->layout != SAGE_LAYOUT_HND && s->layout != SAGE_LAYOUT_NHD) return SAGE_ERR_INVALID_ARGUMENT;
   if (s->dtype != SAGE_DTYPE_F16 && s->dtype != SAGE_DTYPE_BF16) return SAGE_ERR_INVALID_ARGUMENT;
+  if (s->qk_gran != SAGE_QK_PER_BLOCK && s->qk_gran != SAGE_QK_PER_THREAD) return SAGE_ERR_INVALID_ARGUMENT;
   if (s->batch < 0 || s->heads_q < 1 || s->heads_kv < 1 || s->seq_q < 0 || s->seq_k < 0 || s->head_dim < 1)
     return SAGE_ERR_INVALID_ARGUMENT;
   if (s->heads_q % s->heads_kv != 0) return SAGE_ERR_INVALID_ARGUMENT;
@@ -45,6 +47,9 @@ sage_status check_shape(const sage_shape* s, Dims* d) {
   d->D = s->head_dim;
   d->nhd = s->layout == SAGE_LAYOUT_NHD;
   d->bf16 = s->dtype == SAGE_DTYPE_BF16;
+  d->fine = s->qk_gran == SAGE_QK_PER_THREAD;
+  d->blk_q = d->fine ? sage::kFineBlkQ : sage::kBlkQ;
+  d->blk_k = d->fine ? sage::kFineBlkK : sage::kBlkK;
   // grid and buffer-offset limits: (b, head) pairs fit a grid dimension,
   // per-head slices fit a 32-bit byte offset
   if (d->B * d->Hq > (int64_t(1) << 24)) return SAGE_ERR_INVALID_ARGUMENT;
@@ -86,7 +91,7 @@ Layout layout_for(const Dims& d, bool fp8) {
     off = align256(off + bytes);
     return o;
   };
-  const int64_t nbq = cdiv(d.Nq, sage::kBlkQ), nbk = cdiv(d.Nk, sage::kBlkK);
+  const int64_t nbq = cdiv(d.Nq, d.blk_q), nbk = cdiv(d.Nk, d.blk_k);
   const int64_t npad = round_up(d.Nk, sage::kVPad);
   const int64_t chunks = cdiv(d.Nk, kStatChunk);
   L.q_codes = take(size_t(d.B * d.Hq * d.Nq * d.D));
@@ -117,10 +122,12 @@ sage_status from_hip(hipError_t e) { return e == hipSuccess ? SAGE_OK : SAGE_ERR
 
 extern "C" {
 
-sage_status sage_block_sizes(int32_t head_dim, int32_t* blk_q, int32_t* blk_k, int32_t* bkv) {
+sage_status sage_block_sizes(int32_t head_dim, int32_t qk_gran, int32_t* blk_q, int32_t* blk_k, int32_t* bkv) {
+  if (qk_gran != SAGE_QK_PER_BLOCK && qk_gran != SAGE_QK_PER_THREAD) return SAGE_ERR_INVALID_ARGUMENT;
   if (head_dim != 64 && head_dim != 128) return SAGE_ERR_UNSUPPORTED;
-  if (blk_q) *blk_q = sage::kBlkQ;
-  if (blk_k) *blk_k = sage::kBlkK;
+  const bool fine = qk_gran == SAGE_QK_PER_THREAD;
+  if (blk_q) *blk_q = fine ? sage::kFineBlkQ : sage::kBlkQ;
+  if (blk_k) *blk_k = fine ? sage::kFineBlkK : sage::kBlkK;
   if (bkv) *bkv = sage::kBkv;
   return SAGE_OK;
 }
@@ -168,6 +175,7 @@ sage_status sage_quant_qk(const sage_shape* s, const void* q, const void* k, int
   a.kgeo = geom(d, d.Hkv, d.Nk);
   a.B = int(d.B), a.Hq = int(d.Hq), a.Hkv = int(d.Hkv), a.Nq = int(d.Nq), a.Nk = int(d.Nk), a.D = int(d.D);
   a.bf16 = d.bf16;
+  a.fine = d.fine;
   a.q_codes = q_codes;
   a.q_scale = q_scale;
   a.k_codes = k_codes;
@@ -232,6 +240,7 @@ sage_status sage_attn_fwd(const sage_shape* s, const void* q, const void* k, con
   qa.kgeo = geom(d, d.Hkv, d.Nk);
   qa.B = int(d.B), qa.Hq = int(d.Hq), qa.Hkv = int(d.Hkv), qa.Nq = int(d.Nq), qa.Nk = int(d.Nk), qa.D = int(d.D);
   qa.bf16 = d.bf16;
+  qa.fine = d.fine;
   qa.q_codes = at<int8_t>(workspace, L.q_codes);
   qa.q_scale = at<float>(workspace, L.q_scale);
   qa.k_codes = at<int8_t>(workspace, L.k_codes);
@@ -266,12 +275,13 @@ sage_status sage_attn_fwd(const sage_shape* s, const void* q, const void* k, con
   aa.ogeo = geom(d, d.Hq, d.Nq);
   aa.B = int(d.B), aa.Hq = int(d.Hq), aa.Hkv = int(d.Hkv), aa.Nq = int(d.Nq), aa.Nk = int(d.Nk), aa.D = int(d.D);
   aa.n_pad = va.n_pad;
-  aa.nbq = int(cdiv(d.Nq, sage::kBlkQ));
-  aa.nbk = int(cdiv(d.Nk, sage::kBlkK));
+  aa.nbq = int(cdiv(d.Nq, d.blk_q));
+  aa.nbk = int(cdiv(d.Nk, d.blk_k));
   aa.scale_log2 = sm_scale * sage::kLog2E;
   aa.causal = is_causal != 0;
   aa.bf16 = d.bf16;
   aa.fp8 = fp8;
+  aa.fine = d.fine;
   return from_hip(sage::launch_attn(aa, hs));
 }
 
@@ -328,12 +338,13 @@ sage_status sage_attn_fwd_codes(const sage_shape* s, const int8_t* q_codes, cons
   aa.ogeo = geom(d, d.Hq, d.Nq);
   aa.B = int(d.B), aa.Hq = int(d.Hq), aa.Hkv = int(d.Hkv), aa.Nq = int(d.Nq), aa.Nk = int(d.Nk), aa.D = int(d.D);
   aa.n_pad = int(npad);
-  aa.nbq = int(cdiv(d.Nq, sage::kBlkQ));
-  aa.nbk = int(cdiv(d.Nk, sage::kBlkK));
+  aa.nbq = int(cdiv(d.Nq, d.blk_q));
+  aa.nbk = int(cdiv(d.Nk, d.blk_k));
   aa.scale_log2 = sm_scale * sage::kLog2E;
   aa.causal = is_causal != 0;
   aa.bf16 = d.bf16;
   aa.fp8 = fp8;
+  aa.fine = d.fine;
   return from_hip(sage::launch_attn(aa, static_cast<hipStream_t>(stream)));
 }
 

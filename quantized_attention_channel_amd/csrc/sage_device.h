@@ -21,6 +21,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // Method constants (quantisation blocks and the online-softmax KV tile).
 constexpr int kBlkQ = 128;   // query tokens per INT8 scale
 constexpr int kBlkK = 64;    // key tokens per INT8 scale
+// Per-thread granularity: the tokens one lane holds in the attention kernel's
+// matrix instructions (its single query; 16 consecutive keys of a 32-key block).
+constexpr int kFineBlkQ = 1;
+constexpr int kFineBlkK = 16;
 constexpr int kBkv = 128;    // keys per online-softmax tile
 constexpr int kVPad = 128;   // transposed-V rows are padded to a multiple of the tile
 constexpr float kE4m3Max = 448.0f;

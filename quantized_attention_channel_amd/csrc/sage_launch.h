@@ -20,6 +20,7 @@ struct QuantQKArgs {
   TensorGeom qgeo, kgeo;
   int B, Hq, Hkv, Nq, Nk, D;
   bool bf16;
+  bool fine;           // per-thread scales (kFineBlkQ / kFineBlkK), else per block
   int8_t* q_codes;
   float* q_scale;
   int8_t* k_codes;
@@ -52,6 +53,7 @@ struct AttnArgs {
   int nbq, nbk;
   float scale_log2;     // sm_scale * log2(e)
   bool causal, bf16, fp8;
+  bool fine;            // per-thread scales: q_scale per query, k_scale per 16 keys
 };
 
 struct DebugQKArgs {

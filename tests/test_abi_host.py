@@ -51,10 +51,14 @@ def test_binding_covers_the_header():
 def test_block_sizes_match_the_oracle_readings():
     for d in (64, 128):
         assert sage.sage_block_sizes(d) == (sage_ref.BLK_Q, sage_ref.BLK_K, sage_ref.BKV[d])
+        assert sage.sage_block_sizes(d, "per_thread") == (sage_ref.PER_THREAD_BLK_Q, sage_ref.PER_THREAD_BLK_K,
+                                                          sage_ref.BKV[d])
     with pytest.raises(sage.SageError) as e:
         sage.sage_block_sizes(96)
     assert e.value.status == sage.SAGE_ERR_UNSUPPORTED
-    assert sage.lib.sage_block_sizes(64, None, None, None) == sage.SAGE_OK
+    assert sage.lib.sage_block_sizes(64, 0, None, None, None) == sage.SAGE_OK
+    assert sage.lib.sage_block_sizes(64, 2, None, None, None) == sage.SAGE_ERR_INVALID_ARGUMENT
+    assert sage.lib.sage_block_sizes(64, -1, None, None, None) == sage.SAGE_ERR_INVALID_ARGUMENT
 
 
 def test_status_strings():
@@ -71,9 +75,25 @@ def test_v_codes_stride():
 
 
 def _shape(**kw):
-    base = dict(B=2, Hq=4, Hkv=2, Nq=300, Nk=300, d=128, layout="HND")
+    base = dict(B=2, Hq=4, Hkv=2, Nq=300, Nk=300, d=128, layout="HND", gran="per_block")
     base.update(kw)
-    return sage.make_shape(base["B"], base["Hq"], base["Hkv"], base["Nq"], base["Nk"], base["d"], base["layout"])
+    return sage.make_shape(base["B"], base["Hq"], base["Hkv"], base["Nq"], base["Nk"], base["d"], base["layout"],
+                           qk_gran=base["gran"])
+
+
+def test_shape_struct_matches_the_header():
+    # nine int32 fields in header order; a zero-initialised granularity is per-block
+    assert ctypes.sizeof(sage.SageShape) == 9 * 4
+    assert [f[0] for f in sage.SageShape._fields_][-1] == "qk_gran"
+    assert sage.SageShape(1, 1, 1, 8, 8, 64, 0, 0).qk_gran == 0 == sage.QK_GRANS["per_block"]
+
+
+def test_per_thread_workspace_holds_the_finer_scales():
+    pb, pt = _shape(), _shape(gran="per_thread")
+    for pv in ("fp8", "fp16"):
+        grow = sage.sage_workspace_bytes(pt, pv) - sage.sage_workspace_bytes(pb, pv)
+        # q scales: 300 per head instead of 3; k scales: 19 per head instead of 5
+        assert grow >= 4 * (2 * 4 * (300 - 3) + 2 * 2 * (19 - 5))
 
 
 def test_workspace_size_grows_with_the_problem():
@@ -101,6 +121,11 @@ def _attn(shape, q=FAKE, k=FAKE + 2 ** 30, v=FAKE + 2 ** 31, o=FAKE + 3 * 2 ** 3
     ("Hq % Hkv", dict(shape=_shape(Hq=3, Hkv=2)), sage.SAGE_ERR_INVALID_ARGUMENT),
     ("bad layout", dict(shape=sage.SageShape(1, 1, 1, 8, 8, 64, 5, 0)), sage.SAGE_ERR_INVALID_ARGUMENT),
     ("bad dtype", dict(shape=sage.SageShape(1, 1, 1, 8, 8, 64, 0, 9)), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("bad qk_gran", dict(shape=sage.SageShape(1, 1, 1, 8, 8, 64, 0, 0, 7)), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("per-thread, no queries", dict(shape=_shape(gran="per_thread", Nq=0), q=None, o=None), sage.SAGE_OK),
+    ("per-thread, per-block workspace", dict(shape=_shape(gran="per_thread"),
+                                             ws_bytes=sage.lib.sage_workspace_bytes(ctypes.byref(_shape()), 1)),
+     sage.SAGE_ERR_WORKSPACE),
     ("negative seq", dict(shape=_shape(Nq=-1)), sage.SAGE_ERR_INVALID_ARGUMENT),
     ("too long", dict(shape=_shape(Nq=(1 << 20) + 1, Nk=(1 << 20) + 1)), sage.SAGE_ERR_INVALID_ARGUMENT),
     ("head dim 96", dict(shape=_shape(d=96)), sage.SAGE_ERR_UNSUPPORTED),
