@@ -142,6 +142,48 @@ sage_status sage_attn_fwd(const sage_shape* s, const void* q, const void* k, con
                           void* o, int32_t is_causal, float sm_scale, int32_t pv_dtype,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* Variable-length batches (heatdrop.ai review, "Key highlights": variable
+ * sequence lengths within a batch). B sequences are packed along the token
+ * axis: q [total_q, Hq, d], k and v [total_k, Hkv, d], o like q (the NHD order
+ * of one long batch entry, dense, d contiguous). Sequence b owns the query
+ * tokens [cu_seqlens_q[b], cu_seqlens_q[b+1]) and the key tokens
+ * [cu_seqlens_k[b], cu_seqlens_k[b+1]); both are DEVICE int32 arrays of B + 1
+ * non-decreasing offsets from 0 to the total, and no sequence is longer than
+ * its max_seqlen. Every sequence is one independent attention by the method:
+ * its own K channel mean, Q/K INT8 blocks starting at its first token, its own
+ * V channel scales, causal masking top-left within the sequence (query i sees
+ * keys j <= i of its own sequence, also when its query and key counts differ).
+ * A sequence with queries but no keys gets zero output rows.
+ * The host never reads the device offsets. A table that breaks the rules above
+ * gives unspecified output for the sequences involved, but every index is
+ * clamped into the tensors and the workspace, so no access leaves them. */
+typedef struct sage_varlen_shape {
+  int32_t batch;         /* B sequences */
+  int32_t heads_q;       /* Hq  */
+  int32_t heads_kv;      /* Hkv */
+  int32_t head_dim;      /* d   */
+  int32_t total_q;       /* packed query tokens (= cu_seqlens_q[B]) */
+  int32_t total_k;       /* packed key tokens (= cu_seqlens_k[B]) */
+  int32_t max_seqlen_q;  /* bound on every sequence's query count, <= 2^20 */
+  int32_t max_seqlen_k;  /* bound on every sequence's key count, <= 2^20 */
+  int32_t dtype;         /* sage_dtype of q, k, v and o */
+  int32_t qk_gran;       /* sage_qk_gran of the Q and K scales */
+} sage_varlen_shape;
+
+/* Workspace bytes sage_attn_fwd_varlen needs for `s` and `pv` (0 if invalid).
+ * Sizes follow the totals and maximum lengths, not the device offsets. */
+size_t sage_varlen_workspace_bytes(const sage_varlen_shape* s, int32_t pv_dtype);
+
+/* The whole forward over a packed variable-length batch (see above); the other
+ * arguments are as for sage_attn_fwd. Limits: 1 <= Hq, Hkv with Hq % Hkv == 0,
+ * head_dim in {64, 128}, B * Hq <= 2^24, total_k + 127 * B <= 2^24 - 128 (the
+ * padded key columns of the transposed V). B == 0 or total_q == 0 is a no-op.
+ * cu_seqlens pointers must be 4-byte aligned; q, k, v, o 16-byte aligned. */
+sage_status sage_attn_fwd_varlen(const sage_varlen_shape* s, const void* q, const void* k, const void* v,
+                                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* o,
+                                 int32_t is_causal, float sm_scale, int32_t pv_dtype, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 /* FP16-PV preparation of V: the 16-bit values transposed to
  *   v_t [B,Hkv,d,sage_v_codes_stride(Nk)] (keys contiguous per channel, padding keys 0),
  * the layout the PV product reads in FP16/BF16 mode. */

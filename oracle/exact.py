@@ -67,3 +67,20 @@ def online_softmax_attention(q, k, v, *, is_causal: bool, sm_scale: float, bkv: 
                                               p_codec=None, work_dtype=np.float64)
             out[b, h] = o / l[:, None]
     return out
+
+
+def exact_attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, is_causal: bool, sm_scale: float):
+    """fp64 softmax attention of every sequence of a packed batch ([total, H, d]
+    arrays, B + 1 offsets); a sequence without keys has zero rows."""
+    q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+    out = np.zeros((q.shape[0], q.shape[1], v.shape[2]), np.float64)
+    cq = [int(x) for x in cu_seqlens_q]
+    ck = [int(x) for x in cu_seqlens_k]
+    for b in range(len(cq) - 1):
+        q0, q1, k0, k1 = cq[b], cq[b + 1], ck[b], ck[b + 1]
+        if q1 == q0 or k1 == k0:
+            continue
+        o = exact_attention(q[None, q0:q1].transpose(0, 2, 1, 3), k[None, k0:k1].transpose(0, 2, 1, 3),
+                            v[None, k0:k1].transpose(0, 2, 1, 3), is_causal=is_causal, sm_scale=sm_scale)
+        out[q0:q1] = o[0].transpose(1, 0, 2)
+    return out

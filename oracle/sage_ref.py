@@ -54,6 +54,12 @@ Readings where the pages are silent (each also listed in the design notes):
        extra cost: every query token has its own scale (BLK_Q = 1) and every
        run of 16 consecutive keys shares one (BLK_K = 16), blocks starting at
        token 0. All the per-block rules above then apply per group.
+  [R21] variable-length batches (heatdrop.ai review, "Key highlights": variable
+       sequence lengths within a batch) are packed along the token axis with
+       cumulative offsets; every sequence is one independent attention by the
+       method -- its own K channel mean, blocks from its own first token, its
+       own V channel scales, causal masking top-left inside the sequence. A
+       sequence with queries but no keys has zero output rows.
 """
 from __future__ import annotations
 
@@ -300,3 +306,27 @@ def sage_attention(q, k, v, *, dtype: str, is_causal: bool, sm_scale: float, pv:
     if return_fp64:
         return out
     return _round_to(out, dtype)
+
+
+def sage_attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, dtype: str, is_causal: bool, sm_scale: float,
+                          pv: str, blk_q: int = BLK_Q, blk_k: int = BLK_K, return_fp64: bool = False):
+    """Packed variable-length batch [R21].
+
+    ``q``: [total_q, Hq, d], ``k``/``v``: [total_k, Hkv, d] (float32 arrays of
+    the input values); ``cu_seqlens_*``: B + 1 non-decreasing offsets. Sequence
+    b is q[cu_q[b]:cu_q[b+1]] against k, v[cu_k[b]:cu_k[b+1]], run through
+    ``sage_attention`` as a batch of one. Returns [total_q, Hq, d].
+    """
+    q, k, v = (np.asarray(x, np.float32) for x in (q, k, v))
+    cq = [int(x) for x in cu_seqlens_q]
+    ck = [int(x) for x in cu_seqlens_k]
+    out = np.zeros((q.shape[0], q.shape[1], q.shape[2]), np.float64)
+    for b in range(len(cq) - 1):
+        q0, q1, k0, k1 = cq[b], cq[b + 1], ck[b], ck[b + 1]
+        if q1 == q0 or k1 == k0:
+            continue                                    # no rows, or no keys: zero rows
+        o = sage_attention(q[None, q0:q1], k[None, k0:k1], v[None, k0:k1], dtype=dtype, is_causal=is_causal,
+                           sm_scale=sm_scale, pv=pv, layout="NHD", blk_q=blk_q, blk_k=blk_k,
+                           return_fp64=return_fp64)
+        out[q0:q1] = o[0].transpose(1, 0, 2)
+    return out

@@ -8,13 +8,17 @@ the binding raises.
 Entry points (same names as the C ABI):
   sage_block_sizes, sage_v_codes_stride, sage_workspace_bytes,
   sage_quant_qk, sage_quant_v, sage_transpose_v, sage_attn_fwd,
-  sage_attn_fwd_codes, sage_debug_qk_i32.
+  sage_attn_fwd_codes, sage_debug_qk_i32, sage_varlen_workspace_bytes,
+  sage_attn_fwd_varlen.
 User-facing wrapper:
   sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None,
            pv_dtype="fp8", qk_quant_gran="per_block") -- the call shape the
   SageAttention pages show (cnnetsun.cn guide, basic usage; thu-ml/SageAttention
   repo card, "How to use"); qk_quant_gran="per_thread" selects the per-thread
   Q/K scales (heatdrop.ai review, "The interesting bit").
+  sageattn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                  max_seqlen_k, ...) -- packed variable-length batches
+  (heatdrop.ai review, "Key highlights").
 """
 from __future__ import annotations
 
@@ -53,12 +57,21 @@ _SIGNATURES = {
                                            ctypes.c_float, ctypes.c_int32, _vp]),
     "sage_debug_qk_i32": (ctypes.c_int, [_c_shape_p, _vp, _vp, _vp, _vp]),
     "sage_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "sage_varlen_workspace_bytes": (ctypes.c_size_t, [_c_shape_p, ctypes.c_int32]),
+    "sage_attn_fwd_varlen": (ctypes.c_int, [_c_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32,
+                                            ctypes.c_float, ctypes.c_int32, _vp, ctypes.c_size_t, _vp]),
 }
 
 
 class SageShape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("batch", "heads_q", "heads_kv", "seq_q", "seq_k", "head_dim", "layout", "dtype", "qk_gran")]
+
+
+class SageVarlenShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("batch", "heads_q", "heads_kv", "head_dim", "total_q", "total_k", "max_seqlen_q", "max_seqlen_k",
+                 "dtype", "qk_gran")]
 
 
 def _load():
@@ -226,6 +239,49 @@ def sage_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, is_causa
     return o
 
 
+def varlen_shape_of(q: torch.Tensor, k: torch.Tensor, cu_seqlens_q: torch.Tensor, max_seqlen_q: int,
+                    max_seqlen_k: int, qk_gran: str = "per_block") -> SageVarlenShape:
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("packed q, k, v must be 3-D: [total, heads, head_dim]")
+    if q.dtype not in DTYPES:
+        raise TypeError(f"q/k/v must be float16 or bfloat16, got {q.dtype}")
+    if cu_seqlens_q.dim() != 1 or cu_seqlens_q.numel() < 1:
+        raise ValueError("cu_seqlens must be 1-D with B + 1 entries")
+    return SageVarlenShape(cu_seqlens_q.numel() - 1, q.shape[1], k.shape[1], q.shape[2], q.shape[0], k.shape[0],
+                           int(max_seqlen_q), int(max_seqlen_k), DTYPES[q.dtype], QK_GRANS[qk_gran])
+
+
+def sage_varlen_workspace_bytes(shape: SageVarlenShape, pv_dtype: str = "fp8") -> int:
+    return int(lib.sage_varlen_workspace_bytes(_ref(shape), PV_DTYPES[pv_dtype]))
+
+
+def sage_attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                         cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int, *,
+                         is_causal: bool = False, sm_scale: Optional[float] = None, pv_dtype: str = "fp8",
+                         qk_gran: str = "per_block", out: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Packed variable-length batch: q [total_q, Hq, d], k/v [total_k, Hkv, d],
+    cu_seqlens int32 device tensors of B + 1 offsets. Returns o like q."""
+    _check_inputs(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    if cu_seqlens_k.numel() != cu_seqlens_q.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    if tuple(v.shape) != tuple(k.shape) or v.dtype != q.dtype or k.dtype != q.dtype:
+        raise ValueError("v must have k's shape and all inputs one dtype")
+    s = varlen_shape_of(q, k, cu_seqlens_q, max_seqlen_q, max_seqlen_k, qk_gran)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(s.head_dim)
+    dev = q.device
+    o = torch.empty_like(q) if out is None else out
+    need = sage_varlen_workspace_bytes(s, pv_dtype)
+    ws = workspace if workspace is not None and workspace.numel() >= need else _workspace(need, dev)
+    _check(lib.sage_attn_fwd_varlen(_ref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                                    _ptr(o), int(bool(is_causal)), float(sm_scale), PV_DTYPES[pv_dtype], _ptr(ws),
+                                    ws.numel(), _stream(dev)), "sage_attn_fwd_varlen")
+    return o
+
+
 def sage_debug_qk_i32(q_codes: torch.Tensor, k_codes: torch.Tensor) -> torch.Tensor:
     """INT32 S for canonical-order codes [B,Hq,Nq,d] x [B,Hkv,Nk,d] -> [B,Hq,Nq,Nk]."""
     _check_inputs(q_codes, k_codes)
@@ -264,7 +320,21 @@ def sageattn(q, k, v, tensor_layout: str = "HND", is_causal: bool = False, sm_sc
                          qk_gran=qk_quant_gran)
 
 
-__all__ = ["sageattn", "sage_attn_fwd", "sage_attn_fwd_codes", "sage_quant_qk", "sage_quant_v",
+def sageattn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                    is_causal: bool = False, sm_scale: Optional[float] = None, pv_dtype: str = "fp8",
+                    qk_quant_gran: str = "per_block"):
+    """Quantised attention over a packed variable-length batch (the
+    flash-attention varlen convention: tokens of all sequences concatenated,
+    cu_seqlens offsets, maximum lengths)."""
+    if qk_quant_gran not in QK_GRANS:
+        raise ValueError(f"qk_quant_gran must be one of {sorted(QK_GRANS)}, got {qk_quant_gran!r}")
+    return sage_attn_fwd_varlen(q.contiguous(), k.contiguous(), v.contiguous(), cu_seqlens_q.contiguous(),
+                                cu_seqlens_k.contiguous(), max_seqlen_q, max_seqlen_k, is_causal=is_causal,
+                                sm_scale=sm_scale, pv_dtype=pv_dtype, qk_gran=qk_quant_gran)
+
+
+__all__ = ["sageattn", "sageattn_varlen", "sage_attn_fwd_varlen", "sage_varlen_workspace_bytes",
+           "SageVarlenShape", "varlen_shape_of", "sage_attn_fwd", "sage_attn_fwd_codes", "sage_quant_qk", "sage_quant_v",
            "sage_transpose_v", "sage_debug_qk_i32",
            "sage_block_sizes", "sage_v_codes_stride", "sage_workspace_bytes", "make_shape", "shape_of",
            "SageError", "SageShape", "QK_GRANS", "lib", "LIB_PATH"]

@@ -412,7 +412,26 @@ __device__ __forceinline__ void attn_fwd_body(AttnArgs a) {
   int qp = id % n_qp;
   if (CAUSAL) qp = n_qp - 1 - qp;            // longest rows first
   const int b = bh / a.Hq, h = bh % a.Hq;
-  const int bhk = b * a.Hkv + h / (a.Hq / a.Hkv);
+  const int hk = h / (a.Hq / a.Hkv);
+  const int bhk = b * a.Hkv + hk;
+
+  // This work-group's query and key ranges: the whole batch entry, or (packed
+  // variable-length batch) its sequence's ranges from the span table, with the
+  // codes stored [H][total][D] and V^T in the sequence's columns of the rows.
+  int nq = a.Nq, nk = a.Nk;
+  int64_t q_off = (int64_t)bh * a.Nq * D, k_off = (int64_t)bhk * a.Nk * D;
+  int64_t v_off = (int64_t)bhk * D * a.n_pad, v_len = (int64_t)D * a.n_pad, o_tok = 0;
+  if (a.seq) {
+    const SeqSpan sp = a.seq[b];
+    nq = sp.nq;
+    nk = sp.nk;
+    if (2 * qp * kBq >= nq) return;              // no rows of this sequence here
+    q_off = ((int64_t)h * a.total_q + sp.q0) * D;
+    k_off = ((int64_t)hk * a.total_k + sp.k0) * D;
+    v_off = (int64_t)hk * D * a.n_pad + sp.kp0;
+    v_len = (int64_t)D * a.n_pad - sp.kp0;
+    o_tok = sp.q0;
+  }
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);
@@ -422,11 +441,11 @@ __device__ __forceinline__ void attn_fwd_body(AttnArgs a) {
   const int qi = q0w + (lane & 31);
 
   i32x4 qreg[NT];
-  load_q_operand<D>(a.q8 + (int64_t)bh * a.Nq * D, a.Nq, qi, g, qreg);
-  const bool grp_live = qt * kBq < a.Nq;
+  load_q_operand<D>(a.q8 + q_off, nq, qi, g, qreg);
+  const bool grp_live = qt * kBq < nq;
   // Q scale: the group's block, or (per-thread) the lane's own query.
   float cq;
-  if constexpr (FINE) cq = qi < a.Nq ? a.q_scale[(int64_t)bh * a.nbq + qi] * a.scale_log2 : 0.0f;
+  if constexpr (FINE) cq = qi < nq ? a.q_scale[(int64_t)bh * a.nbq + qi] * a.scale_log2 : 0.0f;
   else cq = grp_live ? a.q_scale[(int64_t)bh * a.nbq + qt] * a.scale_log2 : 0.0f;
   const __attribute__((address_space(4))) float* kscale =
       (const __attribute__((address_space(4))) float*)(a.k_scale + (int64_t)bhk * a.nbk);
@@ -435,16 +454,15 @@ __device__ __forceinline__ void attn_fwd_body(AttnArgs a) {
   // Only a group's last tile can need masking: it holds the ragged end of the
   // keys and, with causal masking (Nq == Nk, query tile == KV tile), the diagonal.
   auto tiles_for = [&](int q_tile) {
-    const int kv_end = CAUSAL ? min(a.Nk, (q_tile + 1) * kBq) : a.Nk;
+    const int kv_end = CAUSAL ? min(nk, (q_tile + 1) * kBq) : nk;
     return (kv_end + kBkv - 1) / kBkv;
   };
   const int n_g = grp_live ? tiles_for(qt) : 0;
-  const int n_wg = ((2 * qp + 1) * kBq < a.Nq) ? tiles_for(2 * qp + 1) : tiles_for(2 * qp);
+  const int n_wg = ((2 * qp + 1) * kBq < nq) ? tiles_for(2 * qp + 1) : tiles_for(2 * qp);
 
   constexpr int eb = FP8 ? 1 : 2;
-  const auto rk = make_rsrc(a.k8 + (int64_t)bhk * a.Nk * D, (uint32_t)a.Nk * D);
-  const auto rv = make_rsrc(reinterpret_cast<const uint8_t*>(a.vt) + (int64_t)bhk * D * a.n_pad * eb,
-                            (uint32_t)(D * a.n_pad * eb));
+  const auto rk = make_rsrc(a.k8 + k_off, (uint32_t)nk * D);
+  const auto rv = make_rsrc(reinterpret_cast<const uint8_t*>(a.vt) + v_off * eb, (uint32_t)(v_len * eb));
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   // All eight waves load the first K tile.
   const uint32_t koff = Stage::init_k(wv, lane);
@@ -530,7 +548,7 @@ __device__ __forceinline__ void attn_fwd_body(AttnArgs a) {
       c[2] = c[3] = c1;
     }
     __builtin_amdgcn_s_setprio(0);
-    softmax_phase<D, FP8, CAUSAL, decltype(masked)::value, FINE, T>(s, lane, t * kBkv, qi, a.Nk, c, st.m, pt);
+    softmax_phase<D, FP8, CAUSAL, decltype(masked)::value, FINE, T>(s, lane, t * kBkv, qi, nk, c, st.m, pt);
   };
   using Masked = std::true_type;
   using Full = std::false_type;
@@ -607,11 +625,13 @@ __device__ __forceinline__ void attn_fwd_body(AttnArgs a) {
   __builtin_amdgcn_s_setprio(0);
 
   // Epilogue: normalise, undo the V scale, round, store in the caller's layout.
-  if (qi < a.Nq) {
-    // (the FP8 path's row sum is already complete in both lanes of a query)
-    const float inv_l = 1.0f / (FP8 ? st.l : pair_sum(st.l));
+  if (qi < nq) {
+    // (the FP8 path's row sum is already complete in both lanes of a query; a
+    //  sequence of a packed batch without keys gets zero rows)
+    const float l = FP8 ? st.l : pair_sum(st.l);
+    const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
     uint16_t* orow = reinterpret_cast<uint16_t*>(a.o) + (int64_t)b * a.ogeo.batch_stride +
-                     (int64_t)h * a.ogeo.head_stride + (int64_t)qi * a.ogeo.tok_stride;
+                     (int64_t)h * a.ogeo.head_stride + (o_tok + qi) * a.ogeo.tok_stride;
     const float* vs = FP8 ? a.v_scale + (int64_t)bhk * D : nullptr;
 #pragma unroll
     for (int cb = 0; cb < NT; ++cb) {

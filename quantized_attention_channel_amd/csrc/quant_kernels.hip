@@ -19,10 +19,12 @@ constexpr int kStatChunk = 256;  // tokens per statistics work-group
 // Per (b, kv-head, 256-token chunk): fp64 sums of K over tokens per channel and,
 // optionally, fp32 max |V| per channel. Partials go to [B*H][chunks][D] in a
 // fixed order (no atomics), so the result does not depend on scheduling.
+// Packed batches (seq set): b is the sequence and its keys are the range
+// [k0, k0 + nk) of the packed tensor.
 template <typename T, int D, bool WITH_K, bool WITH_V>
 __global__ __launch_bounds__(256) void channel_stats_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, TensorGeom geo, int H, int N,
-    int chunks, double* __restrict__ ksum_part, float* __restrict__ vmax_part) {
+    int chunks, double* __restrict__ ksum_part, float* __restrict__ vmax_part, const SeqSpan* __restrict__ seq) {
   constexpr int TPR = D / 8;        // threads per token row (8 values each)
   constexpr int RPI = 256 / TPR;    // token rows per iteration
   __shared__ double red_k[RPI][D];
@@ -32,9 +34,14 @@ __global__ __launch_bounds__(256) void channel_stats_kernel(
   const int r0 = tid / TPR;
   const int bh = blockIdx.y;
   const int b = bh / H, h = bh % H;
-  const int64_t base = (int64_t)b * geo.batch_stride + (int64_t)h * geo.head_stride + col;
+  int64_t base = (int64_t)b * geo.batch_stride + (int64_t)h * geo.head_stride + col;
+  int n = N;
+  if (seq) {
+    n = seq[b].nk;
+    base += (int64_t)seq[b].k0 * geo.tok_stride;
+  }
   const int t_begin = blockIdx.x * kStatChunk;
-  const int t_end = min(N, t_begin + kStatChunk);
+  const int t_end = min(n, t_begin + kStatChunk);
 
   double ks[8];
   float vm[8];
@@ -83,11 +90,15 @@ __global__ __launch_bounds__(256) void channel_stats_kernel(
 
 // Per (b, kv-head, channel): mu = fp32(sum / N) (fp64 divide, one rounding to
 // fp32); s_v = a_v / 448 and 448 / a_v (both correctly rounded fp32 divides).
+// (packed batches: the token count is the sequence's; a sequence without keys
+// gets a zero mean)
 template <int D, bool WITH_K, bool WITH_V>
 __global__ __launch_bounds__(D) void channel_finalize_kernel(
     int N, int chunks, const double* __restrict__ ksum_part, const float* __restrict__ vmax_part,
-    float* __restrict__ k_mean, float* __restrict__ v_scale, float* __restrict__ v_inv) {
+    float* __restrict__ k_mean, float* __restrict__ v_scale, float* __restrict__ v_inv, int H,
+    const SeqSpan* __restrict__ seq) {
   const int bh = blockIdx.x, c = threadIdx.x;
+  const int n = seq ? seq[bh / H].nk : N;
   const int64_t p = (int64_t)bh * chunks * D + c;
   // Eight independent accumulators keep eight loads in flight (a single chain
   // would wait one memory latency per chunk); they are combined in a fixed
@@ -101,7 +112,7 @@ __global__ __launch_bounds__(D) void channel_finalize_kernel(
       for (int u = 0; u < U; ++u) s[u] += ksum_part[p + (int64_t)(i + u) * D];
     for (; i < chunks; ++i) s[0] += ksum_part[p + (int64_t)i * D];
     const double total = ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
-    k_mean[bh * D + c] = (float)(total / (double)N);
+    k_mean[bh * D + c] = n > 0 ? (float)(total / (double)n) : 0.0f;
   }
   if (WITH_V) {
     float a[U] = {};
@@ -124,10 +135,15 @@ __global__ __launch_bounds__(D) void channel_finalize_kernel(
 // whole group); smaller blocks share 64-token work-groups, and each pass
 // reduces its 256/G blocks over lane groups of G (in-wave butterflies up to
 // 64 lanes, one LDS exchange between waves above).
+// Packed batches (seq set): b is the sequence, its tokens are the range given
+// by the span's query (side 0) or key (side 1) pair, codes go to
+// [H][total][D], and nblk is the per-sequence scale stride (blocks past the
+// sequence get scale 0).
 template <typename T, int D, int BLK, bool SMOOTH>
 __global__ __launch_bounds__(256) void quant_int8_kernel(
     const uint16_t* __restrict__ x, TensorGeom geo, int H, int N, int nblk,
-    const float* __restrict__ mean, int8_t* __restrict__ codes, float* __restrict__ scale) {
+    const float* __restrict__ mean, int8_t* __restrict__ codes, float* __restrict__ scale,
+    const SeqSpan* __restrict__ seq, int side, int total) {
   constexpr int TPR = D / 8;
   constexpr int G = BLK * TPR;                   // chunks per block
   constexpr bool WHOLE = G >= 256;               // one block per work-group
@@ -141,7 +157,14 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(
   const int bh = blockIdx.y;
   const int b = bh / H, h = bh % H;
   const int t0 = blockIdx.x * TOKS;
-  const int64_t base = (int64_t)b * geo.batch_stride + (int64_t)h * geo.head_stride + col;
+  int64_t base = (int64_t)b * geo.batch_stride + (int64_t)h * geo.head_stride + col;
+  int8_t* out = codes + (int64_t)bh * N * D + col;
+  if (seq) {
+    const int32_t* sp = &seq[b].q0 + 2 * side;   // (q0, nq) or (k0, nk)
+    N = sp[1];
+    base += (int64_t)sp[0] * geo.tok_stride;
+    out = codes + ((int64_t)h * total + sp[0]) * D + col;
+  }
 
   float mu[8];
 #pragma unroll
@@ -201,7 +224,6 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(
     }
   }
 
-  int8_t* out = codes + (int64_t)bh * N * D + col;
 #pragma unroll
   for (int it = 0; it < ITER; ++it) {
     const int t = t0 + (it * 256 + tid) / TPR;
@@ -219,23 +241,27 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(
 }
 
 // Launch of quant_int8_kernel over N tokens of B*H heads.
+// (N: the token count, or the longest sequence of a packed batch)
 template <typename T, int D, int BLK, bool SMOOTH>
 static void launch_quant_int8(const void* x, TensorGeom geo, int BH, int H, int N, const float* mean,
-                              int8_t* codes, float* scale, hipStream_t st) {
+                              int8_t* codes, float* scale, const SeqSpan* seq, int side, int total,
+                              hipStream_t st) {
   constexpr int TOKS = BLK * (D / 8) >= 256 ? BLK : 64;
   const int nblk = (N + BLK - 1) / BLK;
   const int wgs = (N + TOKS - 1) / TOKS;
   hipLaunchKernelGGL((quant_int8_kernel<T, D, BLK, SMOOTH>), dim3(wgs, BH), dim3(256), 0, st,
-                     (const uint16_t*)x, geo, H, N, nblk, mean, codes, scale);
+                     (const uint16_t*)x, geo, H, N, nblk, mean, codes, scale, seq, side, total);
 }
 
 // One work-group per (b, kv-head, 64-token tile): V transposed to
 // [D][Nk_pad] with keys contiguous per channel. FP8: e4m3(v * (448/a_v[c]));
 // otherwise the 16-bit values are copied. Tokens >= N are written as 0.
+// Packed batches (seq set): b is the sequence, its keys [k0, k0 + nk) go to the
+// columns [kp0, kp0 + nk rounded up to the KV tile) of rows [H][D][n_pad].
 template <typename T, int D, bool FP8>
 __global__ __launch_bounds__(256) void transpose_v_kernel(
     const uint16_t* __restrict__ v, TensorGeom geo, int H, int N, int n_pad,
-    const float* __restrict__ v_inv, void* __restrict__ out) {
+    const float* __restrict__ v_inv, void* __restrict__ out, const SeqSpan* __restrict__ seq) {
   constexpr int EB = FP8 ? 1 : 2;               // output bytes per element
   constexpr int ROWB = 64 * EB;                 // bytes per channel row of the tile
   constexpr int UNITS = (64 / 4) * (D / 8);     // 4 tokens x 8 channels per unit
@@ -244,7 +270,15 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(
   const int bh = blockIdx.y;
   const int b = bh / H, h = bh % H;
   const int t0 = blockIdx.x * 64;
-  const int64_t base = (int64_t)b * geo.batch_stride + (int64_t)h * geo.head_stride;
+  int64_t base = (int64_t)b * geo.batch_stride + (int64_t)h * geo.head_stride;
+  int64_t dst0 = (int64_t)bh * D * n_pad;
+  if (seq) {
+    const SeqSpan sp = seq[b];
+    if (t0 >= (sp.nk + kVPad - 1) / kVPad * kVPad) return;   // past this sequence's padded keys
+    N = sp.nk;
+    base += (int64_t)sp.k0 * geo.tok_stride;
+    dst0 = (int64_t)h * D * n_pad + sp.kp0;
+  }
 
   for (int u = tid; u < UNITS; u += 256) {
     const int c0 = (u % (D / 8)) * 8;
@@ -280,7 +314,7 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(
     }
   }
   __syncthreads();
-  uint8_t* dst = reinterpret_cast<uint8_t*>(out) + ((int64_t)bh * D * n_pad + t0) * EB;
+  uint8_t* dst = reinterpret_cast<uint8_t*>(out) + (dst0 + t0) * EB;
   constexpr int CHUNKS = D * ROWB / 16;
   for (int ci = tid; ci < CHUNKS; ci += 256) {
     const int c = ci / (ROWB / 16), j = ci % (ROWB / 16);
@@ -289,7 +323,66 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(
   }
 }
 
+// Per-sequence spans of a packed batch from the caller's cu_seqlens (B + 1
+// non-decreasing offsets each). One work-group walks the sequences 256 at a
+// time with an LDS prefix sum for the padded V^T column starts. Every range is
+// clamped into the packed tensors and the longest-sequence bounds, and a
+// sequence whose padded keys would pass n_pad (possible only for a malformed
+// table) loses its keys, so no later kernel can index out of bounds.
+__global__ __launch_bounds__(256) void varlen_plan_kernel(const int32_t* __restrict__ cu_q,
+                                                          const int32_t* __restrict__ cu_k, int B, int total_q,
+                                                          int total_k, int max_q, int max_k, int n_pad,
+                                                          SeqSpan* __restrict__ out) {
+  __shared__ int part[256];          // <= 256 * 2^20: fits
+  __shared__ int64_t carry;          // a malformed table can pass 2^31
+  const int tid = threadIdx.x;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int b0 = 0; b0 < B; b0 += 256) {
+    const int b = b0 + tid;
+    SeqSpan sp{};
+    int padded = 0;
+    if (b < B) {
+      const int q0 = min(max(cu_q[b], 0), total_q), q1 = min(max(cu_q[b + 1], q0), total_q);
+      const int k0 = min(max(cu_k[b], 0), total_k), k1 = min(max(cu_k[b + 1], k0), total_k);
+      sp.q0 = q0;
+      sp.nq = min(q1 - q0, max_q);
+      sp.k0 = k0;
+      sp.nk = min(k1 - k0, max_k);
+      padded = (sp.nk + kVPad - 1) / kVPad * kVPad;
+    }
+    part[tid] = padded;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {          // inclusive scan
+      const int add = tid >= o ? part[tid - o] : 0;
+      __syncthreads();
+      part[tid] += add;
+      __syncthreads();
+    }
+    if (b < B) {
+      const int64_t kp0 = carry + part[tid] - padded;   // padded keys of the earlier sequences
+      if (kp0 + padded > n_pad) {
+        sp.nk = 0;
+        sp.kp0 = 0;
+      } else {
+        sp.kp0 = (int)kp0;
+      }
+      out[b] = sp;
+    }
+    __syncthreads();
+    if (tid == 0) carry += part[255];
+    __syncthreads();
+  }
+}
+
 // ---------------------------------------------------------------- host launchers
+hipError_t launch_varlen_plan(const int32_t* cu_q, const int32_t* cu_k, int B, int total_q, int total_k, int max_q,
+                              int max_k, int n_pad, SeqSpan* out, hipStream_t st) {
+  hipLaunchKernelGGL(varlen_plan_kernel, dim3(1), dim3(256), 0, st, cu_q, cu_k, B, total_q, total_k, max_q, max_k,
+                     n_pad, out);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 static hipError_t launch_qk_t(const QuantQKArgs& a, hipStream_t st) {
   const int chunks = (a.Nk + kStatChunk - 1) / kStatChunk;
@@ -297,21 +390,25 @@ static hipError_t launch_qk_t(const QuantQKArgs& a, hipStream_t st) {
   if (a.Nk > 0) {
     hipLaunchKernelGGL((channel_stats_kernel<T, D, true, false>), dim3(chunks, bhk), dim3(256), 0, st,
                        (const uint16_t*)a.k, (const uint16_t*)nullptr, a.kgeo, a.Hkv, a.Nk, chunks,
-                       a.ksum_part, (float*)nullptr);
+                       a.ksum_part, (float*)nullptr, a.seq);
     hipLaunchKernelGGL((channel_finalize_kernel<D, true, false>), dim3(bhk), dim3(D), 0, st,
                        a.Nk, chunks, a.ksum_part, (const float*)nullptr, a.k_mean, (float*)nullptr,
-                       (float*)nullptr);
+                       (float*)nullptr, a.Hkv, a.seq);
     if (a.fine)
-      launch_quant_int8<T, D, kFineBlkK, true>(a.k, a.kgeo, bhk, a.Hkv, a.Nk, a.k_mean, a.k_codes, a.k_scale, st);
+      launch_quant_int8<T, D, kFineBlkK, true>(a.k, a.kgeo, bhk, a.Hkv, a.Nk, a.k_mean, a.k_codes, a.k_scale,
+                                               a.seq, 1, a.total_k, st);
     else
-      launch_quant_int8<T, D, kBlkK, true>(a.k, a.kgeo, bhk, a.Hkv, a.Nk, a.k_mean, a.k_codes, a.k_scale, st);
+      launch_quant_int8<T, D, kBlkK, true>(a.k, a.kgeo, bhk, a.Hkv, a.Nk, a.k_mean, a.k_codes, a.k_scale,
+                                           a.seq, 1, a.total_k, st);
   }
   if (a.Nq > 0) {
     const int bhq = a.B * a.Hq;
     if (a.fine)
-      launch_quant_int8<T, D, kFineBlkQ, false>(a.q, a.qgeo, bhq, a.Hq, a.Nq, nullptr, a.q_codes, a.q_scale, st);
+      launch_quant_int8<T, D, kFineBlkQ, false>(a.q, a.qgeo, bhq, a.Hq, a.Nq, nullptr, a.q_codes, a.q_scale,
+                                                a.seq, 0, a.total_q, st);
     else
-      launch_quant_int8<T, D, kBlkQ, false>(a.q, a.qgeo, bhq, a.Hq, a.Nq, nullptr, a.q_codes, a.q_scale, st);
+      launch_quant_int8<T, D, kBlkQ, false>(a.q, a.qgeo, bhq, a.Hq, a.Nq, nullptr, a.q_codes, a.q_scale,
+                                            a.seq, 0, a.total_q, st);
   }
   return hipGetLastError();
 }
@@ -324,20 +421,22 @@ hipError_t launch_quant_qk(const QuantQKArgs& a, hipStream_t st) {
 template <typename T, int D>
 static hipError_t launch_v_t(const QuantVArgs& a, hipStream_t st) {
   const int bhk = a.B * a.Hkv;
-  const int tiles = a.n_pad / 64;
+  // (packed batches: n_pad is the padded-key bound of all sequences; a
+  //  sequence spans at most the longest one rounded up to the tile)
+  const int tiles = (a.seq ? (a.Nk + kVPad - 1) / kVPad * kVPad : a.n_pad) / 64;
   if (a.fp8) {
     const int chunks = (a.Nk + kStatChunk - 1) / kStatChunk;
     hipLaunchKernelGGL((channel_stats_kernel<T, D, false, true>), dim3(chunks, bhk), dim3(256), 0, st,
                        (const uint16_t*)nullptr, (const uint16_t*)a.v, a.vgeo, a.Hkv, a.Nk, chunks,
-                       (double*)nullptr, a.vmax_part);
+                       (double*)nullptr, a.vmax_part, a.seq);
     hipLaunchKernelGGL((channel_finalize_kernel<D, false, true>), dim3(bhk), dim3(D), 0, st,
                        a.Nk, chunks, (const double*)nullptr, a.vmax_part, (float*)nullptr, a.v_scale,
-                       a.v_inv);
+                       a.v_inv, a.Hkv, a.seq);
     hipLaunchKernelGGL((transpose_v_kernel<T, D, true>), dim3(tiles, bhk), dim3(256), 0, st,
-                       (const uint16_t*)a.v, a.vgeo, a.Hkv, a.Nk, a.n_pad, (const float*)a.v_inv, a.out);
+                       (const uint16_t*)a.v, a.vgeo, a.Hkv, a.Nk, a.n_pad, (const float*)a.v_inv, a.out, a.seq);
   } else {
     hipLaunchKernelGGL((transpose_v_kernel<T, D, false>), dim3(tiles, bhk), dim3(256), 0, st,
-                       (const uint16_t*)a.v, a.vgeo, a.Hkv, a.Nk, a.n_pad, (const float*)nullptr, a.out);
+                       (const uint16_t*)a.v, a.vgeo, a.Hkv, a.Nk, a.n_pad, (const float*)nullptr, a.out, a.seq);
   }
   return hipGetLastError();
 }

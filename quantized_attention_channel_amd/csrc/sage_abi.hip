@@ -3,6 +3,7 @@
 // Every entry point validates all arguments on the host before it makes any
 // HIP call, so an invalid request enqueues nothing; this also lets the
 // validation be exercised on a machine without a GPU.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -111,6 +112,84 @@ Layout layout_for(const Dims& d, bool fp8) {
 size_t qk_ws_bytes(const Dims& d) { return align256(size_t(d.B * d.Hkv * cdiv(d.Nk, kStatChunk) * d.D) * 8); }
 size_t v_ws_bytes(const Dims& d) {
   return align256(size_t(d.B * d.Hkv * d.D) * 4) + align256(size_t(d.B * d.Hkv * cdiv(d.Nk, kStatChunk) * d.D) * 4);
+}
+
+// ---- packed variable-length batches
+struct VDims {
+  int64_t B, Hq, Hkv, D, total_q, total_k, max_q, max_k, n_pad;
+  int64_t blk_q, blk_k;
+  bool bf16, fine;
+};
+
+sage_status check_varlen_shape(const sage_varlen_shape* s, VDims* d) {
+  if (!s) return SAGE_ERR_INVALID_ARGUMENT;
+  if (s->dtype != SAGE_DTYPE_F16 && s->dtype != SAGE_DTYPE_BF16) return SAGE_ERR_INVALID_ARGUMENT;
+  if (s->qk_gran != SAGE_QK_PER_BLOCK && s->qk_gran != SAGE_QK_PER_THREAD) return SAGE_ERR_INVALID_ARGUMENT;
+  if (s->batch < 0 || s->heads_q < 1 || s->heads_kv < 1 || s->head_dim < 1 || s->total_q < 0 || s->total_k < 0 ||
+      s->max_seqlen_q < 0 || s->max_seqlen_k < 0)
+    return SAGE_ERR_INVALID_ARGUMENT;
+  if (s->heads_q % s->heads_kv != 0) return SAGE_ERR_INVALID_ARGUMENT;
+  if (s->max_seqlen_q > kMaxSeq || s->max_seqlen_k > kMaxSeq) return SAGE_ERR_INVALID_ARGUMENT;
+  if (s->head_dim != 64 && s->head_dim != 128) return SAGE_ERR_UNSUPPORTED;
+  d->B = s->batch;
+  d->Hq = s->heads_q;
+  d->Hkv = s->heads_kv;
+  d->D = s->head_dim;
+  d->total_q = s->total_q;
+  d->total_k = s->total_k;
+  d->max_q = s->max_seqlen_q;
+  d->max_k = s->max_seqlen_k;
+  d->bf16 = s->dtype == SAGE_DTYPE_BF16;
+  d->fine = s->qk_gran == SAGE_QK_PER_THREAD;
+  d->blk_q = d->fine ? sage::kFineBlkQ : sage::kBlkQ;
+  d->blk_k = d->fine ? sage::kFineBlkK : sage::kBlkK;
+  if (d->B * d->Hq > (int64_t(1) << 24)) return SAGE_ERR_INVALID_ARGUMENT;
+  // padded V^T columns: every sequence's keys rounded up to the tile fit here
+  if (d->total_k + (sage::kVPad - 1) * d->B > (int64_t(1) << 24) - sage::kVPad) return SAGE_ERR_INVALID_ARGUMENT;
+  d->n_pad = round_up(d->total_k + (sage::kVPad - 1) * d->B, sage::kVPad);
+  if (d->n_pad == 0) d->n_pad = sage::kVPad;
+  return SAGE_OK;
+}
+
+// Workspace of a packed batch: the span table, codes [H][total][D], scales
+// and partials with per-sequence strides from the maximum lengths, V^T rows
+// [Hkv][D][n_pad].
+struct VLayout {
+  size_t spans, q_codes, q_scale, k_codes, k_scale, k_mean, vt, v_scale, v_inv, ksum, vmax, total;
+};
+
+VLayout varlen_layout_for(const VDims& d, bool fp8) {
+  VLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  const int64_t nbq = std::max<int64_t>(1, cdiv(d.max_q, d.blk_q)), nbk = std::max<int64_t>(1, cdiv(d.max_k, d.blk_k));
+  const int64_t chunks = cdiv(d.max_k, kStatChunk);
+  L.spans = take(size_t(d.B) * sizeof(sage::SeqSpan));
+  L.q_codes = take(size_t(d.Hq * d.total_q * d.D));
+  L.q_scale = take(size_t(d.B * d.Hq * nbq) * 4);
+  L.k_codes = take(size_t(d.Hkv * d.total_k * d.D));
+  L.k_scale = take(size_t(d.B * d.Hkv * nbk) * 4);
+  L.k_mean = take(size_t(d.B * d.Hkv * d.D) * 4);
+  L.vt = take(size_t(d.Hkv * d.D * d.n_pad) * (fp8 ? 1 : 2));
+  L.v_scale = take(size_t(d.B * d.Hkv * d.D) * 4);
+  L.v_inv = take(size_t(d.B * d.Hkv * d.D) * 4);
+  L.ksum = take(size_t(d.B * d.Hkv * chunks * d.D) * 8);
+  L.vmax = take(size_t(d.B * d.Hkv * chunks * d.D) * 4);
+  L.total = off;
+  return L;
+}
+
+// Packed [total, H, d] tensors: one long batch entry in NHD order.
+TensorGeom packed_geom(int64_t H, int64_t D) {
+  TensorGeom g;
+  g.batch_stride = 0;
+  g.head_stride = D;
+  g.tok_stride = H * D;
+  return g;
 }
 
 template <typename P>
@@ -282,6 +361,105 @@ sage_status sage_attn_fwd(const sage_shape* s, const void* q, const void* k, con
   aa.bf16 = d.bf16;
   aa.fp8 = fp8;
   aa.fine = d.fine;
+  return from_hip(sage::launch_attn(aa, hs));
+}
+
+size_t sage_varlen_workspace_bytes(const sage_varlen_shape* s, int32_t pv_dtype) {
+  VDims d;
+  if (check_varlen_shape(s, &d) != SAGE_OK) return 0;
+  if (pv_dtype != SAGE_PV_FP16 && pv_dtype != SAGE_PV_FP8_E4M3) return 0;
+  return varlen_layout_for(d, pv_dtype == SAGE_PV_FP8_E4M3).total;
+}
+
+sage_status sage_attn_fwd_varlen(const sage_varlen_shape* s, const void* q, const void* k, const void* v,
+                                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* o,
+                                 int32_t is_causal, float sm_scale, int32_t pv_dtype, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  VDims d;
+  sage_status st = check_varlen_shape(s, &d);
+  if (st != SAGE_OK) return st;
+  if (pv_dtype != SAGE_PV_FP16 && pv_dtype != SAGE_PV_FP8_E4M3) return SAGE_ERR_INVALID_ARGUMENT;
+  if (is_causal != 0 && is_causal != 1) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (d.B == 0 || d.total_q == 0 || d.max_q == 0) return SAGE_OK;
+  if (!q || !k || !v || !o || !cu_seqlens_q || !cu_seqlens_k || !workspace) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(cu_seqlens_q, 4) ||
+      !aligned(cu_seqlens_k, 4) || !aligned(workspace, 256))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  const bool fp8 = pv_dtype == SAGE_PV_FP8_E4M3;
+  const VLayout L = varlen_layout_for(d, fp8);
+  if (workspace_bytes < L.total) return SAGE_ERR_WORKSPACE;
+  const size_t qbytes = size_t(d.total_q * d.Hq * d.D) * 2, kvbytes = size_t(d.total_k * d.Hkv * d.D) * 2;
+  if (overlaps(o, qbytes, q, qbytes) || overlaps(o, qbytes, k, kvbytes) || overlaps(o, qbytes, v, kvbytes) ||
+      overlaps(o, qbytes, workspace, L.total))
+    return SAGE_ERR_INVALID_ARGUMENT;
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  sage::SeqSpan* spans = at<sage::SeqSpan>(workspace, L.spans);
+  hipError_t e = sage::launch_varlen_plan(cu_seqlens_q, cu_seqlens_k, int(d.B), int(d.total_q), int(d.total_k),
+                                          int(d.max_q), int(d.max_k), int(d.n_pad), spans, hs);
+  if (e != hipSuccess) return SAGE_ERR_HIP;
+
+  sage::QuantQKArgs qa{};
+  qa.q = q;
+  qa.k = k;
+  qa.qgeo = packed_geom(d.Hq, d.D);
+  qa.kgeo = packed_geom(d.Hkv, d.D);
+  qa.B = int(d.B), qa.Hq = int(d.Hq), qa.Hkv = int(d.Hkv), qa.Nq = int(d.max_q), qa.Nk = int(d.max_k);
+  qa.D = int(d.D);
+  qa.bf16 = d.bf16;
+  qa.fine = d.fine;
+  qa.q_codes = at<int8_t>(workspace, L.q_codes);
+  qa.q_scale = at<float>(workspace, L.q_scale);
+  qa.k_codes = at<int8_t>(workspace, L.k_codes);
+  qa.k_scale = at<float>(workspace, L.k_scale);
+  qa.k_mean = at<float>(workspace, L.k_mean);
+  qa.ksum_part = at<double>(workspace, L.ksum);
+  qa.seq = spans;
+  qa.total_q = int(d.total_q);
+  qa.total_k = int(d.total_k);
+  e = sage::launch_quant_qk(qa, hs);
+  if (e != hipSuccess) return SAGE_ERR_HIP;
+
+  sage::QuantVArgs va{};
+  va.v = v;
+  va.vgeo = packed_geom(d.Hkv, d.D);
+  va.B = int(d.B), va.Hkv = int(d.Hkv), va.Nk = int(d.max_k), va.D = int(d.D);
+  va.n_pad = int(d.n_pad);
+  va.bf16 = d.bf16;
+  va.fp8 = fp8;
+  va.out = at<void>(workspace, L.vt);
+  va.v_scale = at<float>(workspace, L.v_scale);
+  va.v_inv = at<float>(workspace, L.v_inv);
+  va.vmax_part = at<float>(workspace, L.vmax);
+  va.seq = spans;
+  if (d.max_k > 0) {
+    e = sage::launch_quant_v(va, hs);
+    if (e != hipSuccess) return SAGE_ERR_HIP;
+  }
+
+  sage::AttnArgs aa{};
+  aa.q8 = qa.q_codes;
+  aa.q_scale = qa.q_scale;
+  aa.k8 = qa.k_codes;
+  aa.k_scale = qa.k_scale;
+  aa.vt = va.out;
+  aa.v_scale = va.v_scale;
+  aa.o = o;
+  aa.ogeo = packed_geom(d.Hq, d.D);
+  aa.B = int(d.B), aa.Hq = int(d.Hq), aa.Hkv = int(d.Hkv), aa.Nq = int(d.max_q), aa.Nk = int(d.max_k);
+  aa.D = int(d.D);
+  aa.n_pad = int(d.n_pad);
+  aa.nbq = int(std::max<int64_t>(1, cdiv(d.max_q, d.blk_q)));
+  aa.nbk = int(std::max<int64_t>(1, cdiv(d.max_k, d.blk_k)));
+  aa.scale_log2 = sm_scale * sage::kLog2E;
+  aa.causal = is_causal != 0;
+  aa.bf16 = d.bf16;
+  aa.fp8 = fp8;
+  aa.fine = d.fine;
+  aa.seq = spans;
+  aa.total_q = int(d.total_q);
+  aa.total_k = int(d.total_k);
   return from_hip(sage::launch_attn(aa, hs));
 }
 

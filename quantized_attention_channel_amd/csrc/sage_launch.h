@@ -14,6 +14,21 @@ struct TensorGeom {
   int64_t tok_stride;
 };
 
+// One sequence of a packed variable-length batch (tokens of all sequences
+// concatenated, [total, H, d]): its query and key token ranges and the first
+// column of its keys in the padded V^T rows. Written by the plan kernel from
+// the caller's cu_seqlens, clamped so that every range lies inside the packed
+// tensors and the padded V^T rows.
+struct SeqSpan {
+  int32_t q0, nq, k0, nk, kp0, reserved[3];
+};
+
+// Dense batches leave `seq` null. Packed batches set it, and then B is the
+// sequence count, Nq/Nk the maximum sequence lengths (they size the grids and
+// the per-sequence scale and partial strides), the geometries are the packed
+// [total, H, d] ones, codes are stored [H][total][d] and V^T rows
+// [Hkv][d][n_pad] with n_pad the padded-key bound.
+
 struct QuantQKArgs {
   const void* q;
   const void* k;
@@ -27,6 +42,8 @@ struct QuantQKArgs {
   float* k_scale;
   float* k_mean;
   double* ksum_part;   // [B*Hkv][ceil(Nk/256)][D]
+  const SeqSpan* seq;  // packed batches only
+  int total_q, total_k;
 };
 
 struct QuantVArgs {
@@ -38,6 +55,7 @@ struct QuantVArgs {
   float* v_scale;      // FP8 only
   float* v_inv;        // FP8 only (448 / a_v)
   float* vmax_part;    // FP8 only: [B*Hkv][ceil(Nk/256)][D]
+  const SeqSpan* seq;  // packed batches only
 };
 
 struct AttnArgs {
@@ -54,6 +72,8 @@ struct AttnArgs {
   float scale_log2;     // sm_scale * log2(e)
   bool causal, bf16, fp8;
   bool fine;            // per-thread scales: q_scale per query, k_scale per 16 keys
+  const SeqSpan* seq;   // packed batches only
+  int total_q, total_k;
 };
 
 struct DebugQKArgs {
@@ -63,6 +83,8 @@ struct DebugQKArgs {
   int B, Hq, Hkv, Nq, Nk, D;
 };
 
+hipError_t launch_varlen_plan(const int32_t* cu_q, const int32_t* cu_k, int B, int total_q, int total_k,
+                              int max_q, int max_k, int n_pad, SeqSpan* out, hipStream_t st);
 hipError_t launch_quant_qk(const QuantQKArgs& a, hipStream_t st);
 hipError_t launch_quant_v(const QuantVArgs& a, hipStream_t st);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);

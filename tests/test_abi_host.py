@@ -10,6 +10,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 import quantized_attention_channel_amd as sage
@@ -185,3 +186,108 @@ def test_python_wrapper_rejects_unsupported_sdpa_arguments():
         sage.sageattn(q, q, q, bogus=1)
     with pytest.raises(ValueError):                       # CPU tensors never reach the library
         sage.sageattn(q, q, q)
+
+
+# ------------------------------------------------------------------ packed variable-length batches
+def _vshape(**kw):
+    base = dict(B=3, Hq=4, Hkv=2, d=128, tq=500, tk=700, mq=300, mk=400, dtype=0, gran=0)
+    base.update(kw)
+    return sage.SageVarlenShape(base["B"], base["Hq"], base["Hkv"], base["d"], base["tq"], base["tk"], base["mq"],
+                                base["mk"], base["dtype"], base["gran"])
+
+
+def test_varlen_shape_struct_matches_the_header():
+    assert ctypes.sizeof(sage.SageVarlenShape) == 10 * 4
+    assert [f[0] for f in sage.SageVarlenShape._fields_] == [
+        "batch", "heads_q", "heads_kv", "head_dim", "total_q", "total_k", "max_seqlen_q", "max_seqlen_k", "dtype",
+        "qk_gran"]
+
+
+def test_varlen_workspace_holds_the_packed_intermediates():
+    s = _vshape()
+    w8 = sage.sage_varlen_workspace_bytes(s, "fp8")
+    # codes [H][total][d], V^T [Hkv][d][padded total], the span table
+    assert w8 >= 4 * 500 * 128 + 2 * 700 * 128 + 2 * 128 * (700 + 127 * 3) + 3 * 32
+    assert sage.sage_varlen_workspace_bytes(s, "fp16") > w8
+    assert sage.sage_varlen_workspace_bytes(_vshape(gran=1), "fp8") > w8      # finer scales
+    assert sage.lib.sage_varlen_workspace_bytes(None, 1) == 0
+    assert sage.lib.sage_varlen_workspace_bytes(ctypes.byref(_vshape(d=96)), 1) == 0
+
+
+def _vattn(shape, q=FAKE, k=FAKE + 2 ** 30, v=FAKE + 2 ** 31, cq=FAKE + 2 ** 34, ck=FAKE + 2 ** 34 + 64,
+           o=FAKE + 3 * 2 ** 30, causal=0, scale=0.1, pv=1, ws=FAKE + 2 ** 33, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = sage.lib.sage_varlen_workspace_bytes(ctypes.byref(shape), pv) if shape is not None else 0
+    sp = None if shape is None else ctypes.byref(shape)
+    return sage.lib.sage_attn_fwd_varlen(sp, q, k, v, cq, ck, o, causal, scale, pv, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,kw,want", [
+    ("null shape", dict(shape=None), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("Hq % Hkv", dict(shape=_vshape(Hq=3)), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("bad dtype", dict(shape=_vshape(dtype=5)), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("bad qk_gran", dict(shape=_vshape(gran=3)), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("negative total", dict(shape=_vshape(tk=-1)), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("max seqlen too long", dict(shape=_vshape(mq=(1 << 20) + 1)), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("padded keys too many", dict(shape=_vshape(tk=(1 << 24) - 300)), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("head dim 96", dict(shape=_vshape(d=96)), sage.SAGE_ERR_UNSUPPORTED),
+    ("causal flag 2", dict(shape=_vshape(), causal=2), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("sm_scale nan", dict(shape=_vshape(), scale=float("nan")), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("bad pv", dict(shape=_vshape(), pv=2), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("null cu_seqlens_q", dict(shape=_vshape(), cq=None), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("null cu_seqlens_k", dict(shape=_vshape(), ck=None), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("misaligned cu_seqlens", dict(shape=_vshape(), cq=FAKE + 2 ** 34 + 2), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("null o", dict(shape=_vshape(), o=None), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("misaligned v", dict(shape=_vshape(), v=FAKE + 2 ** 31 + 8), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("small workspace", dict(shape=_vshape(), ws_bytes=4096), sage.SAGE_ERR_WORKSPACE),
+    ("o aliases q", dict(shape=_vshape(), o=FAKE + 4096), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("no sequences is a no-op", dict(shape=_vshape(B=0), q=None, o=None), sage.SAGE_OK),
+    ("no queries is a no-op", dict(shape=_vshape(tq=0), q=None, o=None), sage.SAGE_OK),
+])
+def test_attn_fwd_varlen_validation(case, kw, want):
+    assert _vattn(**kw) == want, case
+
+
+def _plan_model(cq, ck, total_q, total_k, max_q, max_k, n_pad):
+    """The span rules of the plan kernel: clamp, then pack the padded keys."""
+    spans, carry = [], 0
+    for b in range(len(cq) - 1):
+        q0 = min(max(cq[b], 0), total_q)
+        q1 = min(max(cq[b + 1], q0), total_q)
+        k0 = min(max(ck[b], 0), total_k)
+        k1 = min(max(ck[b + 1], k0), total_k)
+        nq, nk = min(q1 - q0, max_q), min(k1 - k0, max_k)
+        padded = -(-nk // 128) * 128
+        kp0 = carry
+        carry += padded
+        if kp0 + padded > n_pad:
+            nk, kp0 = 0, 0
+        spans.append((q0, nq, k0, nk, kp0))
+    return spans
+
+
+def test_varlen_plan_clamps_every_span_into_bounds():
+    rng = np.random.default_rng(5)
+    for trial in range(300):
+        B = int(rng.integers(1, 40))
+        total_q, total_k = int(rng.integers(0, 5000)), int(rng.integers(0, 5000))
+        max_q, max_k = int(rng.integers(0, 3000)), int(rng.integers(0, 3000))
+        n_pad = -(-(total_k + 127 * B) // 128) * 128 or 128
+        if trial % 3 == 0:                               # well-formed tables
+            cuts = np.sort(rng.integers(0, total_k + 1, B - 1))
+            ck = [0, *cuts.tolist(), total_k]
+            cq = ck if total_q == total_k else [0, *np.sort(rng.integers(0, total_q + 1, B - 1)).tolist(), total_q]
+        else:                                            # arbitrary, also negative and decreasing
+            cq = rng.integers(-100, total_q + 200, B + 1).tolist()
+            ck = rng.integers(-100, total_k + 200, B + 1).tolist()
+        padded_cols = set()
+        for q0, nq, k0, nk, kp0 in _plan_model(cq, ck, total_q, total_k, max_q, max_k, n_pad):
+            assert 0 <= q0 and q0 + nq <= total_q and 0 <= nq <= max_q
+            assert 0 <= k0 and k0 + nk <= total_k and 0 <= nk <= max_k
+            assert 0 <= kp0 and kp0 + -(-nk // 128) * 128 <= n_pad
+            cols = set(range(kp0, kp0 + -(-nk // 128) * 128))
+            assert not cols & padded_cols                # V^T column slots never overlap
+            padded_cols |= cols
+        if trial % 3 == 0 and max(np.diff(ck)) <= max_k:  # well-formed: nothing is dropped
+            spans = _plan_model(cq, ck, total_q, total_k, max_q, max_k, n_pad)
+            assert [s[3] for s in spans] == np.diff(ck).tolist()

@@ -128,6 +128,8 @@ SHAPES = [(nq, nk, False) for nq in (1, 100, 128, 129, 255, 256, 257, 300, 640, 
           for nk in (1, 7, 128, 129, 300, 1000, 4096)]
 SHAPES += [(n, n, True) for n in (1, 65, 127, 128, 129, 255, 256, 257, 333, 384, 512, 640, 1000, 4096, 8192)]
 SHAPES += [(32768, 32768, False), (32768, 32768, True), (16384, 16384, False)]
+# a sequence of a packed batch can have queries but no keys: both groups idle
+SHAPES += [(nq, 0, c) for nq in (1, 200, 300) for c in (False, True)]
 
 
 @pytest.mark.parametrize("nq,nk,causal", SHAPES)

@@ -129,3 +129,91 @@ def sample_rows(n: int, count: int, block: int, seed: int = 1):
     pick = torch.randperm(n, generator=g)[: min(count, n)].tolist()
     edges = [r for r in (0, 1, block - 1, block, n - 2, n - 1) if 0 <= r < n]
     return sorted(set(pick) | set(edges))
+
+
+# ------------------------------------------------------------------ packed variable-length batches
+@dataclasses.dataclass(frozen=True)
+class VarlenWorkload:
+    """B sequences packed along the token axis ([total, H, d] tensors).
+
+    Recipe: the same generator, seed and variances as ``Workload``; Q, K, V are
+    drawn as [total, H, d] standard normals in that order, then one K channel
+    offset per (sequence, kv head) [B, Hkv, d], added to that sequence's keys
+    (so each sequence has its own channel bias for its own smoothing)."""
+    name: str
+    lens_q: tuple
+    lens_k: tuple
+    Hq: int
+    Hkv: int
+    d: int
+    dtype: str
+    causal: bool
+    pv: str
+    k_off_var: float = 4.0
+    seed: int = 0
+
+    @property
+    def sm_scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def B(self) -> int:
+        return len(self.lens_q)
+
+    def with_(self, **kw) -> "VarlenWorkload":
+        return dataclasses.replace(self, **kw)
+
+    def cu_seqlens(self):
+        cq, ck = [0], [0]
+        for a, b in zip(self.lens_q, self.lens_k):
+            cq.append(cq[-1] + a)
+            ck.append(ck[-1] + b)
+        return cq, ck
+
+    def attention_ops(self) -> float:
+        """Counted operations 4*Hq*d per visible (query, key) pair; causal
+        masking is top-left inside each sequence."""
+        pairs = 0
+        for nq, nk in zip(self.lens_q, self.lens_k):
+            if self.causal:
+                m = min(nq, nk)                    # rows i < nk see i + 1 keys, later rows all nk
+                pairs += m * (m + 1) // 2 + (nq - m) * nk
+            else:
+                pairs += nq * nk
+        return 4.0 * self.Hq * self.d * pairs
+
+
+def seq_lengths(count: int, lo: int, hi: int, seed: int = 0):
+    """``count`` seeded sequence lengths, log-uniform in [lo, hi] (a serving
+    mix: many short requests and a few long ones)."""
+    g = torch.Generator().manual_seed(seed)
+    u = torch.rand(count, generator=g, dtype=torch.float64)
+    return tuple(int(round(math.exp(math.log(lo) + float(x) * (math.log(hi) - math.log(lo))))) for x in u)
+
+
+def generate_varlen(w: VarlenWorkload, device: Optional[str] = None):
+    """Return (q, k, v, cu_seqlens_q, cu_seqlens_k): packed tensors in the
+    workload's dtype and int32 offsets, generated on the CPU and moved to
+    ``device``."""
+    g = torch.Generator().manual_seed(w.seed)
+    tq, tk = sum(w.lens_q), sum(w.lens_k)
+    q = torch.randn((tq, w.Hq, w.d), generator=g, dtype=torch.float32)
+    k = torch.randn((tk, w.Hkv, w.d), generator=g, dtype=torch.float32)
+    v = torch.randn((tk, w.Hkv, w.d), generator=g, dtype=torch.float32)
+    off = torch.randn((w.B, w.Hkv, w.d), generator=g, dtype=torch.float32) * math.sqrt(w.k_off_var)
+    cq, ck = w.cu_seqlens()
+    for b in range(w.B):
+        k[ck[b]:ck[b + 1]] += off[b]
+    dt = TORCH_DTYPE[w.dtype]
+    q, k, v = q.to(dt), k.to(dt), v.to(dt)
+    cu_q = torch.tensor(cq, dtype=torch.int32)
+    cu_k = torch.tensor(ck, dtype=torch.int32)
+    if device is not None:
+        q, k, v, cu_q, cu_k = (t.to(device) for t in (q, k, v, cu_q, cu_k))
+    return q, k, v, cu_q, cu_k
+
+
+# An LLM-prefill serving mix: 16 requests, 256 to 16384 tokens, GQA, causal.
+VARLEN_PREFILL = VarlenWorkload("varlen_prefill_16seq_hq32_hkv8_d128_bf16", lens_q=seq_lengths(16, 256, 16384),
+                                lens_k=seq_lengths(16, 256, 16384), Hq=32, Hkv=8, d=128, dtype="bf16",
+                                causal=True, pv="fp8")
