@@ -15,8 +15,9 @@ roofline     = the attention kernel alone: the same counted operations / its
 cpu_baseline = the CPU oracle on a bounded sample of the same workload.
 
 Default workload: B=1, H=32, N=32768, d=128, fp16, non-causal, PV in e4m3 (the
-long-sequence peak workload), per-block Q/K scales; the causal variant and the
-per-thread-scale variant are reported alongside.
+long-sequence peak workload), per-block Q/K scales; the causal variant, the per-thread-scale variant and a
+packed variable-length serving mix (16 causal GQA sequences of 256-16384
+tokens, one sage_attn_fwd_varlen call per step) are reported alongside.
 """
 from __future__ import annotations
 
@@ -216,6 +217,35 @@ def measure(w: W.Workload, pv: str, steps: int, warmup: int, qk_gran: str = "per
                 quant_bytes=3.0 * (w.B * w.Hq * w.N * w.d + 2 * w.B * w.Hkv * w.N * w.d))
 
 
+def measure_varlen(w: W.VarlenWorkload, steps: int, warmup: int):
+    """One sage_attn_fwd_varlen call per step (quantisation and attention of
+    every sequence of the packed batch), timed with HIP events."""
+    import quantized_attention_channel_amd as sage
+    q, k, v, cq, ck = W.generate_varlen(w, device="cuda")
+    mq, mk = max(w.lens_q), max(w.lens_k)
+    shape = sage.varlen_shape_of(q, k, cq, mq, mk)
+    ws = torch.empty(max(sage.sage_varlen_workspace_bytes(shape, w.pv), 256), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+
+    def run():
+        sage.sage_attn_fwd_varlen(q, k, v, cq, ck, mq, mk, is_causal=w.causal, sm_scale=w.sm_scale,
+                                  pv_dtype=w.pv, out=o, workspace=ws)
+    for _ in range(warmup):
+        run()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(steps):
+        run()
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    ops = w.attention_ops()
+    return {"value": round(ops / (ms * 1e-3) / 1e12, 2), "unit": "TOPS", "ms_per_step": round(ms, 4),
+            "workload": w.name, "sequences": w.B, "tokens": sum(w.lens_q), "causal": w.causal, "pv": w.pv,
+            "ops_per_step": ops}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -280,7 +310,8 @@ def main():
                     "attention_frac": round(rv["attn_tops"] / PEAK_TOPS, 4),
                     "attention_ms": round(rv["attn_ms"], 4), "quant_ms": round(rv["quant_ms"], 4)}
         out["variants"] = {"causal": variant(measure(w.with_(causal=True), pv, args.steps, args.warmup)),
-                           "per_thread": variant(measure(w, pv, args.steps, args.warmup, "per_thread"))}
+                           "per_thread": variant(measure(w, pv, args.steps, args.warmup, "per_thread")),
+                           "varlen": measure_varlen(W.VARLEN_PREFILL, args.steps, args.warmup)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, pv, args.cpu_rows, args.qk_gran)
     else:

@@ -177,7 +177,8 @@ size_t sage_varlen_workspace_bytes(const sage_varlen_shape* s, int32_t pv_dtype)
 /* The whole forward over a packed variable-length batch (see above); the other
  * arguments are as for sage_attn_fwd. Limits: 1 <= Hq, Hkv with Hq % Hkv == 0,
  * head_dim in {64, 128}, B * Hq <= 2^24, total_k + 127 * B <= 2^24 - 128 (the
- * padded key columns of the transposed V). B == 0 or total_q == 0 is a no-op.
+ * padded key columns of the transposed V), (total_q / 256 + B) * Hq <= 2^30
+ * (the attention work list). B == 0 or total_q == 0 is a no-op.
  * cu_seqlens pointers must be 4-byte aligned; q, k, v, o 16-byte aligned. */
 sage_status sage_attn_fwd_varlen(const sage_varlen_shape* s, const void* q, const void* k, const void* v,
                                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* o,

@@ -404,13 +404,36 @@ __device__ __forceinline__ void attn_fwd_body(AttnArgs a) {
   // Work decomposition. Work-groups are dealt round-robin to the 8 XCDs; give
   // each XCD a contiguous range of (head, query) work so the work-groups that
   // share an XCD's L2 stream the same head's K/V tiles.
+  //   Packed variable-length batches: the sequences' work differs widely, so
+  // contiguous (sequence, head) ranges would load some XCDs several times more
+  // than others. There XCD x takes heads [x Hq/8, (x+1) Hq/8) of every sequence
+  // (when Hq % 8 == 0; else plain round-robin) and walks the work list of
+  // query pairs: sequence by sequence, each sequence's pairs from the last
+  // (longest under causal masking) down, the heads of one pair side by side.
+  // The work-groups running together then share one sequence's K/V tiles in
+  // the XCD's L2, and no work-group is spent on pairs a sequence lacks.
   const int n_qp = (a.Nq + 2 * kBq - 1) / (2 * kBq);
-  const int total = n_qp * a.B * a.Hq;
-  int id = blockIdx.x;
-  if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
-  const int bh = id / n_qp;
-  int qp = id % n_qp;
-  if (CAUSAL) qp = n_qp - 1 - qp;            // longest rows first
+  int bh, qp;
+  if (a.seq) {
+    int heads = a.Hq, h0 = 0, j = blockIdx.x;
+    if ((a.Hq & 7) == 0) {
+      heads = a.Hq >> 3;
+      h0 = (blockIdx.x & 7) * heads;
+      j = blockIdx.x >> 3;
+    }
+    const int qpi = j / heads;                                   // work-list query pair
+    const int sb = qpi < a.n_owner ? a.qp_owner[qpi] : -1;
+    if (sb < 0) return;                                          // past the work list
+    qp = (a.seq[sb].nq + 2 * kBq - 1) / (2 * kBq) - 1 - (qpi - a.seq[sb].qp0);
+    bh = sb * a.Hq + h0 + j % heads;
+  } else {
+    const int total = n_qp * a.B * a.Hq;
+    int id = blockIdx.x;
+    if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
+    bh = id / n_qp;
+    qp = id % n_qp;
+    if (CAUSAL) qp = n_qp - 1 - qp;            // longest rows first
+  }
   const int b = bh / a.Hq, h = bh % a.Hq;
   const int hk = h / (a.Hq / a.Hkv);
   const int bhk = b * a.Hkv + hk;
@@ -706,7 +729,7 @@ __global__ __launch_bounds__(256) void debug_qk_kernel(DebugQKArgs a) {
 template <int D, bool FP8, bool CAUSAL, typename T>
 static hipError_t launch_attn_t(const AttnArgs& a, hipStream_t st) {
   const int n_qp = (a.Nq + 2 * kBq - 1) / (2 * kBq);
-  const int grid = n_qp * a.B * a.Hq;
+  const int grid = a.seq ? a.n_owner * a.Hq : n_qp * a.B * a.Hq;   // packed: the work list per head
   if (a.fine)
     hipLaunchKernelGGL((attn_fwd_fine_kernel<D, FP8, CAUSAL, T>), dim3(grid), dim3(64 * kWaves), 0, st, a);
   else

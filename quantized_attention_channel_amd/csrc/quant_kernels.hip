@@ -137,8 +137,9 @@ __global__ __launch_bounds__(D) void channel_finalize_kernel(
 // 64 lanes, one LDS exchange between waves above).
 // Packed batches (seq set): b is the sequence, its tokens are the range given
 // by the span's query (side 0) or key (side 1) pair, codes go to
-// [H][total][D], and nblk is the per-sequence scale stride (blocks past the
-// sequence get scale 0).
+// [H][total][D], and nblk is the per-sequence scale stride. Work-groups past
+// the sequence's end leave at once: the attention kernel reads a Q scale only
+// for rows that exist and a K scale past the keys only for masked scores.
 template <typename T, int D, int BLK, bool SMOOTH>
 __global__ __launch_bounds__(256) void quant_int8_kernel(
     const uint16_t* __restrict__ x, TensorGeom geo, int H, int N, int nblk,
@@ -162,6 +163,7 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(
   if (seq) {
     const int32_t* sp = &seq[b].q0 + 2 * side;   // (q0, nq) or (k0, nk)
     N = sp[1];
+    if (t0 >= N) return;                          // past this sequence (its scale slots are never read)
     base += (int64_t)sp[0] * geo.tok_stride;
     out = codes + ((int64_t)h * total + sp[0]) * D + col;
   }
@@ -324,24 +326,33 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(
 }
 
 // Per-sequence spans of a packed batch from the caller's cu_seqlens (B + 1
-// non-decreasing offsets each). One work-group walks the sequences 256 at a
-// time with an LDS prefix sum for the padded V^T column starts. Every range is
-// clamped into the packed tensors and the longest-sequence bounds, and a
-// sequence whose padded keys would pass n_pad (possible only for a malformed
-// table) loses its keys, so no later kernel can index out of bounds.
+// non-decreasing offsets each), and the attention work list: entry i of
+// qp_owner names the sequence of the i-th query pair (256 queries), the pairs
+// of sequence b being entries [qp0, qp0 + ceil(nq/256)), -1 after the last.
+// One work-group walks the sequences 256 at a time with LDS prefix sums for
+// the padded V^T column starts and the work-list starts. Every range is
+// clamped into the packed tensors and the longest-sequence bounds; a sequence
+// whose padded keys would pass n_pad, or whose query pairs would pass the
+// work list (both possible only for a malformed table), loses its keys or the
+// pairs past the end, so no later kernel can index out of bounds.
 __global__ __launch_bounds__(256) void varlen_plan_kernel(const int32_t* __restrict__ cu_q,
                                                           const int32_t* __restrict__ cu_k, int B, int total_q,
                                                           int total_k, int max_q, int max_k, int n_pad,
-                                                          SeqSpan* __restrict__ out) {
+                                                          SeqSpan* __restrict__ out, int32_t* __restrict__ qp_owner,
+                                                          int n_owner) {
   __shared__ int part[256];          // <= 256 * 2^20: fits
-  __shared__ int64_t carry;          // a malformed table can pass 2^31
+  __shared__ int partq[256];
+  __shared__ int64_t carry, carryq;  // a malformed table can pass 2^31
   const int tid = threadIdx.x;
-  if (tid == 0) carry = 0;
+  if (tid == 0) {
+    carry = 0;
+    carryq = 0;
+  }
   __syncthreads();
   for (int b0 = 0; b0 < B; b0 += 256) {
     const int b = b0 + tid;
     SeqSpan sp{};
-    int padded = 0;
+    int padded = 0, pairs = 0;
     if (b < B) {
       const int q0 = min(max(cu_q[b], 0), total_q), q1 = min(max(cu_q[b + 1], q0), total_q);
       const int k0 = min(max(cu_k[b], 0), total_k), k1 = min(max(cu_k[b + 1], k0), total_k);
@@ -350,13 +361,17 @@ __global__ __launch_bounds__(256) void varlen_plan_kernel(const int32_t* __restr
       sp.k0 = k0;
       sp.nk = min(k1 - k0, max_k);
       padded = (sp.nk + kVPad - 1) / kVPad * kVPad;
+      pairs = (sp.nq + 255) / 256;
     }
     part[tid] = padded;
+    partq[tid] = pairs;
     __syncthreads();
-    for (int o = 1; o < 256; o <<= 1) {          // inclusive scan
+    for (int o = 1; o < 256; o <<= 1) {          // inclusive scans
       const int add = tid >= o ? part[tid - o] : 0;
+      const int addq = tid >= o ? partq[tid - o] : 0;
       __syncthreads();
       part[tid] += add;
+      partq[tid] += addq;
       __syncthreads();
     }
     if (b < B) {
@@ -367,19 +382,26 @@ __global__ __launch_bounds__(256) void varlen_plan_kernel(const int32_t* __restr
       } else {
         sp.kp0 = (int)kp0;
       }
+      const int64_t qp0 = carryq + partq[tid] - pairs;
+      sp.qp0 = (int)min(qp0, (int64_t)n_owner);
+      for (int64_t i = qp0; i < qp0 + pairs && i < n_owner; ++i) qp_owner[i] = b;
       out[b] = sp;
     }
     __syncthreads();
-    if (tid == 0) carry += part[255];
+    if (tid == 0) {
+      carry += part[255];
+      carryq += partq[255];
+    }
     __syncthreads();
   }
+  for (int64_t i = carryq + tid; i < n_owner; i += 256) qp_owner[i] = -1;
 }
 
 // ---------------------------------------------------------------- host launchers
 hipError_t launch_varlen_plan(const int32_t* cu_q, const int32_t* cu_k, int B, int total_q, int total_k, int max_q,
-                              int max_k, int n_pad, SeqSpan* out, hipStream_t st) {
+                              int max_k, int n_pad, SeqSpan* out, int32_t* qp_owner, int n_owner, hipStream_t st) {
   hipLaunchKernelGGL(varlen_plan_kernel, dim3(1), dim3(256), 0, st, cu_q, cu_k, B, total_q, total_k, max_q, max_k,
-                     n_pad, out);
+                     n_pad, out, qp_owner, n_owner);
   return hipGetLastError();
 }
 

@@ -146,6 +146,8 @@ sage_status check_varlen_shape(const sage_varlen_shape* s, VDims* d) {
   if (d->B * d->Hq > (int64_t(1) << 24)) return SAGE_ERR_INVALID_ARGUMENT;
   // padded V^T columns: every sequence's keys rounded up to the tile fit here
   if (d->total_k + (sage::kVPad - 1) * d->B > (int64_t(1) << 24) - sage::kVPad) return SAGE_ERR_INVALID_ARGUMENT;
+  // attention grid: the query-pair work list for every query head
+  if (sage::varlen_qpair_bound(d->total_q, d->B) * d->Hq > (int64_t(1) << 30)) return SAGE_ERR_INVALID_ARGUMENT;
   d->n_pad = round_up(d->total_k + (sage::kVPad - 1) * d->B, sage::kVPad);
   if (d->n_pad == 0) d->n_pad = sage::kVPad;
   return SAGE_OK;
@@ -155,7 +157,7 @@ sage_status check_varlen_shape(const sage_varlen_shape* s, VDims* d) {
 // and partials with per-sequence strides from the maximum lengths, V^T rows
 // [Hkv][D][n_pad].
 struct VLayout {
-  size_t spans, q_codes, q_scale, k_codes, k_scale, k_mean, vt, v_scale, v_inv, ksum, vmax, total;
+  size_t spans, qp_owner, q_codes, q_scale, k_codes, k_scale, k_mean, vt, v_scale, v_inv, ksum, vmax, total;
 };
 
 VLayout varlen_layout_for(const VDims& d, bool fp8) {
@@ -169,6 +171,7 @@ VLayout varlen_layout_for(const VDims& d, bool fp8) {
   const int64_t nbq = std::max<int64_t>(1, cdiv(d.max_q, d.blk_q)), nbk = std::max<int64_t>(1, cdiv(d.max_k, d.blk_k));
   const int64_t chunks = cdiv(d.max_k, kStatChunk);
   L.spans = take(size_t(d.B) * sizeof(sage::SeqSpan));
+  L.qp_owner = take(size_t(sage::varlen_qpair_bound(d.total_q, d.B)) * 4);
   L.q_codes = take(size_t(d.Hq * d.total_q * d.D));
   L.q_scale = take(size_t(d.B * d.Hq * nbq) * 4);
   L.k_codes = take(size_t(d.Hkv * d.total_k * d.D));
@@ -396,8 +399,10 @@ sage_status sage_attn_fwd_varlen(const sage_varlen_shape* s, const void* q, cons
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
   sage::SeqSpan* spans = at<sage::SeqSpan>(workspace, L.spans);
+  int32_t* qp_owner = at<int32_t>(workspace, L.qp_owner);
+  const int n_owner = int(sage::varlen_qpair_bound(d.total_q, d.B));
   hipError_t e = sage::launch_varlen_plan(cu_seqlens_q, cu_seqlens_k, int(d.B), int(d.total_q), int(d.total_k),
-                                          int(d.max_q), int(d.max_k), int(d.n_pad), spans, hs);
+                                          int(d.max_q), int(d.max_k), int(d.n_pad), spans, qp_owner, n_owner, hs);
   if (e != hipSuccess) return SAGE_ERR_HIP;
 
   sage::QuantQKArgs qa{};
@@ -460,6 +465,8 @@ sage_status sage_attn_fwd_varlen(const sage_varlen_shape* s, const void* q, cons
   aa.seq = spans;
   aa.total_q = int(d.total_q);
   aa.total_k = int(d.total_k);
+  aa.qp_owner = qp_owner;
+  aa.n_owner = n_owner;
   return from_hip(sage::launch_attn(aa, hs));
 }
 

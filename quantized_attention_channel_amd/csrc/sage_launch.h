@@ -20,8 +20,13 @@ struct TensorGeom {
 // the caller's cu_seqlens, clamped so that every range lies inside the packed
 // tensors and the padded V^T rows.
 struct SeqSpan {
-  int32_t q0, nq, k0, nk, kp0, reserved[3];
+  int32_t q0, nq, k0, nk, kp0;
+  int32_t qp0;          // index of its first query pair (256 queries) in the packed work list
+  int32_t reserved[2];
 };
+
+// The packed work list holds at most total_q / 256 + B query pairs.
+inline int64_t varlen_qpair_bound(int64_t total_q, int64_t B) { return total_q / 256 + B; }
 
 // Dense batches leave `seq` null. Packed batches set it, and then B is the
 // sequence count, Nq/Nk the maximum sequence lengths (they size the grids and
@@ -74,6 +79,8 @@ struct AttnArgs {
   bool fine;            // per-thread scales: q_scale per query, k_scale per 16 keys
   const SeqSpan* seq;   // packed batches only
   int total_q, total_k;
+  const int32_t* qp_owner;  // packed batches: sequence of each work-list query pair, -1 past the end
+  int n_owner;              // entries of qp_owner
 };
 
 struct DebugQKArgs {
@@ -84,7 +91,8 @@ struct DebugQKArgs {
 };
 
 hipError_t launch_varlen_plan(const int32_t* cu_q, const int32_t* cu_k, int B, int total_q, int total_k,
-                              int max_q, int max_k, int n_pad, SeqSpan* out, hipStream_t st);
+                              int max_q, int max_k, int n_pad, SeqSpan* out, int32_t* qp_owner, int n_owner,
+                              hipStream_t st);
 hipError_t launch_quant_qk(const QuantQKArgs& a, hipStream_t st);
 hipError_t launch_quant_v(const QuantVArgs& a, hipStream_t st);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);

@@ -248,21 +248,31 @@ def test_attn_fwd_varlen_validation(case, kw, want):
     assert _vattn(**kw) == want, case
 
 
-def _plan_model(cq, ck, total_q, total_k, max_q, max_k, n_pad):
-    """The span rules of the plan kernel: clamp, then pack the padded keys."""
-    spans, carry = [], 0
+def _plan_model(cq, ck, total_q, total_k, max_q, max_k, n_pad, owner=None):
+    """The span rules of the plan kernel: clamp, pack the padded keys, and list
+    each sequence's query pairs (256 queries) in a work list of bounded size."""
+    n_owner = total_q // 256 + (len(cq) - 1)
+    spans, carry, carryq = [], 0, 0
+    table = [None] * n_owner
     for b in range(len(cq) - 1):
         q0 = min(max(cq[b], 0), total_q)
         q1 = min(max(cq[b + 1], q0), total_q)
         k0 = min(max(ck[b], 0), total_k)
         k1 = min(max(ck[b + 1], k0), total_k)
         nq, nk = min(q1 - q0, max_q), min(k1 - k0, max_k)
-        padded = -(-nk // 128) * 128
-        kp0 = carry
+        padded, pairs = -(-nk // 128) * 128, -(-nq // 256)
+        kp0, qp0 = carry, carryq
         carry += padded
+        carryq += pairs
         if kp0 + padded > n_pad:
             nk, kp0 = 0, 0
-        spans.append((q0, nq, k0, nk, kp0))
+        for i in range(qp0, min(qp0 + pairs, n_owner)):
+            table[i] = b
+        spans.append((q0, nq, k0, nk, kp0, min(qp0, n_owner)))
+    for i in range(carryq, n_owner):
+        table[i] = -1
+    if owner is not None:
+        owner.extend(table)
     return spans
 
 
@@ -281,13 +291,24 @@ def test_varlen_plan_clamps_every_span_into_bounds():
             cq = rng.integers(-100, total_q + 200, B + 1).tolist()
             ck = rng.integers(-100, total_k + 200, B + 1).tolist()
         padded_cols = set()
-        for q0, nq, k0, nk, kp0 in _plan_model(cq, ck, total_q, total_k, max_q, max_k, n_pad):
+        owner = []
+        spans = _plan_model(cq, ck, total_q, total_k, max_q, max_k, n_pad, owner)
+        for q0, nq, k0, nk, kp0, qp0 in spans:
             assert 0 <= q0 and q0 + nq <= total_q and 0 <= nq <= max_q
             assert 0 <= k0 and k0 + nk <= total_k and 0 <= nk <= max_k
             assert 0 <= kp0 and kp0 + -(-nk // 128) * 128 <= n_pad
             cols = set(range(kp0, kp0 + -(-nk // 128) * 128))
             assert not cols & padded_cols                # V^T column slots never overlap
             padded_cols |= cols
-        if trial % 3 == 0 and max(np.diff(ck)) <= max_k:  # well-formed: nothing is dropped
-            spans = _plan_model(cq, ck, total_q, total_k, max_q, max_k, n_pad)
+        # every work-list entry is filled; an entry names a sequence whose
+        # pair index (entry - qp0) lies inside that sequence's pairs
+        assert all(e is not None for e in owner)
+        for i, b in enumerate(owner):
+            if b >= 0:
+                q0, nq, _, _, _, qp0 = spans[b]
+                assert 0 <= i - qp0 < -(-nq // 256)
+        if trial % 3 == 0 and max(np.diff(ck)) <= max_k and max(np.diff(cq)) <= max_q:
+            # well-formed: nothing is dropped, every query pair is listed once
             assert [s[3] for s in spans] == np.diff(ck).tolist()
+            listed = sorted((b, i - spans[b][5]) for i, b in enumerate(owner) if b >= 0)
+            assert listed == [(b, p) for b in range(B) for p in range(-(-(cq[b + 1] - cq[b]) // 256))]
