@@ -141,3 +141,30 @@ def test_varlen_serving_mix_full_size():
         c, r, ce = cos(g, ref), rel_l1(g, ref), cos(g, ex)
         say(f"   seq {b} (len {q1 - q0}): cos={c:.7f} rel_l1={r:.2e} cos_exact={ce:.6f}")
         assert c >= COS_ORACLE and r <= RL1_ORACLE and ce >= COS_EXACT
+
+
+def test_varlen_longest_sequence():
+    """A packed batch whose longest sequence is the limit (2^20 tokens) between
+    two short ones: spans, packed offsets, padded V^T columns and the work list
+    at their largest, one query head (the plain round-robin order). Rows at both
+    ends and in the middle of the long sequence, and every row of a short one,
+    against the oracle."""
+    n = 1 << 20
+    w = W.VarlenWorkload("longest", (300, n, 77), (300, n, 77), Hq=1, Hkv=1, d=128, dtype="fp16", causal=True,
+                         pv="fp8")
+    say("varlen longest sequence", n)
+    q, k, v, cq, ck = W.generate_varlen(w)
+    got = _run_gpu(w, "per_block", q, k, v, cq, ck)
+    assert np.isfinite(got).all()
+    qn, kn, vn = (t.float().numpy() for t in (q, k, v))
+    for b, rows in ((1, np.array([0, 1, 127, 128, n // 2 + 77, n - 129, n - 1])), (2, np.arange(77))):
+        q0, q1, k0, k1 = int(cq[b]), int(cq[b + 1]), int(ck[b]), int(ck[b + 1])
+        ref = sage_ref.sage_attention(qn[None, q0:q1], kn[None, k0:k1], vn[None, k0:k1], dtype=w.dtype,
+                                      is_causal=True, sm_scale=w.sm_scale, pv=w.pv, layout="NHD", rows=rows)
+        ex = exact.exact_attention(qn[None, q0:q1].transpose(0, 2, 1, 3), kn[None, k0:k1].transpose(0, 2, 1, 3),
+                                   vn[None, k0:k1].transpose(0, 2, 1, 3), is_causal=True, sm_scale=w.sm_scale,
+                                   rows=rows)
+        g = got[q0:q1][rows].transpose(1, 0, 2)[None]
+        c, r, ce = cos(g, ref), rel_l1(g, ref), cos(g, ex)
+        say(f"   seq {b}: cos={c:.7f} rel_l1={r:.2e} cos_exact={ce:.6f}")
+        assert c >= COS_ORACLE and r <= RL1_ORACLE and ce >= COS_EXACT
