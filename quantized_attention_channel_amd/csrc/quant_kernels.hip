@@ -140,21 +140,30 @@ __global__ __launch_bounds__(D) void channel_finalize_kernel(
 // [H][total][D], and nblk is the per-sequence scale stride. Work-groups past
 // the sequence's end leave at once: the attention kernel reads a Q scale only
 // for rows that exist and a K scale past the keys only for masked scores.
+// Threads per work-group: 512 for blocks of at least 2048 chunks (128 tokens
+// at d = 128), so that each thread holds 4 chunks instead of 8 and the kernel
+// keeps 8 waves per SIMD; 256 otherwise.
+template <int D, int BLK>
+struct QuantThreads {
+  static constexpr int value = BLK * (D / 8) >= 2048 ? 512 : 256;
+};
+
 template <typename T, int D, int BLK, bool SMOOTH>
-__global__ __launch_bounds__(256) void quant_int8_kernel(
+__global__ __launch_bounds__((QuantThreads<D, BLK>::value)) void quant_int8_kernel(
     const uint16_t* __restrict__ x, TensorGeom geo, int H, int N, int nblk,
     const float* __restrict__ mean, int8_t* __restrict__ codes, float* __restrict__ scale,
     const SeqSpan* __restrict__ seq, int side, int total) {
+  constexpr int NT = QuantThreads<D, BLK>::value;
   constexpr int TPR = D / 8;
   constexpr int G = BLK * TPR;                   // chunks per block
-  constexpr bool WHOLE = G >= 256;               // one block per work-group
+  constexpr bool WHOLE = G >= NT;                // one block per work-group
   constexpr int TOKS = WHOLE ? BLK : 64;         // token rows per work-group
-  constexpr int ITER = TOKS * TPR / 256;         // 16-byte chunks per thread
-  static_assert(ITER * 256 == TOKS * TPR, "token rows must tile the work-group");
-  static_assert(WHOLE ? G % 256 == 0 : 256 % G == 0, "blocks must tile the passes");
-  __shared__ float red[4];
+  constexpr int ITER = TOKS * TPR / NT;          // 16-byte chunks per thread
+  static_assert(ITER * NT == TOKS * TPR, "token rows must tile the work-group");
+  static_assert(WHOLE ? G % NT == 0 : NT % G == 0, "blocks must tile the passes");
+  __shared__ float red[NT / 64];
   const int tid = threadIdx.x;
-  const int col = (tid % TPR) * 8;        // 256 % TPR == 0: fixed per thread
+  const int col = (tid % TPR) * 8;        // NT % TPR == 0: fixed per thread
   const int bh = blockIdx.y;
   const int b = bh / H, h = bh % H;
   const int t0 = blockIdx.x * TOKS;
@@ -176,7 +185,7 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(
   float amax[ITER];
 #pragma unroll
   for (int it = 0; it < ITER; ++it) {
-    const int t = t0 + (it * 256 + tid) / TPR;
+    const int t = t0 + (it * NT + tid) / TPR;
     amax[it] = 0.0f;
     if (t < N) {
       i32x4 raw = *reinterpret_cast<const i32x4*>(x + base + (int64_t)t * geo.tok_stride);
@@ -201,7 +210,9 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(
     a = wave_max(a);
     if ((tid & 63) == 0) red[tid >> 6] = a;
     __syncthreads();
-    a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    a = red[0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) a = fmaxf(a, red[w]);
     if (tid == 0) scale[(int64_t)bh * nblk + blockIdx.x] = a / 127.0f;
 #pragma unroll
     for (int it = 0; it < ITER; ++it) inv[it] = a > 0.0f ? 127.0f / a : 0.0f;
@@ -220,7 +231,7 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(
         for (int w = 0; w < G / 64; ++w) a = fmaxf(a, red[w0 + w]);
         __syncthreads();                 // red is rewritten by the next pass
       }
-      const int blk = (t0 + (it * 256 + tid) / TPR) / BLK;
+      const int blk = (t0 + (it * NT + tid) / TPR) / BLK;
       if (tid % G == 0 && blk < nblk) scale[(int64_t)bh * nblk + blk] = a / 127.0f;
       inv[it] = a > 0.0f ? 127.0f / a : 0.0f;
     }
@@ -228,7 +239,7 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(
 
 #pragma unroll
   for (int it = 0; it < ITER; ++it) {
-    const int t = t0 + (it * 256 + tid) / TPR;
+    const int t = t0 + (it * NT + tid) / TPR;
     if (t < N) {
       uint32_t w[2] = {0u, 0u};
 #pragma unroll
@@ -248,10 +259,11 @@ template <typename T, int D, int BLK, bool SMOOTH>
 static void launch_quant_int8(const void* x, TensorGeom geo, int BH, int H, int N, const float* mean,
                               int8_t* codes, float* scale, const SeqSpan* seq, int side, int total,
                               hipStream_t st) {
-  constexpr int TOKS = BLK * (D / 8) >= 256 ? BLK : 64;
+  constexpr int NT = QuantThreads<D, BLK>::value;
+  constexpr int TOKS = BLK * (D / 8) >= NT ? BLK : 64;
   const int nblk = (N + BLK - 1) / BLK;
   const int wgs = (N + TOKS - 1) / TOKS;
-  hipLaunchKernelGGL((quant_int8_kernel<T, D, BLK, SMOOTH>), dim3(wgs, BH), dim3(256), 0, st,
+  hipLaunchKernelGGL((quant_int8_kernel<T, D, BLK, SMOOTH>), dim3(wgs, BH), dim3(NT), 0, st,
                      (const uint16_t*)x, geo, H, N, nblk, mean, codes, scale, seq, side, total);
 }
 
