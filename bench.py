@@ -206,6 +206,48 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
 
 
+def copy_bandwidth() -> float:
+    """Measured device copy rate in GB/s (bytes read plus bytes written per
+    second) over a 1 GiB buffer: the practical ceiling for the HBM-bound
+    quantisation kernels."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(5):
+        dst.copy_(src)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / 5
+    del src, dst
+    return 2.0 * n / (ms * 1e-3) / 1e9
+
+
+def host_info():
+    """CPU model and the BLAS behind NumPy, for the CPU baseline record."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [f"{i.get('internal_api')} {i.get('version')}" for i in threadpool_info() if i.get("user_api") == "blas"]
+        blas = ", ".join(libs) or blas
+    except Exception:  # noqa: BLE001
+        pass
+    return {"cpu_model": model, "affinity_cpus": len(os.sched_getaffinity(0)), "numpy_blas": blas}
+
+
 def measure(w: W.Workload, pv: str, steps: int, warmup: int, qk_gran: str = "per_block"):
     q, k, v = W.generate(w, device="cuda")
     plan = Plan(w, pv, q, k, v, qk_gran)
@@ -281,6 +323,7 @@ def main():
     pv = args.pv or w.pv
 
     r = measure(w, pv, args.steps, args.warmup, args.qk_gran)
+    copy_gbps = copy_bandwidth()
     traffic, counters_sha = counters_traffic()
     roof = {"bound": "mfma", "achieved": round(r["attn_tops"], 2), "peak": PEAK_TOPS, "unit": "TFLOP/s",
             "frac": round(r["attn_tops"] / PEAK_TOPS, 4), "traffic": traffic,
@@ -299,7 +342,8 @@ def main():
         "roofline": roof,
         "breakdown_ms": {"gpu_step": round(r["gpu_ms"], 4), "quant": round(r["quant_ms"], 4),
                          "attention": round(r["attn_ms"], 4), "sage_attn_fwd_single_call": round(r["fused_ms"], 4)},
-        "quant_hbm": {"algorithmic_bytes": r["quant_bytes"],
+        "quant_hbm": {"algorithmic_bytes": r["quant_bytes"], "copy_GBps": round(copy_gbps, 1),
+                      "frac_of_copy": round(r["quant_bytes"] / (r["quant_ms"] * 1e-3) / 1e9 / copy_gbps, 4),
                       "GBps": round(r["quant_bytes"] / (r["quant_ms"] * 1e-3) / 1e9, 1),
                       "frac_of_8TBps": round(r["quant_bytes"] / (r["quant_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
     }
@@ -314,6 +358,7 @@ def main():
                            "varlen": measure_varlen(W.VARLEN_PREFILL, args.steps, args.warmup)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, pv, args.cpu_rows, args.qk_gran)
+        out["cpu_baseline"].update(host_info())
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
