@@ -536,9 +536,13 @@ __device__ __forceinline__ void attn_fwd_body(AttnArgs a) {
   };
   // X(t): PV(t-1) with V in buffer 1-P, then QK^T(t) with K in buffer P.
   auto x_bufs = [&](const uint8_t* v_prv, const int8_t* k_cur, bool do_pv, bool do_qk) __attribute__((always_inline)) {
+    // The matrix wave outranks the softmax wave while it issues PV, whose
+    // level-2 merge must not wait behind the softmax's exps; its QK^T part
+    // competes at equal priority (measured: +0.5%; PV at equal priority: -6%).
     __builtin_amdgcn_s_setprio(1);
     if (do_pv) pv_phase<D, FP8, T>(v_prv, lane, pt, st);
     __builtin_amdgcn_sched_barrier(0);         // P and the V operands die before the K operands load
+    __builtin_amdgcn_s_setprio(0);
     if (do_qk) qk_tile<D>(k_cur, qreg, lane, s, qk_init);
   };
   auto x_phase = [&](auto par, int t, bool do_pv, bool do_qk) __attribute__((always_inline)) {
