@@ -9,6 +9,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -312,3 +313,12 @@ def test_varlen_plan_clamps_every_span_into_bounds():
             assert [s[3] for s in spans] == np.diff(ck).tolist()
             listed = sorted((b, i - spans[b][5]) for i, b in enumerate(owner) if b >= 0)
             assert listed == [(b, p) for b in range(B) for p in range(-(-(cq[b + 1] - cq[b]) // 256))]
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """No fallback: importing the binding with the library missing raises."""
+    env = dict(os.environ, SAGE_LIB_PATH=str(tmp_path / "missing" / "libsage.so"))
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", "import quantized_attention_channel_amd"], cwd=root, env=env,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0 and "ImportError" in r.stderr and "not built" in r.stderr
