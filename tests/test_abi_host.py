@@ -322,3 +322,42 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
     r = subprocess.run([sys.executable, "-c", "import quantized_attention_channel_amd"], cwd=root, env=env,
                        capture_output=True, text=True, timeout=300)
     assert r.returncode != 0 and "ImportError" in r.stderr and "not built" in r.stderr
+
+
+C_USER = r"""
+#include <stdio.h>
+#include "sage.h"
+int main(void) {
+  sage_shape s = {2, 4, 2, 300, 300, 128, SAGE_LAYOUT_HND, SAGE_DTYPE_F16, SAGE_QK_PER_BLOCK};
+  sage_varlen_shape vs = {3, 4, 2, 128, 500, 700, 300, 400, SAGE_DTYPE_BF16, SAGE_QK_PER_THREAD};
+  int32_t bq = 0, bk = 0, bkv = 0;
+  if (sage_block_sizes(128, SAGE_QK_PER_THREAD, &bq, &bk, &bkv) != SAGE_OK) return 1;
+  if (sage_workspace_bytes(&s, SAGE_PV_FP8_E4M3) == 0 || sage_varlen_workspace_bytes(&vs, SAGE_PV_FP16) == 0) return 2;
+  /* host validation runs before any HIP call: null tensors are rejected without a GPU */
+  if (sage_attn_fwd(&s, 0, 0, 0, 0, 0, 0.1f, SAGE_PV_FP8_E4M3, 0, 0, 0) != SAGE_ERR_INVALID_ARGUMENT) return 3;
+  printf("%d %d %d %d\n", bq, bk, bkv, (int)sizeof(sage_varlen_shape));
+  return 0;
+}
+"""
+
+
+def test_header_is_plain_c_and_the_library_links_from_c(tmp_path):
+    """The boundary is a C ABI: the header compiles as strict C99 and a C program
+    links against libsage.so and calls its host-side entry points."""
+    import shutil
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    pkg = os.path.join(root, "quantized_attention_channel_amd")
+    src = tmp_path / "use_sage.c"
+    src.write_text(C_USER)
+    exe = tmp_path / "use_sage"
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(root, "include"),
+                        str(src), "-L", pkg, "-lsage", f"-Wl,-rpath,{pkg}", "-o", str(exe)],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, (r.returncode, r.stderr)
+    assert r.stdout.split() == [str(sage_ref.PER_THREAD_BLK_Q), str(sage_ref.PER_THREAD_BLK_K),
+                                str(sage_ref.BKV[128]), str(10 * 4)]
