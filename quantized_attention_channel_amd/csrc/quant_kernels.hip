@@ -164,9 +164,13 @@ __global__ __launch_bounds__((QuantThreads<D, BLK>::value)) void quant_int8_kern
   __shared__ float red[NT / 64];
   const int tid = threadIdx.x;
   const int col = (tid % TPR) * 8;        // NT % TPR == 0: fixed per thread
-  const int bh = blockIdx.y;
+  // Work-groups run in reverse launch order. For K the statistics pass has just
+  // read the tensor front to back, so its tail is the part the last-level cache
+  // still holds; for Q the order makes no difference.
+  const int bx = gridDim.x - 1 - blockIdx.x;
+  const int bh = gridDim.y - 1 - blockIdx.y;
   const int b = bh / H, h = bh % H;
-  const int t0 = blockIdx.x * TOKS;
+  const int t0 = bx * TOKS;
   int64_t base = (int64_t)b * geo.batch_stride + (int64_t)h * geo.head_stride + col;
   int8_t* out = codes + (int64_t)bh * N * D + col;
   if (seq) {
@@ -213,7 +217,7 @@ __global__ __launch_bounds__((QuantThreads<D, BLK>::value)) void quant_int8_kern
     a = red[0];
 #pragma unroll
     for (int w = 1; w < NT / 64; ++w) a = fmaxf(a, red[w]);
-    if (tid == 0) scale[(int64_t)bh * nblk + blockIdx.x] = a / 127.0f;
+    if (tid == 0) scale[(int64_t)bh * nblk + bx] = a / 127.0f;
 #pragma unroll
     for (int it = 0; it < ITER; ++it) inv[it] = a > 0.0f ? 127.0f / a : 0.0f;
   } else {
@@ -281,9 +285,10 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(
   constexpr int UNITS = (64 / 4) * (D / 8);     // 4 tokens x 8 channels per unit
   __shared__ __attribute__((aligned(16))) uint8_t tile[D * ROWB];
   const int tid = threadIdx.x;
-  const int bh = blockIdx.y;
+  // reverse launch order, as in quant_int8_kernel (V's statistics pass ran just before)
+  const int bh = gridDim.y - 1 - blockIdx.y;
   const int b = bh / H, h = bh % H;
-  const int t0 = blockIdx.x * 64;
+  const int t0 = (gridDim.x - 1 - blockIdx.x) * 64;
   int64_t base = (int64_t)b * geo.batch_stride + (int64_t)h * geo.head_stride;
   int64_t dst0 = (int64_t)bh * D * n_pad;
   if (seq) {
