@@ -36,6 +36,10 @@
  *             scales always use the canonical per-head orders given below.
  * Alignment.  Tensor and code pointers must be 16-byte aligned, scale/mean
  *             pointers 4-byte aligned, workspaces 256-byte aligned.
+ * Aliasing.   No buffer a call writes (outputs, and the part of the workspace
+ *             the size query reports) may overlap another such buffer or any
+ *             buffer the call reads; that returns SAGE_ERR_INVALID_ARGUMENT.
+ *             Read-only inputs may share memory (e.g. k == v).
  * Sizes.      1 <= B, Hq, Hkv; Hq % Hkv == 0 (group-query attention: query head
  *             h uses kv head h / (Hq/Hkv)); head_dim in {64, 128}; 0 <= Nq, Nk
  *             <= 2^20 (Nq == 0 or B == 0 is a valid no-op; Nk == 0 with Nq > 0

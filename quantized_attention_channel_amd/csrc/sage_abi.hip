@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <initializer_list>
 
 #include "sage.h"
 #include "sage_device.h"
@@ -76,7 +77,27 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   if (!a || !b || na == 0 || nb == 0) return false;
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
-  return x < y + nb && y < x + na;
+  const uintptr_t xe = na > UINTPTR_MAX - x ? UINTPTR_MAX : x + na;   // (saturating ends)
+  const uintptr_t ye = nb > UINTPTR_MAX - y ? UINTPTR_MAX : y + nb;
+  return x < ye && y < xe;
+}
+
+// One buffer a call touches: base and byte count (a null base or zero count is
+// skipped).
+struct Span {
+  const void* p;
+  size_t n;
+};
+
+// True if two written buffers overlap, or a written buffer overlaps a read one.
+bool aliased(std::initializer_list<Span> written, std::initializer_list<Span> read) {
+  for (auto w = written.begin(); w != written.end(); ++w) {
+    for (auto x = w + 1; x != written.end(); ++x)
+      if (overlaps(w->p, w->n, x->p, x->n)) return true;
+    for (const Span& r : read)
+      if (overlaps(w->p, w->n, r.p, r.n)) return true;
+  }
+  return false;
 }
 
 // Workspace layout (each region 256-byte aligned), shared by all entry points.
@@ -250,6 +271,15 @@ sage_status sage_quant_qk(const sage_shape* s, const void* q, const void* k, int
     if (!workspace || !aligned(workspace, 256)) return SAGE_ERR_INVALID_ARGUMENT;
     if (workspace_bytes < qk_ws_bytes(d)) return SAGE_ERR_WORKSPACE;
   }
+  {
+    const size_t nq = has_q ? size_t(d.B * d.Hq * d.Nq * d.D) : 0, nk = has_k ? size_t(d.B * d.Hkv * d.Nk * d.D) : 0;
+    const size_t sq = has_q ? size_t(d.B * d.Hq * cdiv(d.Nq, d.blk_q)) * 4 : 0;
+    const size_t sk = has_k ? size_t(d.B * d.Hkv * cdiv(d.Nk, d.blk_k)) * 4 : 0;
+    const size_t mk = has_k ? size_t(d.B * d.Hkv * d.D) * 4 : 0, wk = has_k ? qk_ws_bytes(d) : 0;
+    if (aliased({{q_codes, nq}, {q_scale, sq}, {k_codes, nk}, {k_scale, sk}, {k_mean, mk}, {workspace, wk}},
+                {{q, nq * 2}, {k, nk * 2}}))
+      return SAGE_ERR_INVALID_ARGUMENT;
+  }
   sage::QuantQKArgs a{};
   a.q = q;
   a.k = k;
@@ -277,6 +307,10 @@ sage_status sage_quant_v(const sage_shape* s, const void* v, uint8_t* v_codes, f
   if (!aligned(v, 16) || !aligned(v_codes, 16) || !aligned(v_scale, 4) || !aligned(workspace, 256))
     return SAGE_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < v_ws_bytes(d)) return SAGE_ERR_WORKSPACE;
+  if (aliased({{v_codes, size_t(d.B * d.Hkv * d.D * round_up(d.Nk, sage::kVPad))},
+               {v_scale, size_t(d.B * d.Hkv * d.D) * 4}, {workspace, v_ws_bytes(d)}},
+              {{v, size_t(d.B * d.Hkv * d.Nk * d.D) * 2}}))
+    return SAGE_ERR_INVALID_ARGUMENT;
   sage::QuantVArgs a{};
   a.v = v;
   a.vgeo = geom(d, d.Hkv, d.Nk);
@@ -310,8 +344,7 @@ sage_status sage_attn_fwd(const sage_shape* s, const void* q, const void* k, con
   const Layout L = layout_for(d, fp8);
   if (workspace_bytes < L.total) return SAGE_ERR_WORKSPACE;
   const size_t qbytes = size_t(d.B * d.Hq * d.Nq * d.D) * 2, kvbytes = size_t(d.B * d.Hkv * d.Nk * d.D) * 2;
-  if (overlaps(o, qbytes, q, qbytes) || overlaps(o, qbytes, k, kvbytes) || overlaps(o, qbytes, v, kvbytes) ||
-      overlaps(o, qbytes, workspace, L.total))
+  if (aliased({{o, qbytes}, {workspace, L.total}}, {{q, qbytes}, {k, kvbytes}, {v, kvbytes}}))
     return SAGE_ERR_INVALID_ARGUMENT;
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -393,8 +426,9 @@ sage_status sage_attn_fwd_varlen(const sage_varlen_shape* s, const void* q, cons
   const VLayout L = varlen_layout_for(d, fp8);
   if (workspace_bytes < L.total) return SAGE_ERR_WORKSPACE;
   const size_t qbytes = size_t(d.total_q * d.Hq * d.D) * 2, kvbytes = size_t(d.total_k * d.Hkv * d.D) * 2;
-  if (overlaps(o, qbytes, q, qbytes) || overlaps(o, qbytes, k, kvbytes) || overlaps(o, qbytes, v, kvbytes) ||
-      overlaps(o, qbytes, workspace, L.total))
+  const size_t cubytes = size_t(d.B + 1) * 4;
+  if (aliased({{o, qbytes}, {workspace, L.total}},
+              {{q, qbytes}, {k, kvbytes}, {v, kvbytes}, {cu_seqlens_q, cubytes}, {cu_seqlens_k, cubytes}}))
     return SAGE_ERR_INVALID_ARGUMENT;
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -476,6 +510,9 @@ sage_status sage_transpose_v(const sage_shape* s, const void* v, void* v_t, void
   if (st != SAGE_OK) return st;
   if (d.B == 0 || d.Nk == 0) return SAGE_OK;
   if (!v || !v_t || !aligned(v, 16) || !aligned(v_t, 16)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (aliased({{v_t, size_t(d.B * d.Hkv * d.D * round_up(d.Nk, sage::kVPad)) * 2}},
+              {{v, size_t(d.B * d.Hkv * d.Nk * d.D) * 2}}))
+    return SAGE_ERR_INVALID_ARGUMENT;
   sage::QuantVArgs a{};
   a.v = v;
   a.vgeo = geom(d, d.Hkv, d.Nk);
@@ -508,9 +545,11 @@ sage_status sage_attn_fwd_codes(const sage_shape* s, const int8_t* q_codes, cons
     return SAGE_ERR_INVALID_ARGUMENT;
   const size_t obytes = size_t(d.B * d.Hq * d.Nq * d.D) * 2;
   const int64_t npad = round_up(d.Nk, sage::kVPad);
-  if (overlaps(o, obytes, q_codes, size_t(d.B * d.Hq * d.Nq * d.D)) ||
-      overlaps(o, obytes, k_codes, size_t(d.B * d.Hkv * d.Nk * d.D)) ||
-      overlaps(o, obytes, v_prepared, size_t(d.B * d.Hkv * d.D * npad) * (fp8 ? 1 : 2)))
+  if (aliased({{o, obytes}},
+              {{q_codes, size_t(d.B * d.Hq * d.Nq * d.D)}, {q_scale, size_t(d.B * d.Hq * cdiv(d.Nq, d.blk_q)) * 4},
+               {k_codes, size_t(d.B * d.Hkv * d.Nk * d.D)}, {k_scale, size_t(d.B * d.Hkv * cdiv(d.Nk, d.blk_k)) * 4},
+               {v_prepared, size_t(d.B * d.Hkv * d.D * npad) * (fp8 ? 1 : 2)},
+               {fp8 ? v_scale : nullptr, size_t(d.B * d.Hkv * d.D) * 4}}))
     return SAGE_ERR_INVALID_ARGUMENT;
   sage::AttnArgs aa{};
   aa.q8 = q_codes;
@@ -541,6 +580,13 @@ sage_status sage_debug_qk_i32(const sage_shape* s, const int8_t* q_codes, const 
   if (d.B == 0 || d.Nq == 0 || d.Nk == 0) return SAGE_OK;
   if (!q_codes || !k_codes || !s_out) return SAGE_ERR_INVALID_ARGUMENT;
   if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(s_out, 4)) return SAGE_ERR_INVALID_ARGUMENT;
+  {
+    // s_out holds B*Hq*Nq*Nk int32 (saturated: the product can pass 2^64 bytes)
+    const int64_t rows = d.B * d.Hq * d.Nq;
+    const size_t sbytes = rows > int64_t(SIZE_MAX / 4) / d.Nk ? SIZE_MAX : size_t(rows * d.Nk) * 4;
+    if (aliased({{s_out, sbytes}}, {{q_codes, size_t(rows * d.D)}, {k_codes, size_t(d.B * d.Hkv * d.Nk * d.D)}}))
+      return SAGE_ERR_INVALID_ARGUMENT;
+  }
   sage::DebugQKArgs a{};
   a.q8 = q_codes;
   a.k8 = k_codes;

@@ -13,6 +13,7 @@ import sys
 
 import numpy as np
 import pytest
+import torch
 
 import quantized_attention_channel_amd as sage
 from oracle import sage_ref
@@ -21,6 +22,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sage.h")
 
 FAKE = 0x7F0000000000          # a 256-byte aligned address that is never dereferenced
+G = 1 << 30
+
+# The tests marked with this hand fake device addresses to entry points, and
+# every such call must be rejected on the host. Were a check missing on a
+# machine with a GPU, kernels would run on those addresses, so these tests run
+# only where no GPU is visible (device_count does not initialise the runtime).
+FAKE_ADDRESSES = pytest.mark.skipif(torch.cuda.device_count() > 0, reason="fake device addresses: CPU-only test")
 
 
 def declared_functions():
@@ -118,6 +126,7 @@ def _attn(shape, q=FAKE, k=FAKE + 2 ** 30, v=FAKE + 2 ** 31, o=FAKE + 3 * 2 ** 3
     return sage.lib.sage_attn_fwd(sp, q, k, v, o, causal, scale, pv, ws, ws_bytes, None)
 
 
+@FAKE_ADDRESSES
 @pytest.mark.parametrize("case,kw,want", [
     ("null shape", dict(shape=None), sage.SAGE_ERR_INVALID_ARGUMENT),
     ("Hq % Hkv", dict(shape=_shape(Hq=3, Hkv=2)), sage.SAGE_ERR_INVALID_ARGUMENT),
@@ -145,6 +154,8 @@ def _attn(shape, q=FAKE, k=FAKE + 2 ** 30, v=FAKE + 2 ** 31, o=FAKE + 3 * 2 ** 3
     ("small workspace", dict(shape=_shape(), ws_bytes=1024), sage.SAGE_ERR_WORKSPACE),
     ("o aliases q", dict(shape=_shape(), o=FAKE + 4096), sage.SAGE_ERR_INVALID_ARGUMENT),
     ("o aliases workspace", dict(shape=_shape(), o=FAKE + 2 ** 33 + 256), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("workspace aliases k", dict(shape=_shape(), ws=FAKE + 2 ** 30 + 256), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("workspace aliases v", dict(shape=_shape(), ws=FAKE + 2 ** 31), sage.SAGE_ERR_INVALID_ARGUMENT),
     ("no keys", dict(shape=_shape(Nk=0)), sage.SAGE_ERR_INVALID_ARGUMENT),
     ("no queries is a no-op", dict(shape=_shape(Nq=0), q=None, o=None), sage.SAGE_OK),
     ("empty batch is a no-op", dict(shape=_shape(B=0)), sage.SAGE_OK),
@@ -153,6 +164,7 @@ def test_attn_fwd_validation(case, kw, want):
     assert _attn(**kw) == want, case
 
 
+@FAKE_ADDRESSES
 def test_quant_entry_points_validate():
     s = _shape()
     sp = ctypes.byref(s)
@@ -174,6 +186,46 @@ def test_quant_entry_points_validate():
         sage.SAGE_ERR_UNSUPPORTED
     assert sage.lib.sage_debug_qk_i32(sp, None, FAKE, FAKE, None) == sage.SAGE_ERR_INVALID_ARGUMENT
     assert sage.lib.sage_debug_qk_i32(sp, FAKE + 1, FAKE, FAKE, None) == sage.SAGE_ERR_INVALID_ARGUMENT
+
+
+@FAKE_ADDRESSES
+@pytest.mark.parametrize("case,change", [
+    ("q codes on q", dict(qc=FAKE + 4096)),
+    ("k codes on k", dict(kc=FAKE + G)),
+    ("k scale inside q", dict(ks=FAKE + 600000)),
+    ("q scale on k codes", dict(qs=FAKE + 4 * G + 16)),
+    ("k mean inside the workspace", dict(km=FAKE + 8 * G + 256)),
+    ("workspace on k", dict(ws=FAKE + G)),
+])
+def test_quant_qk_rejects_aliased_writes(case, change):
+    sp = ctypes.byref(_shape())
+    a = dict(q=FAKE, k=FAKE + G, qc=FAKE + 2 * G, qs=FAKE + 3 * G, kc=FAKE + 4 * G, ks=FAKE + 5 * G, km=FAKE + 6 * G,
+             ws=FAKE + 8 * G)
+    a.update(change)
+    n = sage.lib.sage_quant_qk_workspace_bytes(sp)
+    assert sage.lib.sage_quant_qk(sp, a["q"], a["k"], a["qc"], a["qs"], a["kc"], a["ks"], a["km"], a["ws"], n,
+                                  None) == sage.SAGE_ERR_INVALID_ARGUMENT, case
+
+
+@FAKE_ADDRESSES
+def test_other_entry_points_reject_aliased_writes():
+    s = _shape()
+    sp = ctypes.byref(s)
+    bad = sage.SAGE_ERR_INVALID_ARGUMENT
+    n = sage.lib.sage_quant_v_workspace_bytes(sp)
+    v, vc, vs, ws = FAKE, FAKE + G, FAKE + 2 * G, FAKE + 3 * G
+    assert sage.lib.sage_quant_v(sp, v, v + 4096, vs, ws, n, None) == bad           # codes on v
+    assert sage.lib.sage_quant_v(sp, v, vc, ws, ws, n, None) == bad                 # scale in the workspace
+    assert sage.lib.sage_quant_v(sp, v, vc, vs, v + 2 ** 18, n, None) == bad        # workspace inside v
+    assert sage.lib.sage_transpose_v(sp, v, v + 4096, None) == bad
+    # attention from codes: o may not cover any of the codes or scales it reads
+    qc, qs, kc, ks, vp, vsc = (FAKE + i * G for i in range(6))
+    for o in (qs, ks, vsc, vp + 4096):
+        assert sage.lib.sage_attn_fwd_codes(sp, qc, qs, kc, ks, vp, vsc, o, 0, 0.1, 1, None) == bad
+    # the INT32 hook: s_out on the codes, and a product of sizes past 2^64 bytes
+    assert sage.lib.sage_debug_qk_i32(sp, FAKE, FAKE + G, FAKE + 64, None) == bad
+    huge = ctypes.byref(_shape(B=1 << 10, Hq=1 << 14, Hkv=1 << 14, Nq=1 << 20, Nk=1 << 20))
+    assert sage.lib.sage_debug_qk_i32(huge, FAKE + (1 << 44), FAKE + (1 << 45), FAKE, None) == bad
 
 
 def test_python_wrapper_rejects_unsupported_sdpa_arguments():
@@ -223,6 +275,7 @@ def _vattn(shape, q=FAKE, k=FAKE + 2 ** 30, v=FAKE + 2 ** 31, cq=FAKE + 2 ** 34,
     return sage.lib.sage_attn_fwd_varlen(sp, q, k, v, cq, ck, o, causal, scale, pv, ws, ws_bytes, None)
 
 
+@FAKE_ADDRESSES
 @pytest.mark.parametrize("case,kw,want", [
     ("null shape", dict(shape=None), sage.SAGE_ERR_INVALID_ARGUMENT),
     ("Hq % Hkv", dict(shape=_vshape(Hq=3)), sage.SAGE_ERR_INVALID_ARGUMENT),
@@ -242,6 +295,9 @@ def _vattn(shape, q=FAKE, k=FAKE + 2 ** 30, v=FAKE + 2 ** 31, cq=FAKE + 2 ** 34,
     ("misaligned v", dict(shape=_vshape(), v=FAKE + 2 ** 31 + 8), sage.SAGE_ERR_INVALID_ARGUMENT),
     ("small workspace", dict(shape=_vshape(), ws_bytes=4096), sage.SAGE_ERR_WORKSPACE),
     ("o aliases q", dict(shape=_vshape(), o=FAKE + 4096), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("workspace aliases q", dict(shape=_vshape(), ws=FAKE + 4096), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("workspace aliases cu_seqlens_q", dict(shape=_vshape(), ws=FAKE + 2 ** 34 - 256), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("o aliases cu_seqlens_k", dict(shape=_vshape(), o=FAKE + 2 ** 34 + 64), sage.SAGE_ERR_INVALID_ARGUMENT),
     ("no sequences is a no-op", dict(shape=_vshape(B=0), q=None, o=None), sage.SAGE_OK),
     ("no queries is a no-op", dict(shape=_vshape(tq=0), q=None, o=None), sage.SAGE_OK),
 ])
