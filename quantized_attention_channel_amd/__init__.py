@@ -125,6 +125,10 @@ def shape_of(q: torch.Tensor, k: torch.Tensor, layout: str, qk_gran: str = "per_
         raise ValueError(f"tensor_layout must be HND or NHD, got {layout!r}")
     if q.dtype not in DTYPES:
         raise TypeError(f"q/k/v must be float16 or bfloat16, got {q.dtype}")
+    if k.dtype != q.dtype:
+        raise TypeError("q and k must have one dtype")
+    if k.shape[0] != B or k.shape[-1] != d:
+        raise ValueError(f"q {tuple(q.shape)} and k {tuple(k.shape)} differ in batch or head_dim")
     return make_shape(B, Hq, Hkv, Nq, Nk, d, layout, q.dtype, qk_gran)
 
 
@@ -150,6 +154,39 @@ def sage_workspace_bytes(shape: SageShape, pv_dtype: str = "fp8") -> int:
 
 def _workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def _expect(t: Optional[torch.Tensor], name: str, dtype: torch.dtype, numel: int, device: torch.device):
+    """A tensor the library reads or writes as a dense buffer of `numel`
+    elements of `dtype` on `device`."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements, got {t.numel()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _out_like(q: torch.Tensor, out: Optional[torch.Tensor]) -> torch.Tensor:
+    if out is None:
+        return torch.empty_like(q)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError(f"out must have q's shape {tuple(q.shape)}, got {tuple(out.shape)}")
+    _expect(out, "out", q.dtype, q.numel(), q.device)
+    return out
+
+
+def _workspace_for(workspace: Optional[torch.Tensor], need: int, device: torch.device) -> torch.Tensor:
+    """The caller's workspace (a contiguous uint8 tensor on `device`) if it
+    holds `need` bytes, else a fresh one."""
+    if workspace is None:
+        return _workspace(need, device)
+    _expect(workspace, "workspace", torch.uint8, workspace.numel(), device)
+    return workspace if workspace.numel() >= need else _workspace(need, device)
 
 
 def _check_inputs(*ts):
@@ -212,6 +249,28 @@ def sage_attn_fwd_codes(shape: SageShape, q_codes, q_scale, k_codes, k_scale, v_
     sage_quant_v (FP8) or sage_transpose_v (FP16). Writes into ``o``."""
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(shape.head_dim)
+    if pv_dtype not in PV_DTYPES:
+        raise ValueError(f"pv_dtype must be one of {sorted(PV_DTYPES)}, got {pv_dtype!r}")
+    fp8 = PV_DTYPES[pv_dtype] == 1
+    in_dtype = {v: k for k, v in DTYPES.items()}.get(shape.dtype)
+    if in_dtype is None:
+        raise ValueError(f"shape.dtype must be one of {sorted(DTYPES.values())}, got {shape.dtype}")
+    gran = {v: k for k, v in QK_GRANS.items()}.get(shape.qk_gran)
+    if gran is None:
+        raise ValueError(f"shape.qk_gran must be one of {sorted(QK_GRANS.values())}, got {shape.qk_gran}")
+    bq, bk, _ = sage_block_sizes(shape.head_dim, gran)
+    B, Hq, Hkv, Nq, Nk, d = shape.batch, shape.heads_q, shape.heads_kv, shape.seq_q, shape.seq_k, shape.head_dim
+    if not isinstance(o, torch.Tensor) or not o.is_cuda:
+        raise ValueError("o must be a GPU tensor")
+    dev = o.device
+    _expect(o, "o", in_dtype, B * Hq * Nq * d, dev)
+    _expect(q_codes, "q_codes", torch.int8, B * Hq * Nq * d, dev)
+    _expect(q_scale, "q_scale", torch.float32, B * Hq * -(-Nq // bq), dev)
+    _expect(k_codes, "k_codes", torch.int8, B * Hkv * Nk * d, dev)
+    _expect(k_scale, "k_scale", torch.float32, B * Hkv * -(-Nk // bk), dev)
+    _expect(v_prepared, "v_prepared", torch.uint8 if fp8 else in_dtype, B * Hkv * d * sage_v_codes_stride(Nk), dev)
+    if fp8:
+        _expect(v_scale, "v_scale", torch.float32, B * Hkv * d, dev)
     _check(lib.sage_attn_fwd_codes(_ref(shape), _ptr(q_codes), _ptr(q_scale), _ptr(k_codes), _ptr(k_scale),
                                    _ptr(v_prepared), _ptr(v_scale), _ptr(o), int(bool(is_causal)),
                                    float(sm_scale), PV_DTYPES[pv_dtype], _stream(o.device)),
@@ -230,9 +289,8 @@ def sage_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, is_causa
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(s.head_dim)
     dev = q.device
-    o = torch.empty_like(q) if out is None else out
-    need = sage_workspace_bytes(s, pv_dtype)
-    ws = workspace if workspace is not None and workspace.numel() >= need else _workspace(need, dev)
+    o = _out_like(q, out)
+    ws = _workspace_for(workspace, sage_workspace_bytes(s, pv_dtype), dev)
     _check(lib.sage_attn_fwd(_ref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(o), int(bool(is_causal)),
                              float(sm_scale), PV_DTYPES[pv_dtype], _ptr(ws), ws.numel(), _stream(dev)),
            "sage_attn_fwd")
@@ -247,6 +305,8 @@ def varlen_shape_of(q: torch.Tensor, k: torch.Tensor, cu_seqlens_q: torch.Tensor
         raise TypeError(f"q/k/v must be float16 or bfloat16, got {q.dtype}")
     if cu_seqlens_q.dim() != 1 or cu_seqlens_q.numel() < 1:
         raise ValueError("cu_seqlens must be 1-D with B + 1 entries")
+    if k.dtype != q.dtype or k.shape[2] != q.shape[2]:
+        raise ValueError(f"packed q {tuple(q.shape)} and k {tuple(k.shape)} differ in dtype or head_dim")
     return SageVarlenShape(cu_seqlens_q.numel() - 1, q.shape[1], k.shape[1], q.shape[2], q.shape[0], k.shape[0],
                            int(max_seqlen_q), int(max_seqlen_k), DTYPES[q.dtype], QK_GRANS[qk_gran])
 
@@ -273,9 +333,8 @@ def sage_attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_s
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(s.head_dim)
     dev = q.device
-    o = torch.empty_like(q) if out is None else out
-    need = sage_varlen_workspace_bytes(s, pv_dtype)
-    ws = workspace if workspace is not None and workspace.numel() >= need else _workspace(need, dev)
+    o = _out_like(q, out)
+    ws = _workspace_for(workspace, sage_varlen_workspace_bytes(s, pv_dtype), dev)
     _check(lib.sage_attn_fwd_varlen(_ref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
                                     _ptr(o), int(bool(is_causal)), float(sm_scale), PV_DTYPES[pv_dtype], _ptr(ws),
                                     ws.numel(), _stream(dev)), "sage_attn_fwd_varlen")
@@ -285,8 +344,14 @@ def sage_attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_s
 def sage_debug_qk_i32(q_codes: torch.Tensor, k_codes: torch.Tensor) -> torch.Tensor:
     """INT32 S for canonical-order codes [B,Hq,Nq,d] x [B,Hkv,Nk,d] -> [B,Hq,Nq,Nk]."""
     _check_inputs(q_codes, k_codes)
+    if q_codes.dtype != torch.int8 or k_codes.dtype != torch.int8:
+        raise TypeError("codes must be int8")
+    if q_codes.dim() != 4 or k_codes.dim() != 4:
+        raise ValueError("codes must be 4-D [B, H, N, d]")
     B, Hq, Nq, d = q_codes.shape
     _, Hkv, Nk, _ = k_codes.shape
+    if k_codes.shape[0] != B or k_codes.shape[3] != d:
+        raise ValueError("q_codes and k_codes differ in batch or head_dim")
     s = make_shape(B, Hq, Hkv, Nq, Nk, d)
     out = torch.empty((B, Hq, Nq, Nk), dtype=torch.int32, device=q_codes.device)
     _check(lib.sage_debug_qk_i32(_ref(s), _ptr(q_codes), _ptr(k_codes), _ptr(out), _stream(q_codes.device)),

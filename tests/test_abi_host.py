@@ -417,3 +417,44 @@ def test_header_is_plain_c_and_the_library_links_from_c(tmp_path):
     assert r.returncode == 0, (r.returncode, r.stderr)
     assert r.stdout.split() == [str(sage_ref.PER_THREAD_BLK_Q), str(sage_ref.PER_THREAD_BLK_K),
                                 str(sage_ref.BKV[128]), str(10 * 4)]
+
+
+def test_binding_checks_shapes_before_any_library_call():
+    """The binding rejects tensors whose sizes would let a kernel run past a
+    buffer (checked on CPU tensors: the checks precede every library call)."""
+    q = torch.empty(2, 4, 100, 64, dtype=torch.float16)
+    with pytest.raises(ValueError, match="batch or head_dim"):
+        sage.shape_of(q, torch.empty(1, 2, 100, 64, dtype=torch.float16), "HND")      # k's batch smaller
+    with pytest.raises(ValueError, match="batch or head_dim"):
+        sage.shape_of(q, torch.empty(2, 2, 100, 32, dtype=torch.float16), "HND")      # k's head_dim smaller
+    with pytest.raises(TypeError, match="one dtype"):
+        sage.shape_of(q, torch.empty(2, 2, 100, 64, dtype=torch.bfloat16), "HND")
+    with pytest.raises(ValueError, match="batch or head_dim"):
+        sage.shape_of(q.transpose(1, 2), torch.empty(2, 100, 2, 128, dtype=torch.float16), "NHD")
+    # packed batches
+    cq = torch.tensor([0, 50, 100], dtype=torch.int32)
+    with pytest.raises(ValueError, match="head_dim"):
+        sage.varlen_shape_of(torch.empty(100, 4, 64, dtype=torch.float16),
+                             torch.empty(100, 2, 128, dtype=torch.float16), cq, 50, 50)
+    # outputs and workspaces handed in by the caller
+    cpu = torch.device("cpu")
+    with pytest.raises(ValueError, match="shape"):
+        sage._out_like(q, torch.empty(2, 4, 99, 64, dtype=torch.float16))
+    with pytest.raises(TypeError, match="float16"):
+        sage._out_like(q, torch.empty(2, 4, 100, 64, dtype=torch.float32))
+    with pytest.raises(ValueError, match="contiguous"):
+        sage._out_like(q, torch.empty(2, 100, 4, 64, dtype=torch.float16).transpose(1, 2))
+    assert sage._out_like(q, None).shape == q.shape
+    with pytest.raises(TypeError, match="uint8"):
+        sage._workspace_for(torch.empty(4096, dtype=torch.float32), 1024, cpu)
+    with pytest.raises(ValueError, match="must be on"):
+        sage._workspace_for(torch.empty(4096, dtype=torch.uint8), 1024, torch.device("meta"))
+    ws = torch.empty(4096, dtype=torch.uint8)
+    assert sage._workspace_for(ws, 1024, cpu) is ws
+    assert sage._workspace_for(ws, 8192, cpu).numel() == 8192
+    with pytest.raises(ValueError, match="elements"):
+        sage._expect(torch.empty(10, dtype=torch.int8), "q_codes", torch.int8, 11, cpu)
+    # the codes entry point checks every buffer against the shape (o first: it must be a GPU tensor)
+    s = sage.make_shape(1, 2, 2, 100, 100, 64)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        sage.sage_attn_fwd_codes(s, None, None, None, None, None, None, torch.empty(1, 2, 100, 64, dtype=torch.float16))
