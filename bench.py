@@ -146,22 +146,25 @@ def time_fused_entry(plan: Plan, steps: int):
     return (time.perf_counter() - t0) / steps * 1e3
 
 
-def counters_traffic():
-    """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary, or None when it is missing or the kernel sources changed since."""
+def counters_traffic(w: W.Workload, pv: str, qk_gran: str):
+    """HBM bytes per attention launch and the vector/matrix utilisation from the
+    committed rocprofv3 counter summary, or (None, None) when it is missing,
+    the kernel sources changed since, or it was taken on another configuration."""
     if not os.path.exists(COUNTERS_MD):
         return None, None
     text = open(COUNTERS_MD).read()
     def grab(key):
-        m = re.search(rf"^{key}:\s*([0-9a-fA-F.e+-]+)\s*$", text, flags=re.M)
+        m = re.search(rf"^{key}:\s*([0-9A-Za-z_.+-]+)\s*$", text, flags=re.M)
         return m.group(1) if m else None
-    sha = grab("kernel_source_sha256")
+    same_config = (grab("counters_workload") == w.name and grab("counters_causal") == str(int(w.causal))
+                   and grab("counters_pv") == pv and grab("counters_qk_gran") == qk_gran)
     vals = [grab(k) for k in ("fetch_kib_per_dispatch", "write_kib_per_dispatch", "copy_fetch_factor",
                               "copy_write_factor")]
-    if sha != kernel_source_hash() or any(v is None for v in vals):
-        return None, sha
+    if grab("kernel_source_sha256") != kernel_source_hash() or not same_config or any(v is None for v in vals):
+        return None, None
     fetch, write, ff, fw = (float(v) for v in vals)
-    return (fetch * ff + write * fw) * 1024.0, sha
+    util = {k: float(grab(k)) for k in ("valu_busy_pct", "mfma_util_pct") if grab(k) is not None}
+    return (fetch * ff + write * fw) * 1024.0, util or None
 
 
 def cpu_baseline(w: W.Workload, pv: str, rows: int, qk_gran: str = "per_block"):
@@ -324,12 +327,14 @@ def main():
 
     r = measure(w, pv, args.steps, args.warmup, args.qk_gran)
     copy_gbps = copy_bandwidth()
-    traffic, counters_sha = counters_traffic()
+    traffic, util = counters_traffic(w, pv, args.qk_gran)
     roof = {"bound": "mfma", "achieved": round(r["attn_tops"], 2), "peak": PEAK_TOPS, "unit": "TFLOP/s",
             "frac": round(r["attn_tops"] / PEAK_TOPS, 4), "traffic": traffic,
             "kernel": "attn_fwd_fine_kernel" if args.qk_gran == "per_thread" else "attn_fwd_kernel",
             "ops_per_launch": counted_ops(w),
             "mean_launch_ms": round(r["attn_ms"], 4)}
+    if util:
+        roof["counters_pct"] = util     # rocprofv3 VALUBusy / MfmaUtil of the same kernel (profiles/)
     out = {
         "metric": METRIC, "value": round(r["tops"], 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(r["wall_ms"], 4), "higher_is_better": True, "scaling": "weak",

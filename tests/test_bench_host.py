@@ -1,0 +1,22 @@
+"""Host checks of the benchmark's bookkeeping (CPU only).
+
+The committed counter summary is attached to a benchmark line only for the
+configuration and the kernel sources it was taken on.
+"""
+import bench
+import workloads as W
+
+
+def test_counters_attach_only_to_their_own_configuration():
+    traffic, util = bench.counters_traffic(W.PEAK, "fp8", "per_block")
+    assert traffic is not None and traffic > 0            # the committed summary matches the current sources
+    assert set(util) == {"valu_busy_pct", "mfma_util_pct"} and all(0 < v <= 100 for v in util.values())
+    for w, pv, gran in [(W.PEAK.with_(causal=True), "fp8", "per_block"), (W.PEAK, "fp16", "per_block"),
+                        (W.PEAK, "fp8", "per_thread"), (W.MID_OUTLIER, "fp8", "per_block")]:
+        assert bench.counters_traffic(w, pv, gran) == (None, None)
+
+
+def test_counted_ops_follow_the_metric():
+    # 4*B*H*N^2*d, halved for causal
+    assert bench.counted_ops(W.PEAK) == 4.0 * 1 * 32 * 32768 ** 2 * 128
+    assert bench.counted_ops(W.PEAK.with_(causal=True)) == 2.0 * 32 * 32768 ** 2 * 128
