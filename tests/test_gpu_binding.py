@@ -79,3 +79,25 @@ def test_given_output_and_workspace_are_used_and_checked():
         sage.sage_attn_fwd(q, k, v, workspace=torch.empty(ws.numel(), dtype=torch.float32, device="cuda"))
     with pytest.raises(ValueError, match="batch or head_dim"):
         sage.sage_attn_fwd(q, k[:1].contiguous(), v[:1].contiguous())
+
+
+def test_many_batch_heads_with_short_sequences():
+    """131072 (batch, head) pairs of 5 tokens: every quantisation launch puts
+    the pairs in its second grid dimension, past 65535. Heads are independent,
+    so the first and last batches are checked against the oracle on their own."""
+    import numpy as np
+    from oracle import exact, sage_ref
+    from tests.parity_util import COS_EXACT, COS_ORACLE, RL1_ORACLE, cos, rel_l1
+
+    w = W.TINY.with_(B=512, Hq=256, Hkv=256, N=5, d=64, dtype="fp16", pv="fp8", seed=11)
+    say("many heads", w.B * w.Hq)
+    q, k, v = W.generate(w)
+    o = sage.sage_attn_fwd(q.cuda(), k.cuda(), v.cuda(), sm_scale=w.sm_scale, pv_dtype="fp8")
+    torch.cuda.synchronize()
+    got = o.float().cpu().numpy()
+    for sl in (slice(0, 2), slice(w.B - 2, w.B)):
+        qn, kn, vn = (t[sl].float().numpy() for t in (q, k, v))
+        ref = sage_ref.sage_attention(qn, kn, vn, dtype="fp16", is_causal=False, sm_scale=w.sm_scale, pv="fp8")
+        ex = exact.exact_attention(qn, kn, vn, is_causal=False, sm_scale=w.sm_scale)
+        g = got[sl].astype(np.float64)
+        assert cos(g, ref) >= COS_ORACLE and rel_l1(g, ref) <= RL1_ORACLE and cos(g, ex) >= COS_EXACT
