@@ -20,3 +20,13 @@ def test_counted_ops_follow_the_metric():
     # 4*B*H*N^2*d, halved for causal
     assert bench.counted_ops(W.PEAK) == 4.0 * 1 * 32 * 32768 ** 2 * 128
     assert bench.counted_ops(W.PEAK.with_(causal=True)) == 2.0 * 32 * 32768 ** 2 * 128
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
