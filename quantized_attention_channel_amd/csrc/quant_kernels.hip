@@ -7,6 +7,8 @@
 // Arithmetic is kept bit-compatible with a plain IEEE reading of the method:
 // fp64 channel sums, correctly rounded fp32 divides, separate (never fused)
 // subtract and multiply, round-half-to-even to integers.
+#include <algorithm>
+
 #include "sage_device.h"
 #include "sage_launch.h"
 
@@ -167,16 +169,13 @@ __global__ __launch_bounds__((QuantThreads<D, BLK>::value)) void quant_int8_kern
   // Work-groups run in reverse launch order. For K the statistics pass has just
   // read the tensor front to back, so its tail is the part the last-level cache
   // still holds; for Q the order makes no difference.
-  const int bx = gridDim.x - 1 - blockIdx.x;
   const int bh = gridDim.y - 1 - blockIdx.y;
   const int b = bh / H, h = bh % H;
-  const int t0 = bx * TOKS;
   int64_t base = (int64_t)b * geo.batch_stride + (int64_t)h * geo.head_stride + col;
   int8_t* out = codes + (int64_t)bh * N * D + col;
   if (seq) {
     const int32_t* sp = &seq[b].q0 + 2 * side;   // (q0, nq) or (k0, nk)
     N = sp[1];
-    if (t0 >= N) return;                          // past this sequence (its scale slots are never read)
     base += (int64_t)sp[0] * geo.tok_stride;
     out = codes + ((int64_t)h * total + sp[0]) * D + col;
   }
@@ -185,76 +184,93 @@ __global__ __launch_bounds__((QuantThreads<D, BLK>::value)) void quant_int8_kern
 #pragma unroll
   for (int e = 0; e < 8; ++e) mu[e] = SMOOTH ? mean[bh * D + col + e] : 0.0f;
 
-  float val[ITER][8];
-  float amax[ITER];
-#pragma unroll
-  for (int it = 0; it < ITER; ++it) {
-    const int t = t0 + (it * NT + tid) / TPR;
-    amax[it] = 0.0f;
-    if (t < N) {
-      i32x4 raw = *reinterpret_cast<const i32x4*>(x + base + (int64_t)t * geo.tok_stride);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint16_t bits = (uint16_t)(((uint32_t)raw[e / 2]) >> (16 * (e & 1)));
-        float f = T::to_f32(bits);
-        if (SMOOTH) f = f - mu[e];
-        val[it][e] = f;
-        amax[it] = fmaxf(amax[it], fabsf(f));
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) val[it][e] = 0.0f;
-    }
-  }
-  float inv[ITER];
-  if constexpr (WHOLE) {
-    float a = 0.0f;
-#pragma unroll
-    for (int it = 0; it < ITER; ++it) a = fmaxf(a, amax[it]);
-    a = wave_max(a);
-    if ((tid & 63) == 0) red[tid >> 6] = a;
-    __syncthreads();
-    a = red[0];
-#pragma unroll
-    for (int w = 1; w < NT / 64; ++w) a = fmaxf(a, red[w]);
-    if (tid == 0) scale[(int64_t)bh * nblk + bx] = a / 127.0f;
-#pragma unroll
-    for (int it = 0; it < ITER; ++it) inv[it] = a > 0.0f ? 127.0f / a : 0.0f;
-  } else {
+  // One pass per TOKS-token tile. A dense launch has one tile per work-group;
+  // a packed batch's grid covers about the average sequence, and its
+  // work-groups stride over the tiles of longer ones (rather than launching
+  // the longest sequence's tile count for every sequence, mostly empty).
+  for (int bx = gridDim.x - 1 - blockIdx.x; bx * TOKS < N; bx += gridDim.x) {
+    const int t0 = bx * TOKS;
+    float val[ITER][8];
+    float amax[ITER];
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
-      float a = amax[it];
+      const int t = t0 + (it * NT + tid) / TPR;
+      amax[it] = 0.0f;
+      if (t < N) {
+        i32x4 raw = *reinterpret_cast<const i32x4*>(x + base + (int64_t)t * geo.tok_stride);
 #pragma unroll
-      for (int o = 1; o < (G < 64 ? G : 64); o <<= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
-      if constexpr (G > 64) {
-        // the G/64 waves of each block exchange their maxima
-        if ((tid & 63) == 0) red[tid >> 6] = a;
-        __syncthreads();
-        const int w0 = (tid >> 6) & ~(G / 64 - 1);
+        for (int e = 0; e < 8; ++e) {
+          uint16_t bits = (uint16_t)(((uint32_t)raw[e / 2]) >> (16 * (e & 1)));
+          float f = T::to_f32(bits);
+          if (SMOOTH) f = f - mu[e];
+          val[it][e] = f;
+          amax[it] = fmaxf(amax[it], fabsf(f));
+        }
+      } else {
 #pragma unroll
-        for (int w = 0; w < G / 64; ++w) a = fmaxf(a, red[w0 + w]);
-        __syncthreads();                 // red is rewritten by the next pass
+        for (int e = 0; e < 8; ++e) val[it][e] = 0.0f;
       }
-      const int blk = (t0 + (it * NT + tid) / TPR) / BLK;
-      if (tid % G == 0 && blk < nblk) scale[(int64_t)bh * nblk + blk] = a / 127.0f;
-      inv[it] = a > 0.0f ? 127.0f / a : 0.0f;
     }
-  }
+    float inv[ITER];
+    if constexpr (WHOLE) {
+      float a = 0.0f;
+#pragma unroll
+      for (int it = 0; it < ITER; ++it) a = fmaxf(a, amax[it]);
+      a = wave_max(a);
+      if ((tid & 63) == 0) red[tid >> 6] = a;
+      __syncthreads();
+      a = red[0];
+#pragma unroll
+      for (int w = 1; w < NT / 64; ++w) a = fmaxf(a, red[w]);
+      if (tid == 0) scale[(int64_t)bh * nblk + bx] = a / 127.0f;
+#pragma unroll
+      for (int it = 0; it < ITER; ++it) inv[it] = a > 0.0f ? 127.0f / a : 0.0f;
+      __syncthreads();                   // red is rewritten by the next pass
+    } else {
+#pragma unroll
+      for (int it = 0; it < ITER; ++it) {
+        float a = amax[it];
+#pragma unroll
+        for (int o = 1; o < (G < 64 ? G : 64); o <<= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
+        if constexpr (G > 64) {
+          // the G/64 waves of each block exchange their maxima
+          if ((tid & 63) == 0) red[tid >> 6] = a;
+          __syncthreads();
+          const int w0 = (tid >> 6) & ~(G / 64 - 1);
+#pragma unroll
+          for (int w = 0; w < G / 64; ++w) a = fmaxf(a, red[w0 + w]);
+          __syncthreads();               // red is rewritten by the next pass
+        }
+        const int blk = (t0 + (it * NT + tid) / TPR) / BLK;
+        if (tid % G == 0 && blk < nblk) scale[(int64_t)bh * nblk + blk] = a / 127.0f;
+        inv[it] = a > 0.0f ? 127.0f / a : 0.0f;
+      }
+    }
 
 #pragma unroll
-  for (int it = 0; it < ITER; ++it) {
-    const int t = t0 + (it * NT + tid) / TPR;
-    if (t < N) {
-      uint32_t w[2] = {0u, 0u};
+    for (int it = 0; it < ITER; ++it) {
+      const int t = t0 + (it * NT + tid) / TPR;
+      if (t < N) {
+        uint32_t w[2] = {0u, 0u};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float prod = val[it][e] * inv[it];
-        const int q = (int)__builtin_rintf(prod);
-        w[e / 4] |= ((uint32_t)(q & 0xff)) << (8 * (e & 3));
+        for (int e = 0; e < 8; ++e) {
+          const float prod = val[it][e] * inv[it];
+          const int q = (int)__builtin_rintf(prod);
+          w[e / 4] |= ((uint32_t)(q & 0xff)) << (8 * (e & 3));
+        }
+        *reinterpret_cast<i32x2*>(out + (int64_t)t * D) = i32x2{(int)w[0], (int)w[1]};
       }
-      *reinterpret_cast<i32x2*>(out + (int64_t)t * D) = i32x2{(int)w[0], (int)w[1]};
     }
   }
+}
+
+// Work-groups along the token axis for `units` slots of `per_unit` tokens: one
+// per slot, or, for a packed batch, about the average sequence's slot count
+// (the kernels then stride over the slots of longer sequences).
+static int token_wgs(int units, int per_unit, const SeqSpan* seq, int B, int total) {
+  if (!seq) return units;
+  const int64_t per = (int64_t)B * per_unit;
+  return (int)std::max<int64_t>(1, std::min<int64_t>(units, ((int64_t)total + per - 1) / per));
 }
 
 // Launch of quant_int8_kernel over N tokens of B*H heads.
@@ -266,7 +282,7 @@ static void launch_quant_int8(const void* x, TensorGeom geo, int BH, int H, int 
   constexpr int NT = QuantThreads<D, BLK>::value;
   constexpr int TOKS = BLK * (D / 8) >= NT ? BLK : 64;
   const int nblk = (N + BLK - 1) / BLK;
-  const int wgs = (N + TOKS - 1) / TOKS;
+  const int wgs = token_wgs((N + TOKS - 1) / TOKS, TOKS, seq, BH / H, total);
   hipLaunchKernelGGL((quant_int8_kernel<T, D, BLK, SMOOTH>), dim3(wgs, BH), dim3(NT), 0, st,
                      (const uint16_t*)x, geo, H, N, nblk, mean, codes, scale, seq, side, total);
 }
