@@ -75,16 +75,17 @@ def test_patch_restores_and_guards_on_the_cpu():
 # ------------------------------------------------------------------ GPU
 @pytest.mark.gpu
 @pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")
-@pytest.mark.parametrize("causal,gqa", [(False, False), (True, True)])
-def test_patched_sdpa_routes_to_the_kernels(causal, gqa):
+@pytest.mark.parametrize("causal,gqa,pv,gran", [(False, False, "fp8", "per_block"), (True, True, "fp8", "per_block"),
+                                               (True, False, "fp16", "per_thread")])
+def test_patched_sdpa_routes_to_the_kernels(causal, gqa, pv, gran):
     g = torch.Generator().manual_seed(3)
     hkv = 2 if gqa else 4
     q = torch.randn(2, 4, 300, 128, generator=g).half().cuda()
     k = torch.randn(2, hkv, 300, 128, generator=g).half().cuda()
     v = torch.randn(2, hkv, 300, 128, generator=g).half().cuda()
-    with torch.no_grad(), patch_sdpa() as p:
+    with torch.no_grad(), patch_sdpa(pv_dtype=pv, qk_quant_gran=gran) as p:
         got = F.scaled_dot_product_attention(q, k, v, is_causal=causal, enable_gqa=gqa)
-    want = sage.sage_attn_fwd(q, k, v, is_causal=causal, sm_scale=128 ** -0.5)
+    want = sage.sage_attn_fwd(q, k, v, is_causal=causal, sm_scale=128 ** -0.5, pv_dtype=pv, qk_gran=gran)
     torch.cuda.synchronize()
     assert p.routed == 1 and torch.equal(got, want)
 
