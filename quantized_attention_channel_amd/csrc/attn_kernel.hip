@@ -22,8 +22,9 @@
 //      straight from registers into the B operand of the PV product: the K rows
 //      of step 1 are permuted so that each lane's keys are contiguous, exactly
 //      the key order the PV operand needs.
-//   4. R = V^T . P^T on the FP8 (or FP16/BF16) matrix cores into a fresh
-//      accumulator (level 1, one tile), then O = alpha * O + R in fp32 (level 2).
+//   4. PV with two-level accumulation: each matrix instruction sums the
+//      products of its 64 (FP8) or 16 (FP16/BF16) keys (level 1) into the fp32
+//      accumulator O (level 2), after O = alpha * O when a row's max moved.
 // Epilogue: O * s_v[c] / l (FP8) or O / l, rounded to the input dtype and
 // stored in the caller's layout.
 #include <climits>
@@ -159,7 +160,7 @@ __device__ __forceinline__ void load_q_operand(const int8_t* q8_head, int nq, in
   for (int t = 0; t < D / 32; ++t) qreg[t] = buf_load16(rq, (uint32_t)qi * D + 32 * t + 16 * g);
 }
 
-// Per-wave online-softmax state and the level-2 accumulator.
+// Per-wave online-softmax state and the fp32 output accumulator (level 2).
 template <int D>
 struct RowState {
   f32x16 o[D / 32];
@@ -311,8 +312,25 @@ __device__ __forceinline__ void softmax_phase(i32x16* s, int lane, int k0, int q
 }
 
 // PV phase of one KV tile for one wave (matrix-core work): the row sum of the
-// quantised P, R = V^T P^T into a fresh accumulator (level 1), O = alpha O + R
-// (level 2).
+// quantised P, then O = alpha O + V^T P^T. Level 1 of the accumulation is the
+// sum of one matrix instruction's products (64 keys in FP8, 16 in FP16/BF16),
+// level 2 the fp32 accumulator O that each instruction adds its sum into. The
+// rescale by alpha runs only when some row of the wave raised its maximum
+// (alpha != 1); with long sequences most tiles leave every row's max alone,
+// and the 16 multiplies per channel block are then skipped.
+// O = alpha O before a tile's products are added, skipped when alpha is 1 on
+// every lane (a wave-uniform branch: exp2(0) is exactly 1, so a row whose
+// maximum did not move keeps O unchanged either way).
+template <int D>
+__device__ __forceinline__ void rescale_o(float alpha, RowState<D>& st) {
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st.o[cb][e] *= alpha;
+  }
+}
+
 template <int D, bool FP8, typename T>
 __device__ __forceinline__ void pv_phase(const uint8_t* sv, int lane, const PTile<FP8, T>& pt, RowState<D>& st) {
   constexpr int NT = D / 32;
@@ -342,30 +360,26 @@ __device__ __forceinline__ void pv_phase(const uint8_t* sv, int lane, const PTil
       ls = mfma_fp8(ones, pt.pk[1], ls);
       st.l = __builtin_fmaf(alpha, st.l, ls[0]);
     }
+    rescale_o<D>(alpha, st);
 #pragma unroll
     for (int cb = 0; cb < NT; ++cb) {
       if (cb + 1 < NT) load_v(cb + 1, va[cb + 1]);
-      f32x16 r = f32x16{};
 #pragma unroll
-      for (int u = 0; u < 2; ++u) r = mfma_fp8(va[cb][u], pt.pk[u], r);  // level 1
-#pragma unroll
-      for (int e = 0; e < 16; ++e) st.o[cb][e] = __builtin_fmaf(alpha, st.o[cb][e], r[e]);   // level 2
+      for (int u = 0; u < 2; ++u) st.o[cb] = mfma_fp8(va[cb][u], pt.pk[u], st.o[cb]);
     }
   } else {
     using H8 = Half8<T>;
     st.l = __builtin_fmaf(alpha, st.l, pt.lsum);
+    rescale_o<D>(alpha, st);
 #pragma unroll
     for (int cb = 0; cb < NT; ++cb) {
       const int row = cb * 32 + n;
-      f32x16 r = f32x16{};
 #pragma unroll
       for (int u = 0; u < 2 * kBlocks; ++u) {
         // keys 32*(u/2) + 16g + 8*(u%2) + 0..7 -> 16-byte chunk 4*(u/2) + 2g + (u%2)
         const i32x4 raw = lds16(sv + v_lds_off<false>(row, 4 * (u >> 1) + 2 * g + (u & 1)));
-        r = mfma_half(__builtin_bit_cast(H8, raw), pt.ph[u], r);          // level 1
+        st.o[cb] = mfma_half(__builtin_bit_cast(H8, raw), pt.ph[u], st.o[cb]);
       }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) st.o[cb][e] = __builtin_fmaf(alpha, st.o[cb][e], r[e]);   // level 2
     }
   }
 #pragma unroll
@@ -536,9 +550,9 @@ __device__ __forceinline__ void attn_fwd_body(AttnArgs a) {
   };
   // X(t): PV(t-1) with V in buffer 1-P, then QK^T(t) with K in buffer P.
   auto x_bufs = [&](const uint8_t* v_prv, const int8_t* k_cur, bool do_pv, bool do_qk) __attribute__((always_inline)) {
-    // The matrix wave outranks the softmax wave while it issues PV, whose
-    // level-2 merge must not wait behind the softmax's exps; its QK^T part
-    // competes at equal priority (measured: +0.5%; PV at equal priority: -6%).
+    // The matrix wave outranks the softmax wave while it issues PV (and the
+    // rescale of O, when taken), which must not wait behind the softmax's
+    // exps; its QK^T part competes at equal priority.
     __builtin_amdgcn_s_setprio(1);
     if (do_pv) pv_phase<D, FP8, T>(v_prv, lane, pt, st);
     __builtin_amdgcn_sched_barrier(0);         // P and the V operands die before the K operands load
