@@ -35,7 +35,8 @@
  *             NHD = [B, N, H, d], dense with d contiguous. Quantised codes and
  *             scales always use the canonical per-head orders given below.
  * Alignment.  Tensor and code pointers must be 16-byte aligned, scale/mean
- *             pointers 4-byte aligned, workspaces 256-byte aligned.
+ *             pointers 4-byte aligned (sage_attn_fwd_codes' v_scale: 16-byte),
+ *             workspaces 256-byte aligned.
  * Aliasing.   No buffer a call writes (outputs, and the part of the workspace
  *             the size query reports) may overlap another such buffer or any
  *             buffer the call reads; that returns SAGE_ERR_INVALID_ARGUMENT.
@@ -91,7 +92,9 @@ typedef struct sage_shape {
 } sage_shape;
 
 /* Quantisation block sizes and the online-softmax KV tile for `head_dim` and
- * the sage_qk_gran `qk_gran`. BLK_Q query tokens / BLK_K key tokens share one
+ * the sage_qk_gran `qk_gran` (the blocks of the per-block INT8 quantisation:
+ * thu-ml/SageAttention repo card, "How it works"; the per-thread groups:
+ * heatdrop.ai review, "The interesting bit"). BLK_Q query tokens / BLK_K key tokens share one
  * INT8 scale (blocks start at token 0, the last one may be short); the softmax
  * walks KV tiles of BKV keys from key 0 upward, so BKV is part of the result's
  * definition (P's FP8 codes depend on the running row max).
@@ -99,22 +102,34 @@ typedef struct sage_shape {
  * for an unknown granularity; null outputs are skipped. */
 sage_status sage_block_sizes(int32_t head_dim, int32_t qk_gran, int32_t* blk_q, int32_t* blk_k, int32_t* bkv);
 
-/* Nk rounded up to the padded key count of transposed V codes (a multiple of BKV = 128). */
+/* Nk rounded up to the padded key count of transposed V codes (a multiple of
+ * BKV = 128): the row stride of the V operand of the FP8 (or FP16) PV product
+ * (repo card, "How it works"). Returns 0 for seq_k <= 0. */
 int64_t sage_v_codes_stride(int32_t seq_k);
 
-/* Workspace bytes sage_quant_qk needs for `s` (K channel-sum partials). */
+/* Workspace bytes sage_quant_qk needs for `s` (K channel-sum partials of the
+ * smoothing, jisaku.com glossary, 概要). 0 for an invalid shape. */
 size_t sage_quant_qk_workspace_bytes(const sage_shape* s);
-/* Workspace bytes sage_quant_v needs for `s` (V channel-absmax partials). */
+/* Workspace bytes sage_quant_v needs for `s` (V channel-absmax partials of the
+ * FP8 V quantisation, repo card, "How it works"). 0 for an invalid shape. */
 size_t sage_quant_v_workspace_bytes(const sage_shape* s);
 /* Workspace bytes sage_attn_fwd needs for `s` and `pv` (all quantised
- * intermediates: Q/K codes and scales, K mean, V codes or transposed V, V
- * scales, reduction partials). Returns 0 for an invalid shape. */
+ * intermediates of the path the repo card's "How it works" describes: Q/K
+ * codes and scales, K mean, V codes or transposed V, V scales, reduction
+ * partials). Returns 0 for an invalid shape. */
 size_t sage_workspace_bytes(const sage_shape* s, int32_t pv_dtype);
 
 /* K smoothing + INT8 quantisation of Q and K, per block of s->qk_gran.
  * (glossary 概要: K smoothed along the channel direction, then INT8;
  *  repo card "How it works": INT8 for QK^T.)
- *   k_mean [B,Hkv,d] fp32      mu = fp32((sum over all Nk tokens, in fp64) / Nk)
+ *   k_mean [B,Hkv,d] fp32      mu = fp32((sum over all Nk tokens, in fp64) / Nk).
+ *              The fp64 sums are exact, so mu is the correctly rounded mean in
+ *              every summation order, whenever no partial sum needs more than
+ *              53 bits: for fp16 inputs when sum_t |k[t,c]| < 2^29 (for example
+ *              |k| < 512 at Nk = 2^20); for bf16 inputs when sum_t |k[t,c]| <
+ *              2^53 * g, g the finest unit in the last place among the
+ *              channel's nonzero values. Beyond that the sum is deterministic
+ *              and within an fp64 rounding of exact.
  *   q_codes [B,Hq,Nq,d] int8   round-half-even(fp32(q * fp32(127/a))), a = block absmax
  *   q_scale [B,Hq,ceil(Nq/BLK_Q)] fp32  a/127 (0 for an all-zero block, codes 0)
  *   k_codes [B,Hkv,Nk,d] int8  the same rule on fp32(k - mu)
@@ -134,7 +149,10 @@ sage_status sage_quant_v(const sage_shape* s, const void* v,
                          uint8_t* v_codes, float* v_scale,
                          void* workspace, size_t workspace_bytes, void* stream);
 
-/* The whole forward: o = SageAttention(q, k, v).
+/* The whole forward: o = SageAttention(q, k, v), the call the pages show as
+ * sageattn(q, k, v, tensor_layout="HND", is_causal=False) and as the drop-in
+ * for scaled_dot_product_attention (cnnetsun.cn guide, basic usage; repo card,
+ * "How to use"; heatdrop.ai review, "What it does").
  * is_causal: query i attends keys j <= i (top-left; requires Nq == Nk).
  * sm_scale:  softmax temperature (finite, > 0; 1/sqrt(d) for the drop-in).
  * pv_dtype:  sage_pv_dtype. o has q's shape, dtype and layout and must not
@@ -189,29 +207,35 @@ sage_status sage_attn_fwd_varlen(const sage_varlen_shape* s, const void* q, cons
                                  int32_t is_causal, float sm_scale, int32_t pv_dtype, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
-/* FP16-PV preparation of V: the 16-bit values transposed to
+/* FP16-PV preparation of V (repo card, "How it works": FP16 for PV): the
+ * 16-bit values transposed to
  *   v_t [B,Hkv,d,sage_v_codes_stride(Nk)] (keys contiguous per channel, padding keys 0),
  * the layout the PV product reads in FP16/BF16 mode. */
 sage_status sage_transpose_v(const sage_shape* s, const void* v, void* v_t, void* stream);
 
-/* The fused attention kernel alone, from precomputed codes (for callers that
- * quantise once and reuse K/V codes, and to time the kernel by itself):
+/* The fused attention kernel alone, from precomputed codes: INT8 QK^T,
+ * online softmax, P quantisation and two-level PV (repo card, "How it works";
+ * jisaku.com glossary, 概要). For callers that quantise once and reuse K/V
+ * codes, and to time the kernel by itself:
  *   q_codes/q_scale/k_codes/k_scale  as written by sage_quant_qk
  *   v_prepared  FP8: e4m3 codes from sage_quant_v;  FP16: v_t from sage_transpose_v
- *   v_scale     FP8: from sage_quant_v;  FP16: ignored (may be NULL)
+ *   v_scale     FP8: from sage_quant_v, 16-byte aligned (read four channels
+ *               at a time);  FP16: ignored (may be NULL)
  * o, is_causal, sm_scale, pv_dtype as for sage_attn_fwd. Needs no workspace. */
 sage_status sage_attn_fwd_codes(const sage_shape* s, const int8_t* q_codes, const float* q_scale,
                                 const int8_t* k_codes, const float* k_scale, const void* v_prepared,
                                 const float* v_scale, void* o, int32_t is_causal, float sm_scale,
                                 int32_t pv_dtype, void* stream);
 
-/* Test hook: the INT32 QK^T of the attention kernel's own matrix-core tile code,
+/* Test hook: the INT32 QK^T of the attention kernel's own matrix-core tile code
+ * (the INT8 QK^T with INT32 accumulation of the repo card's "How it works"),
  * for canonical-order codes as produced by sage_quant_qk.
  *   s_out [B,Hq,Nq,Nk] int32, s_out[b,h,i,j] = sum_c q_codes[b,h,i,c] * k_codes[b,h/G,j,c]. */
 sage_status sage_debug_qk_i32(const sage_shape* s, const int8_t* q_codes, const int8_t* k_codes,
                               int32_t* s_out, void* stream);
 
-/* Static description of a status code (never NULL). */
+/* Static description of a status code (never NULL). Part of the error
+ * convention above, not of the method. */
 const char* sage_status_string(sage_status st);
 
 #ifdef __cplusplus

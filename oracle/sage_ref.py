@@ -25,8 +25,8 @@ Readings where the pages are silent (each also listed in the design notes):
   [R3] codes are symmetric in [-127, 127].
   [R4] an all-zero block gets scale 0 and codes 0.
   [R5] the K mean runs over all Nk tokens of a (batch, kv-head).
-  [R6] K channel sums are taken in fp64 (exact for these inputs), divided by
-       Nk in fp64 and rounded once to fp32.
+  [R6] K channel sums are exact (rounded once to fp64), divided by Nk in
+       fp64 and rounded once to fp32.
   [R7] quantisation blocks: BLK_Q = 128 query tokens, BLK_K = 64 key tokens,
        starting at token 0, the last block possibly short; one scale per
        (batch, head, block) over all d channels.
@@ -89,13 +89,35 @@ def as_hnd(x: np.ndarray, layout: str) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # Step 1: K channel mean  (glossary 概要: smoothing along the channel direction)
 # ---------------------------------------------------------------------------
+def _exact_sums(x: np.ndarray) -> np.ndarray:
+    """sum over axis 0 of x [N, d] (float64), each column's exact sum rounded
+    once to fp64. Where every partial sum is an integer multiple of the
+    column's finest unit g (the lowest set significand bit among its nonzero
+    values) below g * 2^53, plain fp64 addition is exact in any order; the
+    other columns are summed by math.fsum."""
+    total = x.sum(axis=0)
+    a = np.abs(x)
+    m, e = np.frexp(a)                                     # a = m 2^e, m in [0.5, 1)
+    sig = (m * 2.0 ** 53).astype(np.int64)                 # exact: m has at most 53 bits
+    low = sig & -sig                                       # lowest set bit (0 for zeros)
+    unit = np.where(low > 0, np.ldexp(low.astype(np.float64), e - 53), np.inf).min(axis=0)
+    for c in np.nonzero(a.sum(axis=0) >= unit * 2.0 ** 53)[0]:
+        total[c] = math.fsum(x[:, c])
+    return total
+
+
 def k_channel_mean(k: np.ndarray) -> np.ndarray:
-    """mu[b,h,c] = fp32( (sum_t K[b,h,t,c]) / Nk ), sum and division in fp64 [R5, R6].
+    """mu[b,h,c] = fp32( (sum_t K[b,h,t,c]) / Nk ): the exact sum rounded to
+    fp64, an fp64 division, one rounding to fp32 [R5, R6].
 
     ``k``: float32 array [B,Hkv,Nk,d] holding the fp16/bf16 input values.
     """
-    n = k.shape[2]
-    total = np.asarray(k, dtype=np.float64).sum(axis=2)
+    B, H, n, d = k.shape
+    x = np.asarray(k, dtype=np.float64)
+    total = np.zeros((B, H, d), np.float64)
+    for b in range(B):
+        for h in range(H):
+            total[b, h] = _exact_sums(x[b, h])
     return (total / n).astype(np.float32)
 
 
@@ -184,7 +206,8 @@ def dequant_factor(sq_rows: np.ndarray, sk_keys: np.ndarray, sm_scale: float) ->
 # ---------------------------------------------------------------------------
 # Steps 5-9: tiled online softmax with P quantisation and two-level PV
 # ---------------------------------------------------------------------------
-def online_softmax_pv(s2: np.ndarray, vals: np.ndarray, *, bkv: int, p_codec, work_dtype):
+def online_softmax_pv(s2: np.ndarray, vals: np.ndarray, *, bkv: int, p_codec, work_dtype,
+                      row_sum_unquantised: bool = False):
     """FlashAttention-style online softmax over KV tiles of ``bkv`` keys [R14, R15].
 
     ``s2``  : [R, Nk] log2-domain scores, -inf where masked.
@@ -194,6 +217,9 @@ def online_softmax_pv(s2: np.ndarray, vals: np.ndarray, *, bkv: int, p_codec, wo
               (None: identity).
     ``work_dtype``: np.float32 for the method (scores, max, P~ in fp32),
               np.float64 for the unquantised reference recurrence.
+    ``row_sum_unquantised``: the rejected reading of [R16] (l adds the fp32
+              P~ instead of the values entering PV); only for tests that
+              measure how far that reading lands from the chosen one.
 
     Per tile t, in ascending order:
       m_new = max(m_old, max_j s2);  alpha = exp2(m_old - m_new)  (0 on the first tile)
@@ -220,7 +246,7 @@ def online_softmax_pv(s2: np.ndarray, vals: np.ndarray, *, bkv: int, p_codec, wo
         p = np.where(live[:, None], p, 0).astype(work_dtype)
         alpha = np.where(live, alpha, 0.0).astype(np.float64)
         pq = p.astype(np.float64) if p_codec is None else p_codec(p)
-        l = alpha * l + pq.sum(axis=1)                # [R16]
+        l = alpha * l + (p.astype(np.float64) if row_sum_unquantised else pq).sum(axis=1)   # [R16]
         r = pq @ vals[t0:t0 + bkv]                    # level 1 (exact for e4m3 x e4m3)
         o = alpha[:, None] * o + r                    # level 2
         m = m_new
@@ -248,9 +274,20 @@ def _p_codec_half(dtype: str):
     return codec
 
 
+# Readings the method does NOT take, selectable by name so that tests can
+# measure how far each one lands from the chosen reading (the parity bounds
+# must tell them apart). None of them is the method.
+REJECTED_READINGS = (
+    "p_unrounded",           # [R12]/[R13] rejected: P enters PV unrounded (FP8 mode: 448 P~ unquantised)
+    "row_sum_unquantised",   # [R16] rejected: l adds the fp32 P~ rather than the values entering PV
+    "p_half_bf16",           # [R13] rejected for fp16 inputs: P rounded to bf16
+    "p_half_fp16",           # [R13] rejected for bf16 inputs: P rounded to fp16
+)
+
+
 def sage_attention(q, k, v, *, dtype: str, is_causal: bool, sm_scale: float, pv: str,
                    layout: str = "HND", blk_q: int = BLK_Q, blk_k: int = BLK_K, bkv=None,
-                   rows=None, parts=None, return_fp64: bool = False):
+                   rows=None, parts=None, return_fp64: bool = False, rejected: tuple = ()):
     """Quantised attention forward, step by step.
 
     ``q,k,v``: float32 numpy arrays holding the fp16/bf16 input values in
@@ -260,7 +297,12 @@ def sage_attention(q, k, v, *, dtype: str, is_causal: bool, sm_scale: float, pv:
     quantisation outputs (dict from ``quant_qk`` plus ``v8``/``v_scale``).
     Returns [B,Hq,R,d] in HND order, rounded to ``dtype`` (float64 array of the
     rounded values), or the unrounded fp64 result when ``return_fp64``.
+    ``rejected``: names from REJECTED_READINGS to compute a rejected reading
+    instead of the method (tests only; empty for the method itself).
     """
+    unknown = set(rejected) - set(REJECTED_READINGS)
+    if unknown:
+        raise ValueError(f"unknown readings {sorted(unknown)}")
     q = as_hnd(np.asarray(q, np.float32), layout)
     k = as_hnd(np.asarray(k, np.float32), layout)
     v = as_hnd(np.asarray(v, np.float32), layout)
@@ -280,10 +322,20 @@ def sage_attention(q, k, v, *, dtype: str, is_causal: bool, sm_scale: float, pv:
     if pv == "fp8":
         vals_all = e4m3_decode(parts["v8"])                 # [B,Hkv,d,Nk]
         codec = _p_codec_fp8
+        if "p_unrounded" in rejected:
+            codec = lambda p: p.astype(np.float64) * E4M3_MAX          # noqa: E731
     elif pv == "fp16":
-        codec = _p_codec_half(dtype)
+        half = dtype
+        if "p_half_bf16" in rejected:
+            half = "bf16"
+        if "p_half_fp16" in rejected:
+            half = "fp16"
+        codec = _p_codec_half(half)
+        if "p_unrounded" in rejected:
+            codec = lambda p: p.astype(np.float64)                     # noqa: E731
     else:
         raise ValueError(pv)
+    row_sum_unq = "row_sum_unquantised" in rejected
 
     keys = np.arange(Nk)
     out = np.empty((B, Hq, len(rows), d), dtype=np.float64)
@@ -299,7 +351,10 @@ def sage_attention(q, k, v, *, dtype: str, is_causal: bool, sm_scale: float, pv:
                 vals = np.ascontiguousarray(vals_all[b, g].T)                   # [Nk, d] code values
             else:
                 vals = v[b, g].astype(np.float64)
-            o, l = online_softmax_pv(s2, vals, bkv=bkv, p_codec=codec, work_dtype=np.float32)
+            o, l = online_softmax_pv(s2, vals, bkv=bkv, p_codec=codec, work_dtype=np.float32,
+                                     row_sum_unquantised=row_sum_unq)
+            if row_sum_unq and pv == "fp8":
+                l = l * E4M3_MAX                                                # P8 carries the factor 448
             if pv == "fp8":                                                     # epilogue
                 o = o * parts["v_scale"][b, g].astype(np.float64)[None, :]
             out[b, h] = o / l[:, None]

@@ -78,8 +78,12 @@ __device__ __forceinline__ i32x4 lds16(const void* p) { return *reinterpret_cast
 // Direct global -> LDS loads (no staging registers): in each wave-wide load,
 // lane L writes 16 bytes at LDS slot base + 16 * L, so every lane fetches the
 // global chunk that the swizzled layout puts in its slot. Per-lane offsets do
-// not depend on the tile; the tile offset goes in the scalar offset. Rows past
-// Nk read as zeros through the buffer range check.
+// not depend on the tile. The buffer range check covers only the per-lane
+// (VGPR) offset, not the scalar one, so each K load pass gets its own resource,
+// based at the pass's first byte and sized to the bytes of the head that
+// remain: K rows past Nk then read as zeros and no load leaves the K slice.
+// V^T rows are padded to whole tiles, so every V load lies inside its rows and
+// the tile offset can ride in the scalar offset.
 template <int D, bool FP8, int NW>
 struct TileStage {
   static constexpr int kVRowB = kBkv * (FP8 ? 1 : 2);
@@ -106,12 +110,16 @@ struct TileStage {
     const int vrow = slot / (kVRowB / 16), vchunk = slot % (kVRowB / 16);
     voff = (uint32_t)vrow * n_pad * kEb + ((vchunk ^ v_swz<FP8>(vrow)) << 4);
   }
-  static __device__ __forceinline__ void issue_k(__amdgpu_buffer_rsrc_t rk, uint32_t koff, int wave, int k0,
-                                                 int8_t* sk) {
+  // kbase/kbytes: this head's K codes [Nk][D] (or a packed sequence's)
+  static __device__ __forceinline__ void issue_k(const int8_t* kbase, uint32_t kbytes, uint32_t koff, int wave,
+                                                 int k0, int8_t* sk) {
 #pragma unroll
-    for (int i = 0; i < kKLoads; ++i)
+    for (int i = 0; i < kKLoads; ++i) {
+      const uint32_t start = (uint32_t)k0 * D + i * kPass;
+      const auto rk = make_rsrc(kbase + start, kbytes > start ? kbytes - start : 0u);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(sk + (i * NW + wave) * 1024),
-                                              16, koff, k0 * D + i * kPass, 0, 0);
+                                              16, koff, 0, 0, 0);
+    }
   }
   // rv covers this head's V^T rows [D][n_pad]
   static __device__ __forceinline__ void issue_v(__amdgpu_buffer_rsrc_t rv, uint32_t voff, int wave, int k0,
@@ -498,7 +506,8 @@ __device__ __forceinline__ void attn_fwd_body(AttnArgs a) {
   const int n_wg = ((2 * qp + 1) * kBq < nq) ? tiles_for(2 * qp + 1) : tiles_for(2 * qp);
 
   constexpr int eb = FP8 ? 1 : 2;
-  const auto rk = make_rsrc(a.k8 + k_off, (uint32_t)nk * D);
+  const int8_t* kbase = a.k8 + k_off;
+  const uint32_t kbytes = (uint32_t)nk * D;
   const auto rv = make_rsrc(reinterpret_cast<const uint8_t*>(a.vt) + v_off * eb, (uint32_t)(v_len * eb));
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   // All eight waves load the first K tile.
@@ -512,7 +521,7 @@ __device__ __forceinline__ void attn_fwd_body(AttnArgs a) {
   using StageG = TileStage<D, FP8, 4>;
   uint32_t koffg, voffg;
   StageG::init(koffg, voffg, wv & 3, lane, a.n_pad);
-  Stage::issue_k(rk, koff, wv, 0, reinterpret_cast<int8_t*>(smem));
+  Stage::issue_k(kbase, kbytes, koff, wv, 0, reinterpret_cast<int8_t*>(smem));
   wait_loads_barrier();
 
   RowState<D> st;
@@ -541,7 +550,7 @@ __device__ __forceinline__ void attn_fwd_body(AttnArgs a) {
   auto loads = [&](auto par, int t) __attribute__((always_inline)) {
     constexpr int P = decltype(par)::value;
     if (t + 1 < n_wg)
-      StageG::issue_k(rk, koffg, wv & 3, (t + 1) * kBkv, reinterpret_cast<int8_t*>(smem + (1 - P) * kKBytes));
+      StageG::issue_k(kbase, kbytes, koffg, wv & 3, (t + 1) * kBkv, reinterpret_cast<int8_t*>(smem + (1 - P) * kKBytes));
     if (t < n_wg) StageG::issue_v(rv, voffg, wv & 3, t * kBkv, a.n_pad, smem + 2 * kKBytes + P * kVBytes);
   };
   // (the last pairs and the idle pairs: runtime parity)

@@ -541,7 +541,7 @@ sage_status sage_attn_fwd_codes(const sage_shape* s, const int8_t* q_codes, cons
   if (!q_codes || !q_scale || !k_codes || !k_scale || !v_prepared || !o || (fp8 && !v_scale))
     return SAGE_ERR_INVALID_ARGUMENT;
   if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(v_prepared, 16) || !aligned(o, 16) ||
-      !aligned(q_scale, 4) || !aligned(k_scale, 4) || (fp8 && !aligned(v_scale, 4)))
+      !aligned(q_scale, 4) || !aligned(k_scale, 4) || (fp8 && !aligned(v_scale, 16)))
     return SAGE_ERR_INVALID_ARGUMENT;
   const size_t obytes = size_t(d.B * d.Hq * d.Nq * d.D) * 2;
   const int64_t npad = round_up(d.Nk, sage::kVPad);

@@ -222,6 +222,8 @@ def test_other_entry_points_reject_aliased_writes():
     qc, qs, kc, ks, vp, vsc = (FAKE + i * G for i in range(6))
     for o in (qs, ks, vsc, vp + 4096):
         assert sage.lib.sage_attn_fwd_codes(sp, qc, qs, kc, ks, vp, vsc, o, 0, 0.1, 1, None) == bad
+    # v_scale is read as 16-byte vectors: a 4-byte-aligned one is refused
+    assert sage.lib.sage_attn_fwd_codes(sp, qc, qs, kc, ks, vp, vsc + 4, FAKE + 7 * G, 0, 0.1, 1, None) == bad
     # the INT32 hook: s_out on the codes, and a product of sizes past 2^64 bytes
     assert sage.lib.sage_debug_qk_i32(sp, FAKE, FAKE + G, FAKE + 64, None) == bad
     huge = ctypes.byref(_shape(B=1 << 10, Hq=1 << 14, Hkv=1 << 14, Nq=1 << 20, Nk=1 << 20))

@@ -14,6 +14,7 @@ import torch
 
 import workloads as W
 from oracle import exact, sage_ref
+from tests.full_size import run_full_size
 from tests.parity_util import COS_EXACT, COS_ORACLE, RL1_ORACLE, cos, rel_l1, say, worst_head_cos
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -93,45 +94,28 @@ def test_attention_per_thread_all_rows(w, nq, pv):
                                   blk_q=BQ, blk_k=BK)
     ex = exact.exact_attention(qn, kn, vn, is_causal=w.causal, sm_scale=w.sm_scale)
     c, r, ce = cos(got, ref), rel_l1(got, ref), cos(got, ex)
-    say(f"   cos={c:.7f} rel_l1={r:.2e} cos_exact={ce:.6f} worst_head={worst_head_cos(got, ref):.7f}")
+    wh = worst_head_cos(got, ref)
+    say(f"   cos={c:.7f} rel_l1={r:.2e} cos_exact={ce:.6f} worst_head={wh:.7f}")
     assert np.isfinite(got).all()
+    assert wh >= COS_ORACLE
     assert c >= COS_ORACLE and r <= RL1_ORACLE
     assert ce >= COS_EXACT
 
 
 FULL = [
-    (W.MID_OUTLIER, "fp8", 24),
-    (W.GQA_CAUSAL, "fp8", 24),
-    (W.LONG_D64, "fp16", 24),
-    (W.PEAK, "fp8", 16),
+    (W.MID_OUTLIER, "fp8"),
+    (W.GQA_CAUSAL, "fp8"),
+    (W.LONG_D64, "fp16"),
+    (W.LONG_D64, "fp8"),
+    (W.PEAK, "fp8"),
 ]
 
 
-@pytest.mark.parametrize("w,pv,nrows", FULL, ids=[f"{w.name}-{pv}" for w, pv, _ in FULL])
-def test_per_thread_full_size(w, pv, nrows):
-    say("full workload per-thread", w.name, pv)
-    q, k, v = W.generate(w)
-    qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
-    o = sage.sage_attn_fwd(qg, kg, vg, is_causal=w.causal, sm_scale=w.sm_scale, pv_dtype=pv,
-                           tensor_layout=w.layout, qk_gran="per_thread")
-    quant = sage.sage_quant_qk(qg, kg, tensor_layout=w.layout, qk_gran="per_thread")
-    torch.cuda.synchronize()
-    del qg, kg, vg
-    qn, kn, vn = _np_inputs(q, k, v, w.layout)
-    parts = sage_ref.quant_qk(qn, kn, blk_q=BQ, blk_k=BK)
-    _check_quant(quant, parts)
-    if pv == "fp8":
-        parts["v8"], parts["v_scale"] = sage_ref.quant_v_fp8(vn)
-    rows = np.array(W.sample_rows(w.N, nrows, sage_ref.BLK_Q))
-    got = sage_ref.as_hnd(o.float().cpu().numpy(), w.layout)[:, :, rows]
-    ref = sage_ref.sage_attention(qn, kn, vn, dtype=w.dtype, is_causal=w.causal, sm_scale=w.sm_scale, pv=pv,
-                                  rows=rows, parts=parts, blk_q=BQ, blk_k=BK)
-    ex = exact.exact_attention(qn, kn, vn, is_causal=w.causal, sm_scale=w.sm_scale, rows=rows)
-    c, r, ce = cos(got, ref), rel_l1(got, ref), cos(got, ex)
-    say(f"   cos={c:.7f} rel_l1={r:.2e} cos_exact={ce:.6f} worst_head={worst_head_cos(got, ref):.7f}")
-    assert np.isfinite(got).all()
-    assert c >= COS_ORACLE and r <= RL1_ORACLE
-    assert ce >= COS_EXACT
+@pytest.mark.parametrize("w,pv", FULL, ids=[f"{w.name}-{pv}" for w, pv in FULL])
+def test_per_thread_full_size(w, pv):
+    # per-thread scales reach the 0.999 exact-attention bound on every workload,
+    # the outlier one included
+    run_full_size(sage, w, pv, "per_thread", exact_bound=COS_EXACT)
 
 
 def test_sageattn_switch_selects_per_thread_scales():

@@ -88,6 +88,22 @@ def test_patched_sdpa_routes_to_the_kernels(causal, gqa, pv, gran):
     want = sage.sage_attn_fwd(q, k, v, is_causal=causal, sm_scale=128 ** -0.5, pv_dtype=pv, qk_gran=gran)
     torch.cuda.synchronize()
     assert p.routed == 1 and torch.equal(got, want)
+    # and against the oracle (SDPA's default scale 1/sqrt(d)), not only the library itself
+    _against_oracle(got, q, k, v, causal=causal, sm_scale=128 ** -0.5, pv=pv, gran=gran)
+
+
+def _against_oracle(got, q, k, v, *, causal, sm_scale, pv, gran, dtype="fp16"):
+    from oracle import exact, sage_ref
+    from tests.parity_util import COS_EXACT, COS_ORACLE, RL1_ORACLE, cos, rel_l1, worst_head_cos
+    blk = ((sage_ref.PER_THREAD_BLK_Q, sage_ref.PER_THREAD_BLK_K) if gran == "per_thread"
+           else (sage_ref.BLK_Q, sage_ref.BLK_K))
+    qn, kn, vn = (t.float().cpu().numpy() for t in (q, k, v))
+    ref = sage_ref.sage_attention(qn, kn, vn, dtype=dtype, is_causal=causal, sm_scale=sm_scale, pv=pv,
+                                  blk_q=blk[0], blk_k=blk[1])
+    g = got.float().cpu().numpy()
+    assert cos(g, ref) >= COS_ORACLE and rel_l1(g, ref) <= RL1_ORACLE and worst_head_cos(g, ref) >= COS_ORACLE
+    ex = exact.exact_attention(qn, kn, vn, is_causal=causal, sm_scale=sm_scale)
+    assert cos(g, ex) >= COS_EXACT
 
 
 @pytest.mark.gpu
@@ -113,3 +129,38 @@ def test_captured_graph_equals_eager():
     compiled = torch.compile(f, backend="aot_eager", fullgraph=True)(q, k, v)
     torch.cuda.synchronize()
     assert torch.equal(eager, compiled)
+    # the operator's output inside the compiled graph against the oracle
+    def g_(q, k, v):
+        o = torch.ops.sage_mi355x.attn_fwd(q * 2, k, v, True, 0.0625, "fp8", "HND", "per_block")
+        return o
+
+    out = torch.compile(g_, backend="aot_eager", fullgraph=True)(q, k, v)
+    torch.cuda.synchronize()
+    _against_oracle(out, q * 2, k, v, causal=True, sm_scale=0.0625, pv="fp8", gran="per_block", dtype="bf16")
+
+
+@pytest.mark.gpu
+@pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")
+@pytest.mark.parametrize("backend", ["inductor", "aot_eager"])
+def test_compiled_model_against_oracle(backend):
+    """A small attention block compiled with torch.compile: the projections run
+    in torch, the attention in the custom operator (one opaque graph node); the
+    result is checked against the same block with the oracle's attention."""
+    g = torch.Generator().manual_seed(6)
+    B, H, N, d = 1, 4, 300, 64
+    x = torch.randn(B, N, H * d, generator=g).half().cuda()
+    wq, wk, wv = (torch.randn(H * d, H * d, generator=g).mul(0.05).half().cuda() for _ in range(3))
+
+    def block(x):
+        q, k, v = (torch.matmul(x, w).view(B, N, H, d).transpose(1, 2).contiguous() for w in (wq, wk, wv))
+        return torch.ops.sage_mi355x.attn_fwd(q, k, v, False, d ** -0.5, "fp16", "HND", "per_block"), q, k, v
+
+    try:
+        fn = torch.compile(block, backend=backend, fullgraph=True)
+        o, q, k, v = fn(x)
+    except Exception as e:  # noqa: BLE001 -- a backend that cannot build here is reported, not hidden
+        if backend == "inductor":
+            pytest.skip(f"inductor backend unavailable on this machine: {type(e).__name__}: {e}")
+        raise
+    torch.cuda.synchronize()
+    _against_oracle(o, q, k, v, causal=False, sm_scale=d ** -0.5, pv="fp16", gran="per_block")

@@ -139,6 +139,71 @@ def test_p_quantisation_worked_example():
     assert np.all(o[2:] == 0)
 
 
+def _worked_half_case():
+    """One query, four keys and their negations (so every K channel mean is 0),
+    scores exactly 0, -1/2, -1/4, -1 below the row max in the log2 domain
+    (tests/golden/p_half_worked.txt)."""
+    d = 64
+    q = np.zeros((1, 1, 1, d), np.float32)
+    q[0, 0, 0, :2] = [127.0, 1.0]
+    k = np.zeros((1, 1, 8, d), np.float32)
+    v = np.zeros((1, 1, 8, d), np.float32)
+    for j, a in enumerate([127.0, 125.0, 126.0, 123.0]):
+        k[0, 0, j, :2] = a
+        k[0, 0, 4 + j, :2] = -a
+        v[0, 0, j, j] = 1.0
+    v[0, 0, :4, 4] = [1.0, -1.0, 1.0, -1.0]
+    return q, k, v, 2.0 ** -9 / sage_ref.LOG2E
+
+
+def _half_golden():
+    import os
+    rows = {"fp16": [], "bf16": []}
+    with open(os.path.join(os.path.dirname(__file__), "golden", "p_half_worked.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                dt, ch, num, den = line.split()
+                rows[dt].append((int(ch), float(num) / float(den)))
+    return rows
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_p_half_rounding_worked_example(dtype, rejected=()):
+    """FP16-PV mode: P~ rounded to the input dtype and the row sum of the rounded
+    values, by hand (tests/golden/p_half_worked.txt) [R13, R16]."""
+    q, k, v, sm = _worked_half_case()
+    o = sage_ref.sage_attention(q, k, v, dtype=dtype, is_causal=False, sm_scale=sm, pv="fp16",
+                                return_fp64=True, rejected=rejected)[0, 0, 0]
+    for ch, want in _half_golden()[dtype]:
+        assert abs(o[ch] - want) <= 1e-9      # exact dyadic sums; the rejected readings are >1e-5 away
+    assert np.all(o[5:] == 0)
+
+
+@pytest.mark.parametrize("dtype,rejected", [
+    ("fp16", ("p_unrounded",)), ("fp16", ("p_half_bf16",)), ("fp16", ("row_sum_unquantised",)),
+    ("bf16", ("p_unrounded",)), ("bf16", ("p_half_fp16",)), ("bf16", ("row_sum_unquantised",)),
+])
+def test_p_half_worked_example_rejects_other_readings(dtype, rejected):
+    with pytest.raises(AssertionError):
+        test_p_half_rounding_worked_example(dtype, rejected)
+
+
+@pytest.mark.parametrize("rejected", [("p_unrounded",), ("row_sum_unquantised",)])
+def test_p_fp8_worked_example_rejects_other_readings(rejected):
+    q, k, v = _worked_fp8_case()
+    o = sage_ref.sage_attention(q, k, v, dtype="fp16", is_causal=False, sm_scale=0.125, pv="fp8",
+                                return_fp64=True, rejected=rejected)[0, 0, 0]
+    assert abs(o[0] - 608 / 768) > 1e-3
+
+
+def test_unknown_reading_is_refused():
+    q, k, v, sm = _worked_half_case()
+    with pytest.raises(ValueError):
+        sage_ref.sage_attention(q, k, v, dtype="fp16", is_causal=False, sm_scale=sm, pv="fp16",
+                                rejected=("p_scaled_by_240",))
+
+
 # --------------------------------------------------------------------------- structure
 @pytest.mark.parametrize("pv", ["fp16", "fp8"])
 def test_gqa_equals_repeated_heads(pv):
@@ -249,6 +314,29 @@ def test_planted_mistakes_are_caught(monkeypatch):
     with monkeypatch.context() as m:
         m.setattr(sage_ref, "_p_codec_fp8", lambda p: p.astype(np.float64) * 448.0)
         assert _fails(test_p_quantisation_worked_example)
+    # 4b. FP16-PV mode: P left unrounded; P rounded to bf16 for fp16 inputs; P
+    #     rounded to fp16 for bf16 inputs
+    with monkeypatch.context() as m:
+        m.setattr(sage_ref, "_p_codec_half", lambda dtype: (lambda p: p.astype(np.float64)))
+        assert _fails(lambda: test_p_half_rounding_worked_example("fp16"))
+        assert _fails(lambda: test_p_half_rounding_worked_example("bf16"))
+    orig_half = sage_ref._p_codec_half
+    with monkeypatch.context() as m:
+        m.setattr(sage_ref, "_p_codec_half", lambda dtype: orig_half("bf16"))
+        assert _fails(lambda: test_p_half_rounding_worked_example("fp16"))
+    with monkeypatch.context() as m:
+        m.setattr(sage_ref, "_p_codec_half", lambda dtype: orig_half("fp16"))
+        assert _fails(lambda: test_p_half_rounding_worked_example("bf16"))
+    # 4c. the row sum over the unquantised P~ (a dropped codec on the l update)
+    orig_osp = sage_ref.online_softmax_pv
+    with monkeypatch.context() as m:
+        m.setattr(sage_ref, "online_softmax_pv",
+                  lambda *a, **kw: orig_osp(*a, **{**kw, "row_sum_unquantised": True}))
+        assert _fails(lambda: test_p_half_rounding_worked_example("fp16"))
+    # 4d. channel sums by plain fp64 addition (rounds where the exact sum does not)
+    with monkeypatch.context() as m:
+        m.setattr(sage_ref, "_exact_sums", lambda x: x.sum(axis=0))
+        assert _fails(tq.test_k_mean_is_exact_where_fp64_addition_would_round)
     # 5. log2(e) dropped from the dequantisation factor (natural-log scores fed to exp2)
     orig_dq = sage_ref.dequant_factor
     with monkeypatch.context() as m:

@@ -49,6 +49,19 @@ def test_k_mean_is_exact_sum_correctly_divided():
                     assert abs(float(got) - float(want)) <= float(np.spacing(np.float32(abs(want)))), (b, h, c)
 
 
+def test_k_mean_is_exact_where_fp64_addition_would_round():
+    """A channel whose plain fp64 running sum loses a term (2^60 + 1 - 2^60, all
+    bf16-exact) still gets the exact mean; a channel within the fp64 bound is
+    summed plainly and agrees with math.fsum."""
+    k = np.zeros((1, 1, 3, 2), np.float32)
+    k[0, 0, :, 0] = [2.0 ** 60, 1.0, -(2.0 ** 60)]
+    k[0, 0, :, 1] = [0.5, 0.25, -0.125]
+    assert float(np.sum(np.asarray(k[0, 0, :, 0], np.float64))) == 0.0     # the plain sum drops the 1
+    mu = sage_ref.k_channel_mean(k)
+    assert mu[0, 0, 0] == np.float32(1.0 / 3.0)
+    assert mu[0, 0, 1] == np.float32(0.625 / 3.0)
+
+
 def test_int8_worked_examples():
     with open(os.path.join(GOLDEN, "int8_rne_worked.txt")) as f:
         lines = [ln for ln in f if ln.strip() and not ln.startswith("#")]
