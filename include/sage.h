@@ -213,6 +213,25 @@ sage_status sage_attn_fwd_varlen(const sage_varlen_shape* s, const void* q, cons
  * the layout the PV product reads in FP16/BF16 mode. */
 sage_status sage_transpose_v(const sage_shape* s, const void* v, void* v_t, void* stream);
 
+/* Largest workspace sage_attn_fwd_noalloc can use: 32 MiB (for example
+ * B = 1, 16 heads of 4096 tokens at head_dim 128). */
+#define SAGE_NOALLOC_MAX_WORKSPACE_BYTES (32u * 1024u * 1024u)
+
+/* sage_attn_fwd without a caller-supplied workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Arguments are as for sage_attn_fwd; the
+ * caller still passes q, k, v and o. The workspace is a fixed device array of
+ * SAGE_NOALLOC_MAX_WORKSPACE_BYTES inside the library, one per GPU, held until
+ * the process ends; the call allocates and frees nothing (its first call on a
+ * device looks the array's address up once). Errors: SAGE_ERR_WORKSPACE when
+ * sage_workspace_bytes(s, pv_dtype) exceeds that limit, otherwise those of
+ * sage_attn_fwd. Every call on one GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (other streams or threads) race and are not
+ * allowed; calls on one stream are ordered and safe. Each call writes every
+ * part of the array it later reads, so no state carries over between calls. */
+sage_status sage_attn_fwd_noalloc(const sage_shape* s, const void* q, const void* k, const void* v,
+                                  void* o, int32_t is_causal, float sm_scale, int32_t pv_dtype, void* stream);
+
 /* The fused attention kernel alone, from precomputed codes: INT8 QK^T,
  * online softmax, P quantisation and two-level PV (repo card, "How it works";
  * jisaku.com glossary, 概要). For callers that quantise once and reuse K/V

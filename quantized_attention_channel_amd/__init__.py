@@ -9,7 +9,7 @@ Entry points (same names as the C ABI):
   sage_block_sizes, sage_v_codes_stride, sage_workspace_bytes,
   sage_quant_qk, sage_quant_v, sage_transpose_v, sage_attn_fwd,
   sage_attn_fwd_codes, sage_debug_qk_i32, sage_varlen_workspace_bytes,
-  sage_attn_fwd_varlen.
+  sage_attn_fwd_varlen, sage_attn_fwd_noalloc.
 User-facing wrapper:
   sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None,
            pv_dtype="fp8", qk_quant_gran="per_block") -- the call shape the
@@ -60,7 +60,11 @@ _SIGNATURES = {
     "sage_varlen_workspace_bytes": (ctypes.c_size_t, [_c_shape_p, ctypes.c_int32]),
     "sage_attn_fwd_varlen": (ctypes.c_int, [_c_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32,
                                             ctypes.c_float, ctypes.c_int32, _vp, ctypes.c_size_t, _vp]),
+    "sage_attn_fwd_noalloc": (ctypes.c_int, [_c_shape_p, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_float,
+                                             ctypes.c_int32, _vp]),
 }
+# the workspace limit of sage_attn_fwd_noalloc (SAGE_NOALLOC_MAX_WORKSPACE_BYTES in sage.h)
+NOALLOC_MAX_WORKSPACE_BYTES = 32 * 1024 * 1024
 
 
 class SageShape(ctypes.Structure):
@@ -294,6 +298,27 @@ def sage_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, is_causa
     _check(lib.sage_attn_fwd(_ref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(o), int(bool(is_causal)),
                              float(sm_scale), PV_DTYPES[pv_dtype], _ptr(ws), ws.numel(), _stream(dev)),
            "sage_attn_fwd")
+    return o
+
+
+def sage_attn_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, *,
+                          is_causal: bool = False, sm_scale: Optional[float] = None, pv_dtype: str = "fp8",
+                          tensor_layout: str = "HND", qk_gran: str = "per_block") -> torch.Tensor:
+    """sage_attn_fwd with the library's own fixed workspace (no allocation by
+    the call; the caller passes ``out``). Shapes whose workspace exceeds
+    NOALLOC_MAX_WORKSPACE_BYTES raise SageError(SAGE_ERR_WORKSPACE)."""
+    if out is None:
+        raise ValueError("sage_attn_fwd_noalloc needs the caller's output tensor")
+    _check_inputs(q, k, v)
+    s = shape_of(q, k, tensor_layout, qk_gran)
+    if tuple(v.shape) != tuple(k.shape) or v.dtype != q.dtype or k.dtype != q.dtype:
+        raise ValueError("v must have k's shape and all inputs one dtype")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(s.head_dim)
+    o = _out_like(q, out)
+    _check(lib.sage_attn_fwd_noalloc(_ref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(o), int(bool(is_causal)),
+                                     float(sm_scale), PV_DTYPES[pv_dtype], _stream(q.device)),
+           "sage_attn_fwd_noalloc")
     return o
 
 

@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstring>
 #include <initializer_list>
+#include <mutex>
 
 #include "sage.h"
 #include "sage_device.h"
@@ -223,6 +224,113 @@ sage_status from_hip(hipError_t e) { return e == hipSuccess ? SAGE_OK : SAGE_ERR
 
 }  // namespace
 
+// Workspace of sage_attn_fwd_noalloc: a fixed device array, one copy per GPU the
+// library runs on, held until the process ends. Host code never uses its name
+// as an address (on the host it is a stand-in symbol): the device address of
+// each GPU's copy is taken once with hipGetSymbolAddress and kept below.
+static __device__ __align__(256) uint8_t scratch[SAGE_NOALLOC_MAX_WORKSPACE_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, looked up on the first call per device.
+sage_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SAGE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SAGE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SAGE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SAGE_OK;
+}
+
+// The whole forward once the arguments are checked: statistics, quantisation,
+// attention, all writing into `ws` (laid out by layout_for).
+sage_status attn_fwd_launch(const Dims& d, const void* q, const void* k, const void* v, void* o, int32_t is_causal,
+                            float sm_scale, bool fp8, void* workspace, hipStream_t hs) {
+  const Layout L = layout_for(d, fp8);
+  sage::QuantQKArgs qa{};
+  qa.q = q;
+  qa.k = k;
+  qa.qgeo = geom(d, d.Hq, d.Nq);
+  qa.kgeo = geom(d, d.Hkv, d.Nk);
+  qa.B = int(d.B), qa.Hq = int(d.Hq), qa.Hkv = int(d.Hkv), qa.Nq = int(d.Nq), qa.Nk = int(d.Nk), qa.D = int(d.D);
+  qa.bf16 = d.bf16;
+  qa.fine = d.fine;
+  qa.q_codes = at<int8_t>(workspace, L.q_codes);
+  qa.q_scale = at<float>(workspace, L.q_scale);
+  qa.k_codes = at<int8_t>(workspace, L.k_codes);
+  qa.k_scale = at<float>(workspace, L.k_scale);
+  qa.k_mean = at<float>(workspace, L.k_mean);
+  qa.ksum_part = at<double>(workspace, L.ksum);
+  hipError_t e = sage::launch_quant_qk(qa, hs);
+  if (e != hipSuccess) return SAGE_ERR_HIP;
+
+  sage::QuantVArgs va{};
+  va.v = v;
+  va.vgeo = geom(d, d.Hkv, d.Nk);
+  va.B = int(d.B), va.Hkv = int(d.Hkv), va.Nk = int(d.Nk), va.D = int(d.D);
+  va.n_pad = int(round_up(d.Nk, sage::kVPad));
+  va.bf16 = d.bf16;
+  va.fp8 = fp8;
+  va.out = at<void>(workspace, L.vt);
+  va.v_scale = at<float>(workspace, L.v_scale);
+  va.v_inv = at<float>(workspace, L.v_inv);
+  va.vmax_part = at<float>(workspace, L.vmax);
+  e = sage::launch_quant_v(va, hs);
+  if (e != hipSuccess) return SAGE_ERR_HIP;
+
+  sage::AttnArgs aa{};
+  aa.q8 = qa.q_codes;
+  aa.q_scale = qa.q_scale;
+  aa.k8 = qa.k_codes;
+  aa.k_scale = qa.k_scale;
+  aa.vt = va.out;
+  aa.v_scale = va.v_scale;
+  aa.o = o;
+  aa.ogeo = geom(d, d.Hq, d.Nq);
+  aa.B = int(d.B), aa.Hq = int(d.Hq), aa.Hkv = int(d.Hkv), aa.Nq = int(d.Nq), aa.Nk = int(d.Nk), aa.D = int(d.D);
+  aa.n_pad = va.n_pad;
+  aa.nbq = int(cdiv(d.Nq, d.blk_q));
+  aa.nbk = int(cdiv(d.Nk, d.blk_k));
+  aa.scale_log2 = sm_scale * sage::kLog2E;
+  aa.causal = is_causal != 0;
+  aa.bf16 = d.bf16;
+  aa.fp8 = fp8;
+  aa.fine = d.fine;
+  return from_hip(sage::launch_attn(aa, hs));
+}
+
+// Argument checks of the whole forward that do not involve the workspace.
+// SAGE_OK with *noop set means there is nothing to do.
+sage_status attn_fwd_check(const sage_shape* s, const void* q, const void* k, const void* v, void* o,
+                           int32_t is_causal, float sm_scale, int32_t pv_dtype, Dims* d, bool* noop) {
+  *noop = false;
+  sage_status st = check_shape(s, d);
+  if (st != SAGE_OK) return st;
+  if (pv_dtype != SAGE_PV_FP16 && pv_dtype != SAGE_PV_FP8_E4M3) return SAGE_ERR_INVALID_ARGUMENT;
+  if (is_causal != 0 && is_causal != 1) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (d->B == 0 || d->Nq == 0) {
+    *noop = true;
+    return SAGE_OK;
+  }
+  if (d->Nk == 0) return SAGE_ERR_INVALID_ARGUMENT;
+  if (is_causal && d->Nq != d->Nk) return SAGE_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !o) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return SAGE_ERR_INVALID_ARGUMENT;
+  return SAGE_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 sage_status sage_block_sizes(int32_t head_dim, int32_t qk_gran, int32_t* blk_q, int32_t* blk_k, int32_t* bkv) {
@@ -329,75 +437,40 @@ sage_status sage_attn_fwd(const sage_shape* s, const void* q, const void* k, con
                           int32_t is_causal, float sm_scale, int32_t pv_dtype, void* workspace,
                           size_t workspace_bytes, void* stream) {
   Dims d;
-  sage_status st = check_shape(s, &d);
-  if (st != SAGE_OK) return st;
-  if (pv_dtype != SAGE_PV_FP16 && pv_dtype != SAGE_PV_FP8_E4M3) return SAGE_ERR_INVALID_ARGUMENT;
-  if (is_causal != 0 && is_causal != 1) return SAGE_ERR_INVALID_ARGUMENT;
-  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_INVALID_ARGUMENT;
-  if (d.B == 0 || d.Nq == 0) return SAGE_OK;
-  if (d.Nk == 0) return SAGE_ERR_INVALID_ARGUMENT;
-  if (is_causal && d.Nq != d.Nk) return SAGE_ERR_UNSUPPORTED;
-  if (!q || !k || !v || !o || !workspace) return SAGE_ERR_INVALID_ARGUMENT;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(workspace, 256))
-    return SAGE_ERR_INVALID_ARGUMENT;
+  bool noop = false;
+  sage_status st = attn_fwd_check(s, q, k, v, o, is_causal, sm_scale, pv_dtype, &d, &noop);
+  if (st != SAGE_OK || noop) return st;
+  if (!workspace || !aligned(workspace, 256)) return SAGE_ERR_INVALID_ARGUMENT;
   const bool fp8 = pv_dtype == SAGE_PV_FP8_E4M3;
   const Layout L = layout_for(d, fp8);
   if (workspace_bytes < L.total) return SAGE_ERR_WORKSPACE;
   const size_t qbytes = size_t(d.B * d.Hq * d.Nq * d.D) * 2, kvbytes = size_t(d.B * d.Hkv * d.Nk * d.D) * 2;
   if (aliased({{o, qbytes}, {workspace, L.total}}, {{q, qbytes}, {k, kvbytes}, {v, kvbytes}}))
     return SAGE_ERR_INVALID_ARGUMENT;
+  return attn_fwd_launch(d, q, k, v, o, is_causal, sm_scale, fp8, workspace, static_cast<hipStream_t>(stream));
+}
 
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  sage::QuantQKArgs qa{};
-  qa.q = q;
-  qa.k = k;
-  qa.qgeo = geom(d, d.Hq, d.Nq);
-  qa.kgeo = geom(d, d.Hkv, d.Nk);
-  qa.B = int(d.B), qa.Hq = int(d.Hq), qa.Hkv = int(d.Hkv), qa.Nq = int(d.Nq), qa.Nk = int(d.Nk), qa.D = int(d.D);
-  qa.bf16 = d.bf16;
-  qa.fine = d.fine;
-  qa.q_codes = at<int8_t>(workspace, L.q_codes);
-  qa.q_scale = at<float>(workspace, L.q_scale);
-  qa.k_codes = at<int8_t>(workspace, L.k_codes);
-  qa.k_scale = at<float>(workspace, L.k_scale);
-  qa.k_mean = at<float>(workspace, L.k_mean);
-  qa.ksum_part = at<double>(workspace, L.ksum);
-  hipError_t e = sage::launch_quant_qk(qa, hs);
-  if (e != hipSuccess) return SAGE_ERR_HIP;
-
-  sage::QuantVArgs va{};
-  va.v = v;
-  va.vgeo = geom(d, d.Hkv, d.Nk);
-  va.B = int(d.B), va.Hkv = int(d.Hkv), va.Nk = int(d.Nk), va.D = int(d.D);
-  va.n_pad = int(round_up(d.Nk, sage::kVPad));
-  va.bf16 = d.bf16;
-  va.fp8 = fp8;
-  va.out = at<void>(workspace, L.vt);
-  va.v_scale = at<float>(workspace, L.v_scale);
-  va.v_inv = at<float>(workspace, L.v_inv);
-  va.vmax_part = at<float>(workspace, L.vmax);
-  e = sage::launch_quant_v(va, hs);
-  if (e != hipSuccess) return SAGE_ERR_HIP;
-
-  sage::AttnArgs aa{};
-  aa.q8 = qa.q_codes;
-  aa.q_scale = qa.q_scale;
-  aa.k8 = qa.k_codes;
-  aa.k_scale = qa.k_scale;
-  aa.vt = va.out;
-  aa.v_scale = va.v_scale;
-  aa.o = o;
-  aa.ogeo = geom(d, d.Hq, d.Nq);
-  aa.B = int(d.B), aa.Hq = int(d.Hq), aa.Hkv = int(d.Hkv), aa.Nq = int(d.Nq), aa.Nk = int(d.Nk), aa.D = int(d.D);
-  aa.n_pad = va.n_pad;
-  aa.nbq = int(cdiv(d.Nq, d.blk_q));
-  aa.nbk = int(cdiv(d.Nk, d.blk_k));
-  aa.scale_log2 = sm_scale * sage::kLog2E;
-  aa.causal = is_causal != 0;
-  aa.bf16 = d.bf16;
-  aa.fp8 = fp8;
-  aa.fine = d.fine;
-  return from_hip(sage::launch_attn(aa, hs));
+sage_status sage_attn_fwd_noalloc(const sage_shape* s, const void* q, const void* k, const void* v, void* o,
+                                  int32_t is_causal, float sm_scale, int32_t pv_dtype, void* stream) {
+  Dims d;
+  bool noop = false;
+  sage_status st = attn_fwd_check(s, q, k, v, o, is_causal, sm_scale, pv_dtype, &d, &noop);
+  if (st != SAGE_OK || noop) return st;
+  const bool fp8 = pv_dtype == SAGE_PV_FP8_E4M3;
+  const Layout L = layout_for(d, fp8);
+  if (L.total > size_t(SAGE_NOALLOC_MAX_WORKSPACE_BYTES)) return SAGE_ERR_WORKSPACE;
+  const size_t qbytes = size_t(d.B * d.Hq * d.Nq * d.D) * 2, kvbytes = size_t(d.B * d.Hkv * d.Nk * d.D) * 2;
+  if (aliased({{o, qbytes}}, {{q, qbytes}, {k, kvbytes}, {v, kvbytes}})) return SAGE_ERR_INVALID_ARGUMENT;
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != SAGE_OK) return st;
+  if (aliased({{o, qbytes}, {ws, L.total}}, {{q, qbytes}, {k, kvbytes}, {v, kvbytes}}))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  // Every workspace region is written by this call's kernels before any kernel
+  // reads it (codes, scales, K mean, V^T with its zero padding, the reduction
+  // partials), so the array's contents from an earlier call never leak in and
+  // nothing needs clearing.
+  return attn_fwd_launch(d, q, k, v, o, is_causal, sm_scale, fp8, ws, static_cast<hipStream_t>(stream));
 }
 
 size_t sage_varlen_workspace_bytes(const sage_varlen_shape* s, int32_t pv_dtype) {

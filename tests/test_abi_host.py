@@ -230,6 +230,22 @@ def test_other_entry_points_reject_aliased_writes():
     assert sage.lib.sage_debug_qk_i32(huge, FAKE + (1 << 44), FAKE + (1 << 45), FAKE, None) == bad
 
 
+@FAKE_ADDRESSES
+def test_noalloc_entry_point_checks_before_any_hip_call():
+    """The allocation-free forward refuses shapes whose workspace exceeds its
+    fixed array, and bad arguments, before it touches the device."""
+    big = _shape(B=1, Hq=32, Hkv=32, Nq=8192, Nk=8192, d=128)
+    assert sage.lib.sage_workspace_bytes(ctypes.byref(big), 1) > sage.NOALLOC_MAX_WORKSPACE_BYTES
+    assert sage.lib.sage_attn_fwd_noalloc(ctypes.byref(big), FAKE, FAKE + G, FAKE + 2 * G, FAKE + 3 * G, 0, 0.1, 1,
+                                          None) == sage.SAGE_ERR_WORKSPACE
+    sp = ctypes.byref(_shape())
+    bad = sage.SAGE_ERR_INVALID_ARGUMENT
+    assert sage.lib.sage_attn_fwd_noalloc(sp, None, FAKE + G, FAKE + 2 * G, FAKE + 3 * G, 0, 0.1, 1, None) == bad
+    assert sage.lib.sage_attn_fwd_noalloc(sp, FAKE, FAKE + G, FAKE + 2 * G, FAKE + 8, 0, 0.1, 1, None) == bad
+    assert sage.lib.sage_attn_fwd_noalloc(sp, FAKE, FAKE + G, FAKE + 2 * G, FAKE + 3 * G, 0, -1.0, 1, None) == bad
+    assert sage.lib.sage_attn_fwd_noalloc(sp, FAKE, FAKE + G, FAKE + 2 * G, FAKE, 0, 0.1, 1, None) == bad   # o on q
+
+
 def test_python_wrapper_rejects_unsupported_sdpa_arguments():
     import torch
     q = torch.zeros(1, 1, 4, 64, dtype=torch.float16)
