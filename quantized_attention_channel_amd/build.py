@@ -21,7 +21,7 @@ SOURCES = ["sage_abi.hip", "quant_kernels.hip", "attn_kernel.hip"]
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
-    "-Wall", "-Wno-unused-function",
+    "-Wall", "-Wno-unused-function", "-Werror",
     # packed fp32 VALU ops are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,

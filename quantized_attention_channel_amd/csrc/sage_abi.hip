@@ -669,7 +669,12 @@ sage_status sage_debug_qk_i32(const sage_shape* s, const int8_t* q_codes, const 
 }
 
 const char* sage_status_string(sage_status st) {
-  switch (st) {
+  // A C caller may pass any int; read its bits as one, since a value outside
+  // the enumerators is not a valid value of the C++ enum type.
+  int32_t v;
+  static_assert(sizeof(st) == sizeof(v), "sage_status is passed as an int");
+  std::memcpy(&v, &st, sizeof v);
+  switch (v) {
     case SAGE_OK: return "SAGE_OK";
     case SAGE_ERR_INVALID_ARGUMENT: return "SAGE_ERR_INVALID_ARGUMENT: invalid pointer, size, alignment or enum";
     case SAGE_ERR_UNSUPPORTED: return "SAGE_ERR_UNSUPPORTED: head_dim must be 64 or 128; causal needs seq_q == seq_k";
