@@ -207,6 +207,38 @@ sage_status sage_attn_fwd_varlen(const sage_varlen_shape* s, const void* q, cons
                                  int32_t is_causal, float sm_scale, int32_t pv_dtype, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/* Workspace bytes sage_quant_varlen needs for `s` (the span table of the
+ * sequences and the reduction partials). 0 for an invalid shape. */
+size_t sage_quant_varlen_workspace_bytes(const sage_varlen_shape* s);
+
+/* The quantisation stages of sage_attn_fwd_varlen on their own, per sequence
+ * of a packed batch (heatdrop.ai review, "Key highlights": variable sequence
+ * lengths within a batch; jisaku.com glossary, 概要, and the repo card's "How it
+ * works" for the stages). Every sequence is quantised as a batch of one: its
+ * own K channel mean, Q/K INT8 blocks from its first token, its own V channel
+ * scales. Inputs and cu_seqlens as for sage_attn_fwd_varlen; outputs:
+ *   q_codes    [Hq][total_q][d] int8     (sequence b: rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1)
+ *   q_scale    [B][Hq][nbq] fp32         nbq = max(1, ceil(max_seqlen_q / BLK_Q)); sequence b writes
+ *                                        its first ceil(nq_b / BLK_Q) entries
+ *   k_codes    [Hkv][total_k][d] int8
+ *   k_scale    [B][Hkv][nbk] fp32        nbk = max(1, ceil(max_seqlen_k / BLK_K)), likewise
+ *   k_mean     [B][Hkv][d] fp32          0 for a sequence without keys
+ *   v_prepared [Hkv][d][n_pad]           n_pad = 128 * ceil((total_k + 127 B) / 128), at least 128;
+ *                                        FP8: e4m3 codes, FP16: the 16-bit values. Sequence b's keys
+ *                                        are the columns p_b .. p_b + nk_b - 1, p_b = the sum over the
+ *                                        earlier sequences of nk rounded up to 128; the columns up to
+ *                                        p_b + nk_b rounded up to 128 hold zeros; others are not written
+ *   v_scale    [B][Hkv][d] fp32          FP8 only: a_v / 448 per sequence and channel
+ * pv_dtype selects the V stage. With total_q == 0 the Q outputs are not
+ * written (q, q_codes, q_scale may be NULL); with total_k == 0 neither are the
+ * K and V outputs (k, v and their outputs may be NULL). Alignment: tensors and
+ * codes 16 bytes, scales, means and cu_seqlens 4 bytes, workspace 256 bytes. */
+sage_status sage_quant_varlen(const sage_varlen_shape* s, int32_t pv_dtype, const void* q, const void* k,
+                              const void* v, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int8_t* q_codes, float* q_scale, int8_t* k_codes, float* k_scale, float* k_mean,
+                              void* v_prepared, float* v_scale, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /* FP16-PV preparation of V (repo card, "How it works": FP16 for PV): the
  * 16-bit values transposed to
  *   v_t [B,Hkv,d,sage_v_codes_stride(Nk)] (keys contiguous per channel, padding keys 0),

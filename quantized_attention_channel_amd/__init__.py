@@ -9,7 +9,8 @@ Entry points (same names as the C ABI):
   sage_block_sizes, sage_v_codes_stride, sage_workspace_bytes,
   sage_quant_qk, sage_quant_v, sage_transpose_v, sage_attn_fwd,
   sage_attn_fwd_codes, sage_debug_qk_i32, sage_varlen_workspace_bytes,
-  sage_attn_fwd_varlen, sage_attn_fwd_noalloc.
+  sage_attn_fwd_varlen, sage_quant_varlen, sage_quant_varlen_workspace_bytes,
+  sage_attn_fwd_noalloc.
 User-facing wrapper:
   sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None,
            pv_dtype="fp8", qk_quant_gran="per_block") -- the call shape the
@@ -62,6 +63,9 @@ _SIGNATURES = {
                                             ctypes.c_float, ctypes.c_int32, _vp, ctypes.c_size_t, _vp]),
     "sage_attn_fwd_noalloc": (ctypes.c_int, [_c_shape_p, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_float,
                                              ctypes.c_int32, _vp]),
+    "sage_quant_varlen_workspace_bytes": (ctypes.c_size_t, [_c_shape_p]),
+    "sage_quant_varlen": (ctypes.c_int, [_c_shape_p, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                         _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
 }
 # the workspace limit of sage_attn_fwd_noalloc (SAGE_NOALLOC_MAX_WORKSPACE_BYTES in sage.h)
 NOALLOC_MAX_WORKSPACE_BYTES = 32 * 1024 * 1024
@@ -364,6 +368,51 @@ def sage_attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_s
                                     _ptr(o), int(bool(is_causal)), float(sm_scale), PV_DTYPES[pv_dtype], _ptr(ws),
                                     ws.numel(), _stream(dev)), "sage_attn_fwd_varlen")
     return o
+
+
+def varlen_v_codes_stride(total_k: int, batch: int) -> int:
+    """Columns of the packed V operand rows: every sequence's keys rounded up to 128."""
+    return max(128, -(-(total_k + 127 * batch) // 128) * 128)
+
+
+def sage_quant_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                      cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int, *, pv_dtype: str = "fp8",
+                      qk_gran: str = "per_block") -> dict:
+    """The quantisation stages of a packed batch, per sequence (see sage.h):
+    q_codes [Hq,total_q,d], q_scale [B,Hq,nbq], k_codes [Hkv,total_k,d],
+    k_scale [B,Hkv,nbk], k_mean [B,Hkv,d], v_codes (FP8) or v_t (FP16)
+    [Hkv,d,n_pad] and v_scale [B,Hkv,d] (FP8)."""
+    _check_inputs(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    if cu_seqlens_k.numel() != cu_seqlens_q.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    if tuple(v.shape) != tuple(k.shape) or v.dtype != q.dtype or k.dtype != q.dtype:
+        raise ValueError("v must have k's shape and all inputs one dtype")
+    s = varlen_shape_of(q, k, cu_seqlens_q, max_seqlen_q, max_seqlen_k, qk_gran)
+    blk_q, blk_k, _ = sage_block_sizes(s.head_dim, qk_gran)
+    B, dev, d = s.batch, q.device, s.head_dim
+    nbq = max(1, -(-int(max_seqlen_q) // blk_q))
+    nbk = max(1, -(-int(max_seqlen_k) // blk_k))
+    npad = varlen_v_codes_stride(s.total_k, B)
+    out = {"q_codes": torch.zeros((s.heads_q, s.total_q, d), dtype=torch.int8, device=dev),
+           "q_scale": torch.zeros((B, s.heads_q, nbq), dtype=torch.float32, device=dev),
+           "k_codes": torch.zeros((s.heads_kv, s.total_k, d), dtype=torch.int8, device=dev),
+           "k_scale": torch.zeros((B, s.heads_kv, nbk), dtype=torch.float32, device=dev),
+           "k_mean": torch.zeros((B, s.heads_kv, d), dtype=torch.float32, device=dev)}
+    if PV_DTYPES[pv_dtype] == 1:
+        out["v_codes"] = torch.zeros((s.heads_kv, d, npad), dtype=torch.uint8, device=dev)
+        out["v_scale"] = torch.zeros((B, s.heads_kv, d), dtype=torch.float32, device=dev)
+        vp, vs = out["v_codes"], out["v_scale"]
+    else:
+        out["v_t"] = torch.zeros((s.heads_kv, d, npad), dtype=q.dtype, device=dev)
+        vp, vs = out["v_t"], None
+    ws = _workspace_for(None, int(lib.sage_quant_varlen_workspace_bytes(_ref(s))), dev)
+    _check(lib.sage_quant_varlen(_ref(s), PV_DTYPES[pv_dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q),
+                                 _ptr(cu_seqlens_k), _ptr(out["q_codes"]), _ptr(out["q_scale"]),
+                                 _ptr(out["k_codes"]), _ptr(out["k_scale"]), _ptr(out["k_mean"]), _ptr(vp),
+                                 _ptr(vs), _ptr(ws), ws.numel(), _stream(dev)), "sage_quant_varlen")
+    return out
 
 
 def sage_debug_qk_i32(q_codes: torch.Tensor, k_codes: torch.Tensor) -> torch.Tensor:

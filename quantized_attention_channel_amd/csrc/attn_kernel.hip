@@ -691,7 +691,7 @@ __device__ __forceinline__ void attn_fwd_body(AttnArgs a) {
         float x[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[i] = st.o[cb][4 * j + i] * inv_l;
-        if (FP8) {
+        if (FP8 && l > 0.0f) {   // (a row without keys is exactly zero; its V scales may be unset)
           const f32x4 sv4 = *reinterpret_cast<const f32x4*>(vs + ch);
 #pragma unroll
           for (int i = 0; i < 4; ++i) x[i] *= sv4[i];

@@ -222,6 +222,96 @@ P* at(void* base, size_t off) { return reinterpret_cast<P*>(static_cast<uint8_t*
 
 sage_status from_hip(hipError_t e) { return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP; }
 
+// Buffers of the quantisation stages of a packed batch.
+struct VarlenBufs {
+  sage::SeqSpan* spans;
+  int32_t* qp_owner;
+  int8_t* q_codes;
+  float* q_scale;
+  int8_t* k_codes;
+  float* k_scale;
+  float* k_mean;
+  void* vt;
+  float* v_scale;
+  float* v_inv;
+  double* ksum;
+  float* vmax;
+};
+
+// Workspace of sage_quant_varlen: the span table and work list, 448/a_v, and
+// the reduction partials (everything else goes to the caller's buffers).
+struct VQLayout {
+  size_t spans, qp_owner, v_inv, ksum, vmax, total;
+};
+
+VQLayout varlen_quant_layout_for(const VDims& d) {
+  VQLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  const int64_t chunks = cdiv(d.max_k, kStatChunk);
+  L.spans = take(size_t(d.B) * sizeof(sage::SeqSpan));
+  L.qp_owner = take(size_t(sage::varlen_qpair_bound(d.total_q, d.B)) * 4);
+  L.v_inv = take(size_t(d.B * d.Hkv * d.D) * 4);
+  L.ksum = take(size_t(d.B * d.Hkv * chunks * d.D) * 8);
+  L.vmax = take(size_t(d.B * d.Hkv * chunks * d.D) * 4);
+  L.total = off;
+  return L;
+}
+
+// The plan kernel (span table from the device offsets) and the quantisation
+// stages of a packed batch into `b`.
+sage_status varlen_quant_launch(const VDims& d, bool fp8, const void* q, const void* k, const void* v,
+                                const int32_t* cu_q, const int32_t* cu_k, const VarlenBufs& b, bool run_q,
+                                bool run_kv, hipStream_t hs) {
+  const int n_owner = int(sage::varlen_qpair_bound(d.total_q, d.B));
+  hipError_t e = sage::launch_varlen_plan(cu_q, cu_k, int(d.B), int(d.total_q), int(d.total_k), int(d.max_q),
+                                          int(d.max_k), int(d.n_pad), b.spans, b.qp_owner, n_owner, hs);
+  if (e != hipSuccess) return SAGE_ERR_HIP;
+  sage::QuantQKArgs qa{};
+  qa.q = q;
+  qa.k = k;
+  qa.qgeo = packed_geom(d.Hq, d.D);
+  qa.kgeo = packed_geom(d.Hkv, d.D);
+  qa.B = int(d.B), qa.Hq = int(d.Hq), qa.Hkv = int(d.Hkv), qa.Nq = int(d.max_q), qa.Nk = int(d.max_k);
+  qa.D = int(d.D);
+  qa.bf16 = d.bf16;
+  qa.fine = d.fine;
+  qa.q_codes = b.q_codes;
+  qa.q_scale = b.q_scale;
+  qa.k_codes = b.k_codes;
+  qa.k_scale = b.k_scale;
+  qa.k_mean = b.k_mean;
+  qa.ksum_part = b.ksum;
+  qa.seq = b.spans;
+  qa.total_q = int(d.total_q);
+  qa.total_k = int(d.total_k);
+  if (!run_q) qa.Nq = 0;
+  if (!run_kv) qa.Nk = 0;
+  e = sage::launch_quant_qk(qa, hs);
+  if (e != hipSuccess) return SAGE_ERR_HIP;
+  if (run_kv) {
+    sage::QuantVArgs va{};
+    va.v = v;
+    va.vgeo = packed_geom(d.Hkv, d.D);
+    va.B = int(d.B), va.Hkv = int(d.Hkv), va.Nk = int(d.max_k), va.D = int(d.D);
+    va.n_pad = int(d.n_pad);
+    va.bf16 = d.bf16;
+    va.fp8 = fp8;
+    va.out = b.vt;
+    va.v_scale = b.v_scale;
+    va.v_inv = b.v_inv;
+    va.vmax_part = b.vmax;
+    va.seq = b.spans;
+    e = sage::launch_quant_v(va, hs);
+    if (e != hipSuccess) return SAGE_ERR_HIP;
+  }
+  return SAGE_OK;
+}
+
 }  // namespace
 
 // Workspace of sage_attn_fwd_noalloc: a fixed device array, one copy per GPU the
@@ -505,58 +595,29 @@ sage_status sage_attn_fwd_varlen(const sage_varlen_shape* s, const void* q, cons
     return SAGE_ERR_INVALID_ARGUMENT;
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  sage::SeqSpan* spans = at<sage::SeqSpan>(workspace, L.spans);
-  int32_t* qp_owner = at<int32_t>(workspace, L.qp_owner);
-  const int n_owner = int(sage::varlen_qpair_bound(d.total_q, d.B));
-  hipError_t e = sage::launch_varlen_plan(cu_seqlens_q, cu_seqlens_k, int(d.B), int(d.total_q), int(d.total_k),
-                                          int(d.max_q), int(d.max_k), int(d.n_pad), spans, qp_owner, n_owner, hs);
-  if (e != hipSuccess) return SAGE_ERR_HIP;
-
-  sage::QuantQKArgs qa{};
-  qa.q = q;
-  qa.k = k;
-  qa.qgeo = packed_geom(d.Hq, d.D);
-  qa.kgeo = packed_geom(d.Hkv, d.D);
-  qa.B = int(d.B), qa.Hq = int(d.Hq), qa.Hkv = int(d.Hkv), qa.Nq = int(d.max_q), qa.Nk = int(d.max_k);
-  qa.D = int(d.D);
-  qa.bf16 = d.bf16;
-  qa.fine = d.fine;
-  qa.q_codes = at<int8_t>(workspace, L.q_codes);
-  qa.q_scale = at<float>(workspace, L.q_scale);
-  qa.k_codes = at<int8_t>(workspace, L.k_codes);
-  qa.k_scale = at<float>(workspace, L.k_scale);
-  qa.k_mean = at<float>(workspace, L.k_mean);
-  qa.ksum_part = at<double>(workspace, L.ksum);
-  qa.seq = spans;
-  qa.total_q = int(d.total_q);
-  qa.total_k = int(d.total_k);
-  e = sage::launch_quant_qk(qa, hs);
-  if (e != hipSuccess) return SAGE_ERR_HIP;
-
-  sage::QuantVArgs va{};
-  va.v = v;
-  va.vgeo = packed_geom(d.Hkv, d.D);
-  va.B = int(d.B), va.Hkv = int(d.Hkv), va.Nk = int(d.max_k), va.D = int(d.D);
-  va.n_pad = int(d.n_pad);
-  va.bf16 = d.bf16;
-  va.fp8 = fp8;
-  va.out = at<void>(workspace, L.vt);
-  va.v_scale = at<float>(workspace, L.v_scale);
-  va.v_inv = at<float>(workspace, L.v_inv);
-  va.vmax_part = at<float>(workspace, L.vmax);
-  va.seq = spans;
-  if (d.max_k > 0) {
-    e = sage::launch_quant_v(va, hs);
-    if (e != hipSuccess) return SAGE_ERR_HIP;
-  }
+  VarlenBufs bufs{};
+  bufs.spans = at<sage::SeqSpan>(workspace, L.spans);
+  bufs.qp_owner = at<int32_t>(workspace, L.qp_owner);
+  bufs.q_codes = at<int8_t>(workspace, L.q_codes);
+  bufs.q_scale = at<float>(workspace, L.q_scale);
+  bufs.k_codes = at<int8_t>(workspace, L.k_codes);
+  bufs.k_scale = at<float>(workspace, L.k_scale);
+  bufs.k_mean = at<float>(workspace, L.k_mean);
+  bufs.vt = at<void>(workspace, L.vt);
+  bufs.v_scale = at<float>(workspace, L.v_scale);
+  bufs.v_inv = at<float>(workspace, L.v_inv);
+  bufs.ksum = at<double>(workspace, L.ksum);
+  bufs.vmax = at<float>(workspace, L.vmax);
+  st = varlen_quant_launch(d, fp8, q, k, v, cu_seqlens_q, cu_seqlens_k, bufs, true, d.max_k > 0, hs);
+  if (st != SAGE_OK) return st;
 
   sage::AttnArgs aa{};
-  aa.q8 = qa.q_codes;
-  aa.q_scale = qa.q_scale;
-  aa.k8 = qa.k_codes;
-  aa.k_scale = qa.k_scale;
-  aa.vt = va.out;
-  aa.v_scale = va.v_scale;
+  aa.q8 = bufs.q_codes;
+  aa.q_scale = bufs.q_scale;
+  aa.k8 = bufs.k_codes;
+  aa.k_scale = bufs.k_scale;
+  aa.vt = bufs.vt;
+  aa.v_scale = bufs.v_scale;
   aa.o = o;
   aa.ogeo = packed_geom(d.Hq, d.D);
   aa.B = int(d.B), aa.Hq = int(d.Hq), aa.Hkv = int(d.Hkv), aa.Nq = int(d.max_q), aa.Nk = int(d.max_k);
@@ -569,12 +630,67 @@ sage_status sage_attn_fwd_varlen(const sage_varlen_shape* s, const void* q, cons
   aa.bf16 = d.bf16;
   aa.fp8 = fp8;
   aa.fine = d.fine;
-  aa.seq = spans;
+  aa.seq = bufs.spans;
   aa.total_q = int(d.total_q);
   aa.total_k = int(d.total_k);
-  aa.qp_owner = qp_owner;
-  aa.n_owner = n_owner;
+  aa.qp_owner = bufs.qp_owner;
+  aa.n_owner = int(sage::varlen_qpair_bound(d.total_q, d.B));
   return from_hip(sage::launch_attn(aa, hs));
+}
+
+size_t sage_quant_varlen_workspace_bytes(const sage_varlen_shape* s) {
+  VDims d;
+  if (check_varlen_shape(s, &d) != SAGE_OK) return 0;
+  return varlen_quant_layout_for(d).total;
+}
+
+sage_status sage_quant_varlen(const sage_varlen_shape* s, int32_t pv_dtype, const void* q, const void* k,
+                              const void* v, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int8_t* q_codes, float* q_scale, int8_t* k_codes, float* k_scale, float* k_mean,
+                              void* v_prepared, float* v_scale, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  VDims d;
+  sage_status st = check_varlen_shape(s, &d);
+  if (st != SAGE_OK) return st;
+  if (pv_dtype != SAGE_PV_FP16 && pv_dtype != SAGE_PV_FP8_E4M3) return SAGE_ERR_INVALID_ARGUMENT;
+  if (d.B == 0) return SAGE_OK;
+  const bool fp8 = pv_dtype == SAGE_PV_FP8_E4M3;
+  const bool has_q = d.total_q > 0 && d.max_q > 0, has_k = d.total_k > 0 && d.max_k > 0;
+  if (!cu_seqlens_q || !cu_seqlens_k || !workspace) return SAGE_ERR_INVALID_ARGUMENT;
+  if (has_q && (!q || !q_codes || !q_scale)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (has_k && (!k || !v || !k_codes || !k_scale || !k_mean || !v_prepared || (fp8 && !v_scale)))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  if (!aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4) || !aligned(workspace, 256)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (has_q && (!aligned(q, 16) || !aligned(q_codes, 16) || !aligned(q_scale, 4))) return SAGE_ERR_INVALID_ARGUMENT;
+  if (has_k && (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_codes, 16) || !aligned(k_scale, 4) ||
+                !aligned(k_mean, 4) || !aligned(v_prepared, 16) || (fp8 && !aligned(v_scale, 4))))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  const VQLayout L = varlen_quant_layout_for(d);
+  if (workspace_bytes < L.total) return SAGE_ERR_WORKSPACE;
+  const int64_t nbq = std::max<int64_t>(1, cdiv(d.max_q, d.blk_q)), nbk = std::max<int64_t>(1, cdiv(d.max_k, d.blk_k));
+  const size_t nq = has_q ? size_t(d.Hq * d.total_q * d.D) : 0, nk = has_k ? size_t(d.Hkv * d.total_k * d.D) : 0;
+  const size_t cubytes = size_t(d.B + 1) * 4;
+  if (aliased({{q_codes, nq}, {q_scale, has_q ? size_t(d.B * d.Hq * nbq) * 4 : 0}, {k_codes, nk},
+               {k_scale, has_k ? size_t(d.B * d.Hkv * nbk) * 4 : 0}, {k_mean, has_k ? size_t(d.B * d.Hkv * d.D) * 4 : 0},
+               {v_prepared, has_k ? size_t(d.Hkv * d.D * d.n_pad) * (fp8 ? 1 : 2) : 0},
+               {fp8 ? v_scale : nullptr, has_k ? size_t(d.B * d.Hkv * d.D) * 4 : 0}, {workspace, L.total}},
+              {{q, nq * 2}, {k, nk * 2}, {v, nk * 2}, {cu_seqlens_q, cubytes}, {cu_seqlens_k, cubytes}}))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  VarlenBufs bufs{};
+  bufs.spans = at<sage::SeqSpan>(workspace, L.spans);
+  bufs.qp_owner = at<int32_t>(workspace, L.qp_owner);
+  bufs.q_codes = q_codes;
+  bufs.q_scale = q_scale;
+  bufs.k_codes = k_codes;
+  bufs.k_scale = k_scale;
+  bufs.k_mean = k_mean;
+  bufs.vt = v_prepared;
+  bufs.v_scale = v_scale;
+  bufs.v_inv = at<float>(workspace, L.v_inv);
+  bufs.ksum = at<double>(workspace, L.ksum);
+  bufs.vmax = at<float>(workspace, L.vmax);
+  return varlen_quant_launch(d, fp8, q, k, v, cu_seqlens_q, cu_seqlens_k, bufs, has_q, has_k,
+                             static_cast<hipStream_t>(stream));
 }
 
 sage_status sage_transpose_v(const sage_shape* s, const void* v, void* v_t, void* stream) {

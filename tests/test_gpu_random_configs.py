@@ -109,3 +109,12 @@ def test_random_varlen_config(i):
     cc, r, ce = cos(got, ref), rel_l1(got, ref), cos(got, ex)
     say(f"   cos={cc:.7f} rel_l1={r:.2e} cos_exact={ce:.6f}")
     assert cc >= COS_ORACLE and r <= RL1_ORACLE and ce >= COS_EXACT
+
+
+@pytest.mark.parametrize("i", range(len(VARLEN)))
+def test_random_varlen_quant_stages(i):
+    """The same 24 packed mixes: every sequence's integer stages bit for bit."""
+    from tests.test_gpu_varlen import check_varlen_quant
+    w, gran = VARLEN[i]
+    say("random varlen quant stages", i, w.lens_q, w.lens_k, w.Hq, w.Hkv, w.d, w.dtype, w.pv, gran)
+    check_varlen_quant(w, gran)

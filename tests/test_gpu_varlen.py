@@ -168,3 +168,57 @@ def test_varlen_longest_sequence():
         c, r, ce = cos(g, ref), rel_l1(g, ref), cos(g, ex)
         say(f"   seq {b}: cos={c:.7f} rel_l1={r:.2e} cos_exact={ce:.6f}")
         assert c >= COS_ORACLE and r <= RL1_ORACLE and ce >= COS_EXACT
+
+
+# ------------------------------------------------------------------ integer stages per sequence, bit for bit
+def check_varlen_quant(w, gran):
+    """sage_quant_varlen against the oracle, sequence by sequence: K mean, Q/K
+    codes and scales, V e4m3 codes (with their zero padding) and scales, or the
+    transposed 16-bit V in FP16 mode, all bit for bit [R21]."""
+    q, k, v, cq, ck = W.generate_varlen(w)
+    got = sage.sage_quant_varlen(q.cuda(), k.cuda(), v.cuda(), cq.cuda(), ck.cuda(), max(w.lens_q), max(w.lens_k),
+                                 pv_dtype=w.pv, qk_gran=gran)
+    torch.cuda.synchronize()
+    got = {n: t.cpu() for n, t in got.items()}
+    bq, bk = GRAN_BLK[gran]
+    qn, kn, vn = (t.float().numpy() for t in (q, k, v))
+    p = 0                                              # first V column of the sequence
+    for b in range(w.B):
+        q0, q1, k0, k1 = int(cq[b]), int(cq[b + 1]), int(ck[b]), int(ck[b + 1])
+        nq, nk = q1 - q0, k1 - k0
+        if nq:
+            ref = sage_ref.quant_int8_blocks(np.ascontiguousarray(qn[q0:q1].transpose(1, 0, 2))[None], bq)
+            assert np.array_equal(got["q_codes"][:, q0:q1].numpy(), ref[0][0]), ("q codes", b)
+            assert np.array_equal(got["q_scale"][b, :, :ref[1].shape[2]].numpy(), ref[1][0]), ("q scale", b)
+        if nk:
+            kh = np.ascontiguousarray(kn[k0:k1].transpose(1, 0, 2))[None]
+            ref = sage_ref.quant_qk(np.zeros_like(kh[:, :, :1]), kh, blk_q=bq, blk_k=bk)
+            assert np.array_equal(got["k_mean"][b].numpy(), ref["k_mean"][0]), ("k mean", b)
+            assert np.array_equal(got["k_codes"][:, k0:k1].numpy(), ref["k8"][0]), ("k codes", b)
+            assert np.array_equal(got["k_scale"][b, :, :ref["k_scale"].shape[2]].numpy(), ref["k_scale"][0]), b
+            vh = np.ascontiguousarray(vn[k0:k1].transpose(1, 0, 2))[None]
+            pad = -(-nk // 128) * 128
+            if w.pv == "fp8":
+                c, s = sage_ref.quant_v_fp8(vh)
+                assert np.array_equal(got["v_codes"][:, :, p:p + nk].numpy(), c[0]), ("v codes", b)
+                assert not got["v_codes"][:, :, p + nk:p + pad].numpy().any(), ("v padding", b)
+                assert np.array_equal(got["v_scale"][b].numpy(), s[0]), ("v scale", b)
+            else:
+                want = v[k0:k1].transpose(0, 1).transpose(1, 2)            # [Hkv, d, nk], the input bits
+                assert torch.equal(got["v_t"][:, :, p:p + nk], want), ("v transposed", b)
+                assert not got["v_t"][:, :, p + nk:p + pad].float().abs().sum(), ("v padding", b)
+            p += pad
+        else:
+            assert not got["k_mean"][b].numpy().any(), ("k mean of a sequence without keys", b)
+
+
+@pytest.mark.parametrize("w,gran", CASES, ids=[f"{w.name}-{g}" for w, g in CASES])
+def test_varlen_quant_stages_bit_exact(w, gran):
+    say("varlen quant stages", w.name, gran)
+    check_varlen_quant(w, gran)
+
+
+def test_varlen_quant_stages_serving_mix():
+    say("varlen quant stages, serving mix")
+    check_varlen_quant(W.VARLEN_PREFILL, "per_block")
+    check_varlen_quant(W.VARLEN_PREFILL, "per_thread")
