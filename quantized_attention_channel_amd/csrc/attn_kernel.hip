@@ -121,6 +121,18 @@ struct TileStage {
                                               16, koff, 0, 0, 0);
     }
   }
+  static __device__ __forceinline__ void issue_k_pass(const int8_t* kbase, uint32_t kbytes, uint32_t koff, int wave,
+                                                      int k0, int8_t* sk, int i) {
+    const uint32_t start = (uint32_t)k0 * D + i * kPass;
+    const auto rk = make_rsrc(kbase + start, kbytes > start ? kbytes - start : 0u);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(sk + (i * NW + wave) * 1024),
+                                            16, koff, 0, 0, 0);
+  }
+  static __device__ __forceinline__ void issue_v_pass(__amdgpu_buffer_rsrc_t rv, uint32_t voff, int wave, int k0,
+                                                      int n_pad, uint8_t* sv, int i) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(sv + (i * NW + wave) * 1024),
+                                            16, voff, (k0 + i * kVRowsPerPass * n_pad) * kEb, 0, 0);
+  }
   // rv covers this head's V^T rows [D][n_pad]
   static __device__ __forceinline__ void issue_v(__amdgpu_buffer_rsrc_t rv, uint32_t voff, int wave, int k0,
                                                  int n_pad, uint8_t* sv) {
@@ -339,8 +351,13 @@ __device__ __forceinline__ void rescale_o(float alpha, RowState<D>& st) {
   }
 }
 
-template <int D, bool FP8, typename T>
-__device__ __forceinline__ void pv_phase(const uint8_t* sv, int lane, const PTile<FP8, T>& pt, RowState<D>& st) {
+struct NoHook {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
+template <int D, bool FP8, typename T, typename Hook = NoHook>
+__device__ __forceinline__ void pv_phase(const uint8_t* sv, int lane, const PTile<FP8, T>& pt, RowState<D>& st,
+                                         const Hook& hook = Hook{}) {
   constexpr int NT = D / 32;
   const int g = lane >> 5, n = lane & 31;
   const float alpha = pt.alpha;
@@ -373,7 +390,10 @@ __device__ __forceinline__ void pv_phase(const uint8_t* sv, int lane, const PTil
     for (int cb = 0; cb < NT; ++cb) {
       if (cb + 1 < NT) load_v(cb + 1, va[cb + 1]);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) st.o[cb] = mfma_fp8(va[cb][u], pt.pk[u], st.o[cb]);
+      for (int u = 0; u < 2; ++u) {
+        st.o[cb] = mfma_fp8(va[cb][u], pt.pk[u], st.o[cb]);
+        hook(2 * cb + u);
+      }
     }
   } else {
     using H8 = Half8<T>;
@@ -387,6 +407,7 @@ __device__ __forceinline__ void pv_phase(const uint8_t* sv, int lane, const PTil
         // keys 32*(u/2) + 16g + 8*(u%2) + 0..7 -> 16-byte chunk 4*(u/2) + 2g + (u%2)
         const i32x4 raw = lds16(sv + v_lds_off<false>(row, 4 * (u >> 1) + 2 * g + (u & 1)));
         st.o[cb] = mfma_half(__builtin_bit_cast(H8, raw), pt.ph[u], st.o[cb]);
+        hook(2 * kBlocks * cb + u);
       }
     }
   }
@@ -407,10 +428,10 @@ __device__ __forceinline__ void pv_phase(const uint8_t* sv, int lane, const PTil
 //
 // Global phase p: group 0 runs X(t) at p = 2t and Y(t) at p = 2t + 1; group 1
 // runs one phase later. X(t) = PV(t-1) + QK^T(t), Y(t) = softmax(t). K(t) is
-// read in phases 2t and 2t+1, V(t-1) in the same two phases. In phase 2t
-// group 0 issues the loads of K(t+1) and V(t) into the buffers that K(t-1) and
-// V(t-2) left (after its matrix work in the steady pairs); they must land by
-// the end of phase 2t+1.
+// read in phases 2t and 2t+1, V(t-1) in the same two phases. Group 0 issues
+// the load of K(t+1) in phase 2t (into the buffer K(t-1) left), group 1 the
+// load of V(t) in phase 2t+1 (into the buffer V(t-2) left), each during its
+// matrix phase; both must land by the end of phase 2t+1.
 constexpr int kWaves = 8;
 
 __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
@@ -544,33 +565,66 @@ __device__ __forceinline__ void attn_fwd_body(AttnArgs a) {
   for (int e = 0; e < 16; ++e) qk_init[e] = FP8 ? kScoreOffset : 0;
   if constexpr (FP8) pin(qk_init);
 
-  // Phase pair t = global phases 2t and 2t+1, P = t & 1. In its first phase
-  // group 0 issues the loads of K(t+1) and V(t) (into the buffers K(t-1) and
-  // V(t-2) left); the pair ends with their wait, and a plain barrier splits it.
-  auto loads = [&](auto par, int t) __attribute__((always_inline)) {
+  // Phase pair t = global phases 2t and 2t+1, P = t & 1. The tile loads are
+  // split between the groups, each issuing its share while its own matrix
+  // work runs: group 0 loads K(t+1) in phase 2t (into the buffer K(t-1)
+  // left), group 1 loads V(t) in phase 2t+1 (into the buffer V(t-2) left).
+  // Both land by the wait that ends the pair. A load instruction holds its
+  // wave until the address unit takes it (about one matrix instruction's
+  // time per kilobyte and wave when four waves load together), so one group
+  // carrying all of them lengthened its matrix phase past the other group's
+  // softmax phase; split, each matrix phase takes half and the two phases of
+  // a pair balance.
+  auto loads_k = [&](auto par, int t) __attribute__((always_inline)) {
     constexpr int P = decltype(par)::value;
     if (t + 1 < n_wg)
       StageG::issue_k(kbase, kbytes, koffg, wv & 3, (t + 1) * kBkv, reinterpret_cast<int8_t*>(smem + (1 - P) * kKBytes));
+  };
+  auto loads_v = [&](auto par, int t) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;
     if (t < n_wg) StageG::issue_v(rv, voffg, wv & 3, t * kBkv, a.n_pad, smem + 2 * kKBytes + P * kVBytes);
   };
   // (the last pairs and the idle pairs: runtime parity)
-  auto loads_rt = [&](int t) __attribute__((always_inline)) {
-    if (t & 1) loads(Odd{}, t); else loads(Even{}, t);
+  auto loads_k_rt = [&](int t) __attribute__((always_inline)) {
+    if (t & 1) loads_k(Odd{}, t); else loads_k(Even{}, t);
+  };
+  auto loads_v_rt = [&](int t) __attribute__((always_inline)) {
+    if (t & 1) loads_v(Odd{}, t); else loads_v(Even{}, t);
   };
   // X(t): PV(t-1) with V in buffer 1-P, then QK^T(t) with K in buffer P.
-  auto x_bufs = [&](const uint8_t* v_prv, const int8_t* k_cur, bool do_pv, bool do_qk) __attribute__((always_inline)) {
+  auto x_bufs = [&](const uint8_t* v_prv, const int8_t* k_cur, bool do_pv, bool do_qk,
+                    const auto& hook) __attribute__((always_inline)) {
     // The matrix wave outranks the softmax wave while it issues PV (and the
     // rescale of O, when taken), which must not wait behind the softmax's
     // exps; its QK^T part competes at equal priority.
     __builtin_amdgcn_s_setprio(1);
-    if (do_pv) pv_phase<D, FP8, T>(v_prv, lane, pt, st);
+    if (do_pv) pv_phase<D, FP8, T>(v_prv, lane, pt, st, hook);
     __builtin_amdgcn_sched_barrier(0);         // P and the V operands die before the K operands load
     __builtin_amdgcn_s_setprio(0);
     if (do_qk) qk_tile<D>(k_cur, qreg, lane, s, qk_init);
   };
   auto x_phase = [&](auto par, int t, bool do_pv, bool do_qk) __attribute__((always_inline)) {
     constexpr int P = decltype(par)::value;
-    x_bufs(smem + 2 * kKBytes + (1 - P) * kVBytes, reinterpret_cast<const int8_t*>(smem + P * kKBytes), do_pv, do_qk);
+    x_bufs(smem + 2 * kKBytes + (1 - P) * kVBytes, reinterpret_cast<const int8_t*>(smem + P * kKBytes), do_pv, do_qk,
+           NoHook{});
+  };
+  // X(t) in the steady pairs with this group's loads issued one after each
+  // PV product, so that the wait for the address unit overlaps matrix work
+  // already issued: K(t+1) for group 0, V(t) for group 1.
+  auto x_phase_loading = [&](auto par, int t) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;
+    int8_t* kdst = reinterpret_cast<int8_t*>(smem + (1 - P) * kKBytes);
+    uint8_t* vdst = smem + 2 * kKBytes + P * kVBytes;
+    auto hook = [&](int j) __attribute__((always_inline)) {
+      if (grp == 0) {
+        if (j < StageG::kKLoads && t + 1 < n_wg)
+          StageG::issue_k_pass(kbase, kbytes, koffg, wv & 3, (t + 1) * kBkv, kdst, j);
+      } else {
+        if (j < StageG::kVLoads && t < n_wg) StageG::issue_v_pass(rv, voffg, wv & 3, t * kBkv, a.n_pad, vdst, j);
+      }
+    };
+    x_bufs(smem + 2 * kKBytes + (1 - P) * kVBytes, reinterpret_cast<const int8_t*>(smem + P * kKBytes), true, true,
+           hook);
   };
   // The same with the parity known only at run time (the last pairs of a
   // group): the compiler then cannot separate these reads from the prefetch in
@@ -578,7 +632,8 @@ __device__ __forceinline__ void attn_fwd_body(AttnArgs a) {
   // per work-group.
   auto x_phase_rt = [&](int t, bool do_pv, bool do_qk) __attribute__((always_inline)) {
     const int P = t & 1;
-    x_bufs(smem + 2 * kKBytes + (1 - P) * kVBytes, reinterpret_cast<const int8_t*>(smem + P * kKBytes), do_pv, do_qk);
+    x_bufs(smem + 2 * kKBytes + (1 - P) * kVBytes, reinterpret_cast<const int8_t*>(smem + P * kKBytes), do_pv, do_qk,
+           NoHook{});
   };
   // Y(t): softmax of tile t (registers only).
   auto y_phase = [&](int t, auto masked) __attribute__((always_inline)) {
@@ -605,16 +660,15 @@ __device__ __forceinline__ void attn_fwd_body(AttnArgs a) {
   const int n = n_g;
 
   if (grp == 0) {
-    // group 0, pair t: X(t) | Y(t)
+    // group 0, pair t: X(t) | Y(t); issues K(t+1) in X(t)
     if (n > 0) {
       x_phase(Even{}, 0, false, true);
-      loads(Even{}, 0);
+      loads_k(Even{}, 0);
       barrier_only();
       if (n == 1) y_phase(0, Masked{}); else y_phase(0, Full{});
       wait_loads_barrier();
       auto steady = [&](auto par, int t) __attribute__((always_inline)) {
-        x_phase(par, t, true, true);
-        loads(par, t);
+        x_phase_loading(par, t);
         barrier_only();
         y_phase(t, Full{});
         wait_loads_barrier();
@@ -625,34 +679,34 @@ __device__ __forceinline__ void attn_fwd_body(AttnArgs a) {
         steady(Even{}, t + 1);
       }
       if (t <= n - 2) { steady(Odd{}, t); ++t; }
-      // t == n - 1 (when n >= 2): masked last tile, then PV(n - 1) at pair n
       if (n >= 2) {
-        loads_rt(n - 1);
+        loads_k_rt(n - 1);
         x_phase_rt(n - 1, true, true);
         barrier_only();
         y_phase(n - 1, Masked{});
         wait_loads_barrier();
       }
-      loads_rt(n);
+      loads_k_rt(n);
       x_phase_rt(n, true, false);
       barrier_only();
       wait_loads_barrier();
     }
     for (int t = n + (n > 0 ? 1 : 0); t <= n_wg; ++t) {
-      loads_rt(t);
+      loads_k_rt(t);
       barrier_only();
       wait_loads_barrier();
     }
   } else {
-    // group 1, pair t: Y(t-1) | X(t)
+    // group 1, pair t: Y(t-1) | X(t); issues V(t) in X(t)
     if (n > 0) {
       barrier_only();
       x_phase(Even{}, 0, false, true);
+      loads_v(Even{}, 0);
       wait_loads_barrier();
       auto steady = [&](auto par, int t) __attribute__((always_inline)) {
         y_phase(t - 1, Full{});
         barrier_only();
-        x_phase(par, t, true, true);
+        x_phase_loading(par, t);
         wait_loads_barrier();
       };
       int t = 1;
@@ -661,7 +715,7 @@ __device__ __forceinline__ void attn_fwd_body(AttnArgs a) {
         steady(Even{}, t + 1);
       }
       if (t <= n - 1) { steady(Odd{}, t); ++t; }
-      // t == n: masked last tile's softmax, then PV(n - 1)
+      // t == n (== n_wg): masked last tile's softmax, then PV(n - 1); no V(n)
       y_phase(n - 1, Masked{});
       barrier_only();
       x_phase_rt(n, true, false);
@@ -669,6 +723,7 @@ __device__ __forceinline__ void attn_fwd_body(AttnArgs a) {
     }
     for (int t = n + (n > 0 ? 1 : 0); t <= n_wg; ++t) {
       barrier_only();
+      loads_v_rt(t);
       wait_loads_barrier();
     }
   }

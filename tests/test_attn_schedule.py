@@ -9,8 +9,9 @@ pairs -- and checks for every tile count a launch can see:
 
 * both groups arrive at the same number of barriers, of the same kinds in the
   same order (a mismatch would hang the work-group);
-* the loads of pair t are issued once, by group 0, in the pair's first phase
-  (after its matrix work in the steady pairs, before it in the last two);
+* the loads of pair t are issued once each: K(t+1) by group 0 in the pair's
+  first phase, V(t) by group 1 in its second phase (each group during its
+  matrix phase, or in an idle pair where it has none);
 * every LDS read finds the tile it expects in its buffer, and no load in
   flight targets a buffer that is being read;
 * each group reads every K and V tile it attends to exactly once, in order.
@@ -28,9 +29,11 @@ def tiles_for(q_tile, nk, causal):
 
 
 def group_events(grp, n, n_wg):
-    """Events of one group: ('loads', t), ('read_k', t), ('read_v', t), ('bar',), ('barw',)."""
+    """Events of one group: ('load_k', t) for K(t+1), ('load_v', t) for V(t),
+    ('read_k', t), ('read_v', t), ('bar',), ('barw',)."""
     ev = []
     bar, barw = ('bar',), ('barw',)
+    own = 'load_k' if grp == 0 else 'load_v'    # group 0 loads K(t+1), group 1 V(t)
 
     def x(t, pv, qk):
         if pv:
@@ -38,27 +41,29 @@ def group_events(grp, n, n_wg):
         if qk:
             ev.append(('read_k', t))
 
-    def pair(t, first, second, loads_after=False):
-        if grp == 0 and not loads_after:
-            ev.append(('loads', t))
+    def pair(t, first, second):
+        # a group issues its load of pair t in its own phase of the pair: the
+        # first for group 0, the second for group 1
+        if grp == 0:
+            ev.append((own, t))
         first()
-        if grp == 0 and loads_after:
-            ev.append(('loads', t))
         ev.append(bar)
+        if grp == 1:
+            ev.append((own, t))
         second()
         ev.append(barw)
 
     nothing = lambda: None
     if grp == 0:                                   # pair t: X(t) | Y(t)
         if n > 0:
-            pair(0, lambda: x(0, False, True), nothing, loads_after=True)
+            pair(0, lambda: x(0, False, True), nothing)
             t = 1
             while t + 1 <= n - 2:
                 for tt in (t, t + 1):
-                    pair(tt, lambda tt=tt: x(tt, True, True), nothing, loads_after=True)
+                    pair(tt, lambda tt=tt: x(tt, True, True), nothing)
                 t += 2
             if t <= n - 2:
-                pair(t, lambda: x(t, True, True), nothing, loads_after=True)
+                pair(t, lambda: x(t, True, True), nothing)
             if n >= 2:
                 pair(n - 1, lambda: x(n - 1, True, True), nothing)
             pair(n, lambda: x(n, True, False), nothing)
@@ -72,7 +77,12 @@ def group_events(grp, n, n_wg):
                 t += 2
             if t <= n - 1:
                 pair(t, nothing, lambda: x(t, True, True))
-            pair(n, nothing, lambda: x(n, True, False))
+            # the last pair: PV(n-1) only; a live group 1 walks every tile of
+            # the work-group (n == n_wg), so there is no V(n) to load
+            assert n == n_wg
+            ev.append(bar)
+            x(n, True, False)
+            ev.append(barw)
     for t in range(n + (1 if n > 0 else 0), n_wg + 1):
         pair(t, nothing, nothing)
     return ev
@@ -96,15 +106,19 @@ def check_work_group(nq, nk, causal, qp):
     kbuf = {0: 0, 1: None}                          # K(0) is staged before the first phase
     vbuf = {0: None, 1: None}
     pending = []
-    issued_all = []
+    issued_k, issued_v = [], []
     for p in range(len(kinds[0])):
-        issued = [[e[1] for e in phases[g][p] if e[0] == 'loads'] for g in (0, 1)]
-        assert issued[1] == [], "group 1 issues no loads"
-        assert issued[0] == ([p // 2] if p % 2 == 0 else []), "pair t's loads in its first phase"
-        issued_all += issued[0]
-        for t in issued[0]:
+        lk = [[e[1] for e in phases[g][p] if e[0] == 'load_k'] for g in (0, 1)]
+        lv = [[e[1] for e in phases[g][p] if e[0] == 'load_v'] for g in (0, 1)]
+        assert lk[1] == [] and lv[0] == [], "K loads by group 0, V loads by group 1"
+        assert lk[0] == ([p // 2] if p % 2 == 0 else []), "K(t+1) in pair t's first phase"
+        assert lv[1] in ([], [p // 2]) if p % 2 == 1 else lv[1] == [], "V(t) in pair t's second phase"
+        issued_k += lk[0]
+        issued_v += lv[1]
+        for t in lk[0]:
             if t + 1 < n_wg:
                 pending.append(('k', (t + 1) & 1, t + 1))
+        for t in lv[1]:
             if t < n_wg:
                 pending.append(('v', t & 1, t))
         for g in (0, 1):
@@ -118,7 +132,8 @@ def check_work_group(nq, nk, causal, qp):
             for kind, b, t in pending:
                 (kbuf if kind == 'k' else vbuf)[b] = t
             pending = []
-    assert issued_all == list(range(n_wg + 1)), "every pair's loads are issued once"
+    assert issued_k == list(range(n_wg + 1)), "every pair's K load is issued once"
+    assert [t for t in issued_v if t < n_wg] == list(range(n_wg)), "every V tile is loaded once, in order"
     for g in (0, 1):
         assert [e[1] for e in evs[g] if e[0] == 'read_k'] == list(range(ns[g]))
         assert [e[1] for e in evs[g] if e[0] == 'read_v'] == list(range(ns[g]))
@@ -150,5 +165,22 @@ def test_model_catches_a_missing_barrier(monkeypatch):
             ev = ev[:i] + ev[i + 1:]
         return ev
     monkeypatch.setitem(globals(), "group_events", broken)
+    with pytest.raises(AssertionError):
+        check_work_group(1000, 1000, False, 0)
+
+
+def test_model_catches_a_late_value_load(monkeypatch):
+    """The check fails when group 1 issues V(t) a phase late (after the wait
+    that should have landed it): group 0 would read a buffer still loading."""
+    orig = group_events
+
+    def late(grp, n, n_wg):
+        ev = orig(grp, n, n_wg)
+        if grp == 1:
+            i = next(i for i, e in enumerate(ev) if e[0] == 'load_v' and e[1] == 1)
+            j = ev.index(('barw',), i)
+            ev = ev[:i] + ev[i + 1:j + 1] + [ev[i]] + ev[j + 1:]
+        return ev
+    monkeypatch.setitem(globals(), "group_events", late)
     with pytest.raises(AssertionError):
         check_work_group(1000, 1000, False, 0)
