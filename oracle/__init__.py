@@ -15,6 +15,9 @@ method does not fix the precision, slow and meant to be read against the pages:
                     per-block INT8 Q/K, INT32 QK^T, dequantisation, tiled
                     online softmax, P to FP8 (or FP16), V to FP8 per channel,
                     two-level PV accumulation, epilogue.
+* ``mxfp4``      -- OCP MXFP4 codec (E2M1 elements, E8M0 shared scales per
+                    32 elements) written from the Microscaling specification,
+                    for the FP4 variant of the method.
 * ``exact``      -- fp64 exact softmax attention (the error bound the method
                     is measured against) and an fp64 tiled online softmax
                     with quantisation switched off.

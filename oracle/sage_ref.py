@@ -60,6 +60,19 @@ Readings where the pages are silent (each also listed in the design notes):
        method -- its own K channel mean, blocks from its own first token, its
        own V channel scales, causal masking top-left inside the sequence. A
        sequence with queries but no keys has zero output rows.
+  [R22] the FP4 microscaling variant (SageAttention3: heatdrop.ai review, "Key
+       highlights"; cnnetsun.cn guide, 序列长度优化技巧 -- named, never defined)
+       is read as OCP MXFP4: E2M1 elements with one E8M0 power-of-two scale per
+       32 elements along the contraction axis of each product (oracle/mxfp4.py).
+       Q and the smoothed K are blocked per token and 32 channels, V per channel
+       and 32 keys (from key 0 of the sequence), P~ per query row and 32 keys of
+       its KV tile. K smoothing [R5, R6, R8] is kept; there is no V scale in the
+       epilogue (the block scales enter the products).
+  [R23] the P block scale follows the same rule as every other MX block (shared
+       exponent floor(log2 max P~) - 2), and the row sum adds the P values that
+       enter the PV product [R16]; the online softmax is unchanged [R14, R15].
+  [R24] scores: S = dequant(Q) . dequant(K)^T (exact here in fp64; the matrix
+       cores sum it in fp32), S2 = fp32(fp32(S) * fp32(sm_scale * log2 e)).
 """
 from __future__ import annotations
 
@@ -69,6 +82,7 @@ import numpy as np
 import torch
 
 from .fp8_e4m3 import E4M3_MAX, e4m3_encode, e4m3_decode, e4m3_round
+from .mxfp4 import mxfp4_quantize
 
 LOG2E = 1.4426950408889634
 INT8_MAX = 127.0
@@ -385,3 +399,75 @@ def sage_attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, dtype: str, is
                            return_fp64=return_fp64)
         out[q0:q1] = o[0].transpose(1, 0, 2)
     return out
+
+
+# ---------------------------------------------------------------------------
+# FP4 microscaling variant (SageAttention3: heatdrop.ai review, "Key
+# highlights"; cnnetsun.cn guide, 序列长度优化技巧) [R22-R24]
+# ---------------------------------------------------------------------------
+def quant_qk_fp4(q: np.ndarray, k: np.ndarray, *, k_mean=None):
+    """Q and smoothed K to MXFP4 along the head dimension [R22]: one E8M0 scale
+    per token and 32 consecutive channels. Returns dict(q4, q_exp, qd, k4,
+    k_exp, kd, k_mean): codes [B,H,N,d] (one E2M1 code per byte), block
+    exponents [B,H,N,d/32], dequantised values (float64)."""
+    mu = k_channel_mean(k) if k_mean is None else np.asarray(k_mean, np.float32)
+    q4, qe, qd = mxfp4_quantize(np.asarray(q, np.float32), axis=3)
+    k4, ke, kd = mxfp4_quantize(smooth_k(k, mu), axis=3)
+    return dict(q4=q4, q_exp=qe, qd=qd, k4=k4, k_exp=ke, kd=kd, k_mean=mu)
+
+
+def quant_v_fp4(v: np.ndarray):
+    """V to MXFP4 along the tokens [R22]: one E8M0 scale per channel and 32
+    consecutive keys from key 0. Returns (codes [B,H,N,d], exponents
+    [B,H,ceil(N/32),d], dequantised float64 [B,H,N,d])."""
+    return mxfp4_quantize(np.asarray(v, np.float32), axis=2)
+
+
+def _p_codec_fp4(p: np.ndarray) -> np.ndarray:
+    """P~ of one KV tile to MXFP4 along the keys [R23]: per query row, blocks of
+    32 consecutive keys of the tile; returns the dequantised values."""
+    return mxfp4_quantize(p.astype(np.float32), axis=1)[2]
+
+
+def sage_attention_fp4(q, k, v, *, dtype: str, is_causal: bool, sm_scale: float, layout: str = "HND",
+                       bkv=None, rows=None, parts=None, return_fp64: bool = False):
+    """The FP4 microscaling variant of the forward, step by step [R22-R24].
+
+    K is smoothed as in the INT8 method; Q and K go to MXFP4 along the head
+    dimension, S = dequant(Q) dequant(K)^T (exact in fp64; the matrix cores
+    accumulate it in fp32), S2 = fp32(fp32(S) * fp32(sm_scale * log2 e)); the
+    online softmax is the method's (KV tiles of BKV keys, running max); P~ goes
+    to MXFP4 per query row and 32 keys; the row sum adds the dequantised P
+    [R16]; PV uses V in MXFP4 per channel and 32 keys, accumulated in two
+    levels as before. ``parts``: optional dict from quant_qk_fp4 plus ``vd``.
+    Returns [B,Hq,R,d] (HND), rounded to ``dtype`` unless ``return_fp64``.
+    """
+    q = as_hnd(np.asarray(q, np.float32), layout)
+    k = as_hnd(np.asarray(k, np.float32), layout)
+    v = as_hnd(np.asarray(v, np.float32), layout)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    bkv = BKV[d] if bkv is None else bkv
+    rows = np.arange(Nq) if rows is None else np.asarray(rows)
+    if parts is None:
+        parts = quant_qk_fp4(q, k)
+        parts["vd"] = quant_v_fp4(v)[2]
+    c = np.float32(float(sm_scale) * LOG2E)                                      # [R24]
+    keys = np.arange(Nk)
+    out = np.empty((B, Hq, len(rows), d), dtype=np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            s = parts["qd"][b, h, rows] @ parts["kd"][b, g].T                   # exact in fp64
+            s2 = (s.astype(np.float32) * c).astype(np.float32)
+            if is_causal:
+                s2 = np.where(keys[None, :] > rows[:, None], np.float32(-np.inf), s2)
+            o, l = online_softmax_pv(s2, parts["vd"][b, g], bkv=bkv, p_codec=_p_codec_fp4,
+                                     work_dtype=np.float32)
+            out[b, h] = o / l[:, None]
+    if return_fp64:
+        return out
+    return _round_to(out, dtype)
