@@ -285,6 +285,59 @@ sage_status sage_attn_fwd_codes(const sage_shape* s, const int8_t* q_codes, cons
 sage_status sage_debug_qk_i32(const sage_shape* s, const int8_t* q_codes, const int8_t* k_codes,
                               int32_t* s_out, void* stream);
 
+/* ---- FP4 microscaling variant (SageAttention3: heatdrop.ai review, "Key
+ * highlights"; cnnetsun.cn guide, 序列长度优化技巧 -- named on the pages
+ * without a format). Read as OCP MXFP4: FP4 E2M1 elements (values 0, 0.5, 1,
+ * 1.5, 2, 3, 4, 6 and their negatives) with one E8M0 power-of-two scale byte
+ * (2^(byte - 127)) per 32 elements along the contraction axis of each product.
+ * The shared exponent of a block is floor(log2(max |x|)) - 2, clamped to
+ * [-127, 127] (-127 for a block of zeros); each element is x / 2^exponent
+ * rounded half to even, magnitudes above 6 saturating to 6. Codes are packed
+ * two per byte, element 2i in the low nibble. K is smoothed by its channel mean
+ * first, exactly as in sage_quant_qk (the same k_mean). The attention kernel
+ * computes S = Q.K^T on the block-scaled FP4 matrix cores (fp32 sums), the
+ * online softmax in the log2 domain over 128-key tiles, P~ to MXFP4 per query
+ * row and 32 keys of the tile (the row sum adds the values that enter PV),
+ * and PV with V in MXFP4, two-level accumulation, O / l in the epilogue.
+ * s->qk_gran must be SAGE_QK_PER_BLOCK (0): the MX blocks are fixed; any
+ * other valid value returns SAGE_ERR_UNSUPPORTED. */
+
+/* Workspace bytes sage_quant_fp4 needs (K channel-sum partials, as for
+ * sage_quant_qk). 0 for an invalid or unsupported shape. */
+size_t sage_quant_fp4_workspace_bytes(const sage_shape* s);
+/* Workspace bytes sage_attn_fwd_fp4 needs (all MXFP4 codes and scales, the K
+ * mean and the partials). 0 for an invalid or unsupported shape. */
+size_t sage_fp4_workspace_bytes(const sage_shape* s);
+
+/* MXFP4 quantisation of Q, smoothed K and V, with N = sage_v_codes_stride(Nk):
+ *   q_codes [B,Hq,Nq,d/2] u8    q_scale [B,Hq,Nq,d/32] u8: blocks of 32 channels per token
+ *   k_codes [B,Hkv,Nk,d/2] u8   k_scale [B,Hkv,Nk,d/32] u8: the same on fp32(k - k_mean)
+ *   k_mean  [B,Hkv,d] fp32      as in sage_quant_qk
+ *   v_codes [B,Hkv,d,N/2] u8    V transposed (keys contiguous per channel), blocks
+ *                               of 32 keys from key 0; keys past Nk are code 0
+ *   v_scale [B,Hkv,N/128,d,4] u8  per 128-key tile, each channel's four block
+ *                               scales (16-byte aligned); blocks past Nk get 0
+ * Codes are in canonical HND order whatever s->layout is. Skips Q when Nq == 0
+ * and K/V when Nk == 0 (their pointers may then be NULL). */
+sage_status sage_quant_fp4(const sage_shape* s, const void* q, const void* k, const void* v,
+                           uint8_t* q_codes, uint8_t* q_scale, uint8_t* k_codes, uint8_t* k_scale,
+                           float* k_mean, uint8_t* v_codes, uint8_t* v_scale,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* The FP4 attention kernel alone, from codes as sage_quant_fp4 writes them;
+ * o, is_causal and sm_scale as for sage_attn_fwd. Needs no workspace. */
+sage_status sage_attn_fwd_fp4_codes(const sage_shape* s, const uint8_t* q_codes, const uint8_t* q_scale,
+                                    const uint8_t* k_codes, const uint8_t* k_scale, const uint8_t* v_codes,
+                                    const uint8_t* v_scale, void* o, int32_t is_causal, float sm_scale,
+                                    void* stream);
+
+/* The whole FP4 forward (quantisation then attention) on `stream`; arguments
+ * and errors as for sage_attn_fwd without pv_dtype, the workspace sized by
+ * sage_fp4_workspace_bytes. */
+sage_status sage_attn_fwd_fp4(const sage_shape* s, const void* q, const void* k, const void* v, void* o,
+                              int32_t is_causal, float sm_scale, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /* Static description of a status code (never NULL). Part of the error
  * convention above, not of the method. */
 const char* sage_status_string(sage_status st);

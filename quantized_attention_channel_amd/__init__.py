@@ -10,7 +10,8 @@ Entry points (same names as the C ABI):
   sage_quant_qk, sage_quant_v, sage_transpose_v, sage_attn_fwd,
   sage_attn_fwd_codes, sage_debug_qk_i32, sage_varlen_workspace_bytes,
   sage_attn_fwd_varlen, sage_quant_varlen, sage_quant_varlen_workspace_bytes,
-  sage_attn_fwd_noalloc.
+  sage_attn_fwd_noalloc, sage_quant_fp4, sage_quant_fp4_workspace_bytes,
+  sage_fp4_workspace_bytes, sage_attn_fwd_fp4_codes, sage_attn_fwd_fp4.
 User-facing wrapper:
   sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None,
            pv_dtype="fp8", qk_quant_gran="per_block") -- the call shape the
@@ -20,6 +21,9 @@ User-facing wrapper:
   sageattn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
                   max_seqlen_k, ...) -- packed variable-length batches
   (heatdrop.ai review, "Key highlights").
+  pv_dtype="fp4" in sageattn selects the FP4 microscaling variant (MXFP4 Q, K,
+  P and V; heatdrop.ai review, "Key highlights"; cnnetsun.cn guide,
+  序列长度优化技巧).
 """
 from __future__ import annotations
 
@@ -66,6 +70,14 @@ _SIGNATURES = {
     "sage_quant_varlen_workspace_bytes": (ctypes.c_size_t, [_c_shape_p]),
     "sage_quant_varlen": (ctypes.c_int, [_c_shape_p, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                          _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "sage_quant_fp4_workspace_bytes": (ctypes.c_size_t, [_c_shape_p]),
+    "sage_fp4_workspace_bytes": (ctypes.c_size_t, [_c_shape_p]),
+    "sage_quant_fp4": (ctypes.c_int, [_c_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _vp, ctypes.c_size_t, _vp]),
+    "sage_attn_fwd_fp4_codes": (ctypes.c_int, [_c_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32,
+                                               ctypes.c_float, _vp]),
+    "sage_attn_fwd_fp4": (ctypes.c_int, [_c_shape_p, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_float, _vp,
+                                         ctypes.c_size_t, _vp]),
 }
 # the workspace limit of sage_attn_fwd_noalloc (SAGE_NOALLOC_MAX_WORKSPACE_BYTES in sage.h)
 NOALLOC_MAX_WORKSPACE_BYTES = 32 * 1024 * 1024
@@ -415,6 +427,83 @@ def sage_quant_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seql
     return out
 
 
+# ------------------------------------------------------------------ FP4 microscaling variant
+def sage_fp4_workspace_bytes(shape: SageShape) -> int:
+    return int(lib.sage_fp4_workspace_bytes(_ref(shape)))
+
+
+def fp4_buffers(shape: SageShape, device) -> dict:
+    """Empty MXFP4 buffers of ``shape`` (layouts of sage.h): codes two per byte,
+    E8M0 scale bytes; V transposed and padded to sage_v_codes_stride(Nk) keys,
+    its scales per 128-key tile."""
+    B, Hq, Hkv, Nq, Nk, d = shape.batch, shape.heads_q, shape.heads_kv, shape.seq_q, shape.seq_k, shape.head_dim
+    npad = sage_v_codes_stride(Nk)
+    u8 = dict(dtype=torch.uint8, device=device)
+    return dict(q_codes=torch.empty((B, Hq, Nq, d // 2), **u8), q_scale=torch.empty((B, Hq, Nq, d // 32), **u8),
+                k_codes=torch.empty((B, Hkv, Nk, d // 2), **u8), k_scale=torch.empty((B, Hkv, Nk, d // 32), **u8),
+                k_mean=torch.empty((B, Hkv, d), dtype=torch.float32, device=device),
+                v_codes=torch.empty((B, Hkv, d, npad // 2), **u8),
+                v_scale=torch.empty((B, Hkv, npad // 128, d, 4), **u8))
+
+
+def sage_quant_fp4(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout: str = "HND") -> dict:
+    """MXFP4 quantisation of Q, smoothed K and V; returns fp4_buffers' dict."""
+    _check_inputs(q, k, v)
+    s = shape_of(q, k, tensor_layout)
+    if tuple(v.shape) != tuple(k.shape) or v.dtype != q.dtype:
+        raise ValueError("v must have k's shape and all inputs one dtype")
+    dev = q.device
+    out = fp4_buffers(s, dev)
+    ws = _workspace(int(lib.sage_quant_fp4_workspace_bytes(_ref(s))), dev)
+    _check(lib.sage_quant_fp4(_ref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(out["q_codes"]), _ptr(out["q_scale"]),
+                              _ptr(out["k_codes"]), _ptr(out["k_scale"]), _ptr(out["k_mean"]), _ptr(out["v_codes"]),
+                              _ptr(out["v_scale"]), _ptr(ws), ws.numel(), _stream(dev)), "sage_quant_fp4")
+    return out
+
+
+def sage_attn_fwd_fp4_codes(shape: SageShape, codes: dict, o: torch.Tensor, *, is_causal: bool = False,
+                            sm_scale: Optional[float] = None) -> torch.Tensor:
+    """The FP4 attention kernel alone, from sage_quant_fp4's buffers. Writes into ``o``."""
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(shape.head_dim)
+    in_dtype = {v: k for k, v in DTYPES.items()}.get(shape.dtype)
+    if in_dtype is None:
+        raise ValueError(f"shape.dtype must be one of {sorted(DTYPES.values())}, got {shape.dtype}")
+    if not isinstance(o, torch.Tensor) or not o.is_cuda:
+        raise ValueError("o must be a GPU tensor")
+    dev = o.device
+    B, Hq, Hkv, Nq, Nk, d = shape.batch, shape.heads_q, shape.heads_kv, shape.seq_q, shape.seq_k, shape.head_dim
+    npad = sage_v_codes_stride(Nk)
+    sizes = dict(q_codes=B * Hq * Nq * d // 2, q_scale=B * Hq * Nq * d // 32, k_codes=B * Hkv * Nk * d // 2,
+                 k_scale=B * Hkv * Nk * d // 32, v_codes=B * Hkv * d * npad // 2, v_scale=B * Hkv * d * npad // 32)
+    _expect(o, "o", in_dtype, B * Hq * Nq * d, dev)
+    for name, n in sizes.items():
+        _expect(codes.get(name), name, torch.uint8, n, dev)
+    _check(lib.sage_attn_fwd_fp4_codes(_ref(shape), _ptr(codes["q_codes"]), _ptr(codes["q_scale"]),
+                                       _ptr(codes["k_codes"]), _ptr(codes["k_scale"]), _ptr(codes["v_codes"]),
+                                       _ptr(codes["v_scale"]), _ptr(o), int(bool(is_causal)), float(sm_scale),
+                                       _stream(dev)), "sage_attn_fwd_fp4_codes")
+    return o
+
+
+def sage_attn_fwd_fp4(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, is_causal: bool = False,
+                      sm_scale: Optional[float] = None, tensor_layout: str = "HND",
+                      out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The whole FP4 microscaling forward (quantisation and attention)."""
+    _check_inputs(q, k, v)
+    s = shape_of(q, k, tensor_layout)
+    if tuple(v.shape) != tuple(k.shape) or v.dtype != q.dtype:
+        raise ValueError("v must have k's shape and all inputs one dtype")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(s.head_dim)
+    dev = q.device
+    o = _out_like(q, out)
+    ws = _workspace_for(workspace, sage_fp4_workspace_bytes(s), dev)
+    _check(lib.sage_attn_fwd_fp4(_ref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(o), int(bool(is_causal)),
+                                 float(sm_scale), _ptr(ws), ws.numel(), _stream(dev)), "sage_attn_fwd_fp4")
+    return o
+
+
 def sage_debug_qk_i32(q_codes: torch.Tensor, k_codes: torch.Tensor) -> torch.Tensor:
     """INT32 S for canonical-order codes [B,Hq,Nq,d] x [B,Hkv,Nk,d] -> [B,Hq,Nq,Nk]."""
     _check_inputs(q_codes, k_codes)
@@ -454,6 +543,11 @@ def sageattn(q, k, v, tensor_layout: str = "HND", is_causal: bool = False, sm_sc
         raise TypeError(f"unexpected arguments: {sorted(kwargs)}")
     if qk_quant_gran not in QK_GRANS:
         raise ValueError(f"qk_quant_gran must be one of {sorted(QK_GRANS)}, got {qk_quant_gran!r}")
+    if pv_dtype == "fp4":
+        if qk_quant_gran != "per_block":
+            raise ValueError("the FP4 variant has fixed MX blocks; qk_quant_gran must be per_block")
+        return sage_attn_fwd_fp4(q.contiguous(), k.contiguous(), v.contiguous(), is_causal=is_causal,
+                                 sm_scale=sm_scale, tensor_layout=tensor_layout)
     return sage_attn_fwd(q.contiguous(), k.contiguous(), v.contiguous(), is_causal=is_causal,
                          sm_scale=sm_scale, pv_dtype=pv_dtype, tensor_layout=tensor_layout,
                          qk_gran=qk_quant_gran)
@@ -474,6 +568,7 @@ def sageattn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_
 
 __all__ = ["sageattn", "sageattn_varlen", "sage_attn_fwd_varlen", "sage_varlen_workspace_bytes",
            "SageVarlenShape", "varlen_shape_of", "sage_attn_fwd", "sage_attn_fwd_codes", "sage_quant_qk", "sage_quant_v",
-           "sage_transpose_v", "sage_debug_qk_i32",
+           "sage_transpose_v", "sage_debug_qk_i32", "sage_quant_fp4", "sage_attn_fwd_fp4",
+           "sage_attn_fwd_fp4_codes", "sage_fp4_workspace_bytes", "fp4_buffers",
            "sage_block_sizes", "sage_v_codes_stride", "sage_workspace_bytes", "make_shape", "shape_of",
            "SageError", "SageShape", "QK_GRANS", "lib", "LIB_PATH"]

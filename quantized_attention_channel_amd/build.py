@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsage.so")
-SOURCES = ["sage_abi.hip", "quant_kernels.hip", "attn_kernel.hip"]
+SOURCES = ["sage_abi.hip", "quant_kernels.hip", "attn_kernel.hip", "fp4_kernels.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -30,6 +30,7 @@
 #include <climits>
 #include <type_traits>
 
+#include "attn_schedule.h"
 #include "sage_device.h"
 #include "sage_launch.h"
 
@@ -190,12 +191,6 @@ struct RowState {
 
 template <typename T>
 using Half8 = typename std::conditional<std::is_same<T, BF16>::value, bf16x8, f16x8>::type;
-
-// Pins a value in registers at this point: it must be computed before here and
-// cannot be sunk past it. Used to keep each phase's work inside its phase (the
-// barriers order memory only). Emits no instruction.
-template <typename V>
-__device__ __forceinline__ void pin(V& x) { asm volatile("" : "+v"(x)); }
 
 // P of one tile as the PV product consumes it, with the tile's rescale factor.
 template <bool FP8, typename T>
@@ -434,8 +429,6 @@ __device__ __forceinline__ void pv_phase(const uint8_t* sv, int lane, const PTil
 // matrix phase; both must land by the end of phase 2t+1.
 constexpr int kWaves = 8;
 
-__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
-__device__ __forceinline__ void wait_loads_barrier() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int D, bool FP8, bool CAUSAL, typename T, bool FINE>
 __device__ __forceinline__ void attn_fwd_body(AttnArgs a) {
@@ -655,78 +648,8 @@ __device__ __forceinline__ void attn_fwd_body(AttnArgs a) {
     __builtin_amdgcn_s_setprio(0);
     softmax_phase<D, FP8, CAUSAL, decltype(masked)::value, FINE, T>(s, lane, t * kBkv, qi, nk, c, st.m, pt);
   };
-  using Masked = std::true_type;
-  using Full = std::false_type;
-  const int n = n_g;
-
-  if (grp == 0) {
-    // group 0, pair t: X(t) | Y(t); issues K(t+1) in X(t)
-    if (n > 0) {
-      x_phase(Even{}, 0, false, true);
-      loads_k(Even{}, 0);
-      barrier_only();
-      if (n == 1) y_phase(0, Masked{}); else y_phase(0, Full{});
-      wait_loads_barrier();
-      auto steady = [&](auto par, int t) __attribute__((always_inline)) {
-        x_phase_loading(par, t);
-        barrier_only();
-        y_phase(t, Full{});
-        wait_loads_barrier();
-      };
-      int t = 1;
-      for (; t + 1 <= n - 2; t += 2) {
-        steady(Odd{}, t);
-        steady(Even{}, t + 1);
-      }
-      if (t <= n - 2) { steady(Odd{}, t); ++t; }
-      if (n >= 2) {
-        loads_k_rt(n - 1);
-        x_phase_rt(n - 1, true, true);
-        barrier_only();
-        y_phase(n - 1, Masked{});
-        wait_loads_barrier();
-      }
-      loads_k_rt(n);
-      x_phase_rt(n, true, false);
-      barrier_only();
-      wait_loads_barrier();
-    }
-    for (int t = n + (n > 0 ? 1 : 0); t <= n_wg; ++t) {
-      loads_k_rt(t);
-      barrier_only();
-      wait_loads_barrier();
-    }
-  } else {
-    // group 1, pair t: Y(t-1) | X(t); issues V(t) in X(t)
-    if (n > 0) {
-      barrier_only();
-      x_phase(Even{}, 0, false, true);
-      loads_v(Even{}, 0);
-      wait_loads_barrier();
-      auto steady = [&](auto par, int t) __attribute__((always_inline)) {
-        y_phase(t - 1, Full{});
-        barrier_only();
-        x_phase_loading(par, t);
-        wait_loads_barrier();
-      };
-      int t = 1;
-      for (; t + 1 <= n - 1; t += 2) {
-        steady(Odd{}, t);
-        steady(Even{}, t + 1);
-      }
-      if (t <= n - 1) { steady(Odd{}, t); ++t; }
-      // t == n (== n_wg): masked last tile's softmax, then PV(n - 1); no V(n)
-      y_phase(n - 1, Masked{});
-      barrier_only();
-      x_phase_rt(n, true, false);
-      wait_loads_barrier();
-    }
-    for (int t = n + (n > 0 ? 1 : 0); t <= n_wg; ++t) {
-      barrier_only();
-      loads_v_rt(t);
-      wait_loads_barrier();
-    }
-  }
+  run_pingpong(grp, n_g, n_wg, x_phase, x_phase_loading, x_phase_rt, y_phase, loads_k, loads_v, loads_k_rt,
+               loads_v_rt);
   __builtin_amdgcn_s_setprio(0);
 
   // Epilogue: normalise, undo the V scale, round, store in the caller's layout.

@@ -419,6 +419,104 @@ sage_status attn_fwd_check(const sage_shape* s, const void* q, const void* k, co
   return SAGE_OK;
 }
 
+// ---- FP4 microscaling variant
+// Byte counts of the MXFP4 buffers of shape `d` (layouts in include/sage.h).
+struct Fp4Sizes {
+  size_t q_codes, q_scale, k_codes, k_scale, k_mean, v_codes, v_scale, ksum;
+};
+
+Fp4Sizes fp4_sizes(const Dims& d) {
+  const int64_t npad = round_up(d.Nk, sage::kVPad);
+  Fp4Sizes z;
+  z.q_codes = size_t(d.B * d.Hq * d.Nq * d.D / 2);
+  z.q_scale = size_t(d.B * d.Hq * d.Nq * d.D / 32);
+  z.k_codes = size_t(d.B * d.Hkv * d.Nk * d.D / 2);
+  z.k_scale = size_t(d.B * d.Hkv * d.Nk * d.D / 32);
+  z.k_mean = size_t(d.B * d.Hkv * d.D) * 4;
+  z.v_codes = size_t(d.B * d.Hkv * d.D * npad / 2);
+  z.v_scale = size_t(d.B * d.Hkv * d.D * npad / 32);
+  z.ksum = size_t(d.B * d.Hkv * cdiv(d.Nk, kStatChunk) * d.D) * 8;
+  return z;
+}
+
+struct Fp4Layout {
+  size_t q_codes, q_scale, k_codes, k_scale, k_mean, v_codes, v_scale, ksum, total;
+};
+
+Fp4Layout fp4_layout_for(const Dims& d) {
+  const Fp4Sizes z = fp4_sizes(d);
+  Fp4Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  L.q_codes = take(z.q_codes);
+  L.q_scale = take(z.q_scale);
+  L.k_codes = take(z.k_codes);
+  L.k_scale = take(z.k_scale);
+  L.k_mean = take(z.k_mean);
+  L.v_codes = take(z.v_codes);
+  L.v_scale = take(z.v_scale);
+  L.ksum = take(z.ksum);
+  L.total = off;
+  return L;
+}
+
+// Shape checks of the FP4 entry points: the MX blocks are fixed, so only the
+// default granularity is accepted.
+sage_status check_fp4_shape(const sage_shape* s, Dims* d) {
+  sage_status st = check_shape(s, d);
+  if (st != SAGE_OK) return st;
+  if (d->fine) return SAGE_ERR_UNSUPPORTED;
+  return SAGE_OK;
+}
+
+sage::Fp4QuantArgs fp4_quant_args(const Dims& d, const void* q, const void* k, const void* v, uint8_t* q_codes,
+                                  uint8_t* q_scale, uint8_t* k_codes, uint8_t* k_scale, float* k_mean,
+                                  uint8_t* v_codes, uint8_t* v_scale, double* ksum) {
+  sage::Fp4QuantArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.qgeo = geom(d, d.Hq, d.Nq);
+  a.kgeo = geom(d, d.Hkv, d.Nk);
+  a.vgeo = geom(d, d.Hkv, d.Nk);
+  a.B = int(d.B), a.Hq = int(d.Hq), a.Hkv = int(d.Hkv), a.Nq = int(d.Nq), a.Nk = int(d.Nk), a.D = int(d.D);
+  a.n_pad = int(round_up(d.Nk, sage::kVPad));
+  a.bf16 = d.bf16;
+  a.q_codes = q_codes;
+  a.q_scale = q_scale;
+  a.k_codes = k_codes;
+  a.k_scale = k_scale;
+  a.k_mean = k_mean;
+  a.v_codes = v_codes;
+  a.v_scale = v_scale;
+  a.ksum_part = ksum;
+  return a;
+}
+
+sage::Fp4AttnArgs fp4_attn_args(const Dims& d, const uint8_t* q_codes, const uint8_t* q_scale,
+                                const uint8_t* k_codes, const uint8_t* k_scale, const uint8_t* v_codes,
+                                const uint8_t* v_scale, void* o, int32_t is_causal, float sm_scale) {
+  sage::Fp4AttnArgs a{};
+  a.q4 = q_codes;
+  a.q_sc = q_scale;
+  a.k4 = k_codes;
+  a.k_sc = k_scale;
+  a.v4 = v_codes;
+  a.v_sc = v_scale;
+  a.o = o;
+  a.ogeo = geom(d, d.Hq, d.Nq);
+  a.B = int(d.B), a.Hq = int(d.Hq), a.Hkv = int(d.Hkv), a.Nq = int(d.Nq), a.Nk = int(d.Nk), a.D = int(d.D);
+  a.n_pad = int(round_up(d.Nk, sage::kVPad));
+  a.scale_log2 = sm_scale * sage::kLog2E;
+  a.causal = is_causal != 0;
+  a.bf16 = d.bf16;
+  return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -759,6 +857,99 @@ sage_status sage_attn_fwd_codes(const sage_shape* s, const int8_t* q_codes, cons
   aa.fp8 = fp8;
   aa.fine = d.fine;
   return from_hip(sage::launch_attn(aa, static_cast<hipStream_t>(stream)));
+}
+
+size_t sage_quant_fp4_workspace_bytes(const sage_shape* s) {
+  Dims d;
+  return check_fp4_shape(s, &d) == SAGE_OK ? qk_ws_bytes(d) : 0;
+}
+
+size_t sage_fp4_workspace_bytes(const sage_shape* s) {
+  Dims d;
+  return check_fp4_shape(s, &d) == SAGE_OK ? fp4_layout_for(d).total : 0;
+}
+
+sage_status sage_quant_fp4(const sage_shape* s, const void* q, const void* k, const void* v, uint8_t* q_codes,
+                           uint8_t* q_scale, uint8_t* k_codes, uint8_t* k_scale, float* k_mean, uint8_t* v_codes,
+                           uint8_t* v_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  Dims d;
+  sage_status st = check_fp4_shape(s, &d);
+  if (st != SAGE_OK) return st;
+  if (d.B == 0 || (d.Nq == 0 && d.Nk == 0)) return SAGE_OK;
+  const bool has_q = d.Nq > 0, has_k = d.Nk > 0;
+  if (has_q && (!q || !q_codes || !q_scale)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (has_k && (!k || !v || !k_codes || !k_scale || !k_mean || !v_codes || !v_scale || !workspace))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  if (has_q && (!aligned(q, 16) || !aligned(q_codes, 16) || !aligned(q_scale, 4))) return SAGE_ERR_INVALID_ARGUMENT;
+  if (has_k && (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_codes, 16) || !aligned(k_scale, 4) ||
+                !aligned(k_mean, 4) || !aligned(v_codes, 16) || !aligned(v_scale, 16) || !aligned(workspace, 256)))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  if (has_k && workspace_bytes < qk_ws_bytes(d)) return SAGE_ERR_WORKSPACE;
+  const Fp4Sizes z = fp4_sizes(d);
+  const size_t qin = has_q ? size_t(d.B * d.Hq * d.Nq * d.D) * 2 : 0, kin = has_k ? size_t(d.B * d.Hkv * d.Nk * d.D) * 2 : 0;
+  if (aliased({{q_codes, has_q ? z.q_codes : 0}, {q_scale, has_q ? z.q_scale : 0}, {k_codes, has_k ? z.k_codes : 0},
+               {k_scale, has_k ? z.k_scale : 0}, {k_mean, has_k ? z.k_mean : 0}, {v_codes, has_k ? z.v_codes : 0},
+               {v_scale, has_k ? z.v_scale : 0}, {workspace, has_k ? qk_ws_bytes(d) : 0}},
+              {{q, qin}, {k, kin}, {v, kin}}))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  sage::Fp4QuantArgs a = fp4_quant_args(d, q, k, v, q_codes, q_scale, k_codes, k_scale, k_mean, v_codes, v_scale,
+                                        static_cast<double*>(workspace));
+  if (!has_q) a.Nq = 0;
+  if (!has_k) a.Nk = 0, a.n_pad = 0;
+  return from_hip(sage::launch_quant_fp4(a, static_cast<hipStream_t>(stream)));
+}
+
+sage_status sage_attn_fwd_fp4_codes(const sage_shape* s, const uint8_t* q_codes, const uint8_t* q_scale,
+                                    const uint8_t* k_codes, const uint8_t* k_scale, const uint8_t* v_codes,
+                                    const uint8_t* v_scale, void* o, int32_t is_causal, float sm_scale,
+                                    void* stream) {
+  Dims d;
+  sage_status st = check_fp4_shape(s, &d);
+  if (st != SAGE_OK) return st;
+  if (is_causal != 0 && is_causal != 1) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (d.B == 0 || d.Nq == 0) return SAGE_OK;
+  if (d.Nk == 0) return SAGE_ERR_INVALID_ARGUMENT;
+  if (is_causal && d.Nq != d.Nk) return SAGE_ERR_UNSUPPORTED;
+  if (!q_codes || !q_scale || !k_codes || !k_scale || !v_codes || !v_scale || !o) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(o, 16) ||
+      !aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(v_scale, 16))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  const Fp4Sizes z = fp4_sizes(d);
+  if (aliased({{o, size_t(d.B * d.Hq * d.Nq * d.D) * 2}},
+              {{q_codes, z.q_codes}, {q_scale, z.q_scale}, {k_codes, z.k_codes}, {k_scale, z.k_scale},
+               {v_codes, z.v_codes}, {v_scale, z.v_scale}}))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  return from_hip(sage::launch_attn_fp4(
+      fp4_attn_args(d, q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, o, is_causal, sm_scale),
+      static_cast<hipStream_t>(stream)));
+}
+
+sage_status sage_attn_fwd_fp4(const sage_shape* s, const void* q, const void* k, const void* v, void* o,
+                              int32_t is_causal, float sm_scale, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  Dims d;
+  bool noop = false;
+  sage_status st = check_fp4_shape(s, &d);
+  if (st != SAGE_OK) return st;
+  st = attn_fwd_check(s, q, k, v, o, is_causal, sm_scale, SAGE_PV_FP16, &d, &noop);
+  if (st != SAGE_OK || noop) return st;
+  if (!workspace || !aligned(workspace, 256)) return SAGE_ERR_INVALID_ARGUMENT;
+  const Fp4Layout L = fp4_layout_for(d);
+  if (workspace_bytes < L.total) return SAGE_ERR_WORKSPACE;
+  const size_t qbytes = size_t(d.B * d.Hq * d.Nq * d.D) * 2, kvbytes = size_t(d.B * d.Hkv * d.Nk * d.D) * 2;
+  if (aliased({{o, qbytes}, {workspace, L.total}}, {{q, qbytes}, {k, kvbytes}, {v, kvbytes}}))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const sage::Fp4QuantArgs qa =
+      fp4_quant_args(d, q, k, v, at<uint8_t>(workspace, L.q_codes), at<uint8_t>(workspace, L.q_scale),
+                     at<uint8_t>(workspace, L.k_codes), at<uint8_t>(workspace, L.k_scale),
+                     at<float>(workspace, L.k_mean), at<uint8_t>(workspace, L.v_codes),
+                     at<uint8_t>(workspace, L.v_scale), at<double>(workspace, L.ksum));
+  if (sage::launch_quant_fp4(qa, hs) != hipSuccess) return SAGE_ERR_HIP;
+  return from_hip(sage::launch_attn_fp4(fp4_attn_args(d, qa.q_codes, qa.q_scale, qa.k_codes, qa.k_scale,
+                                                      qa.v_codes, qa.v_scale, o, is_causal, sm_scale),
+                                        hs));
 }
 
 sage_status sage_debug_qk_i32(const sage_shape* s, const int8_t* q_codes, const int8_t* k_codes, int32_t* s_out,

@@ -90,6 +90,39 @@ struct DebugQKArgs {
   int B, Hq, Hkv, Nq, Nk, D;
 };
 
+// FP4 microscaling variant: MXFP4 codes two per byte, E8M0 scale bytes (the
+// layouts are listed at the top of fp4_kernels.hip).
+struct Fp4QuantArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  TensorGeom qgeo, kgeo, vgeo;
+  int B, Hq, Hkv, Nq, Nk, n_pad, D;
+  bool bf16;
+  uint8_t* q_codes;    // [B*Hq][Nq][D/2]
+  uint8_t* q_scale;    // [B*Hq][Nq][D/32]
+  uint8_t* k_codes;    // [B*Hkv][Nk][D/2]
+  uint8_t* k_scale;    // [B*Hkv][Nk][D/32]
+  float* k_mean;       // [B*Hkv][D]
+  uint8_t* v_codes;    // [B*Hkv][D][n_pad/2]
+  uint8_t* v_scale;    // [B*Hkv][n_pad/128][D][4]
+  double* ksum_part;   // [B*Hkv][ceil(Nk/256)][D]
+};
+
+struct Fp4AttnArgs {
+  const uint8_t* q4;
+  const uint8_t* q_sc;
+  const uint8_t* k4;
+  const uint8_t* k_sc;
+  const uint8_t* v4;
+  const uint8_t* v_sc;
+  void* o;
+  TensorGeom ogeo;
+  int B, Hq, Hkv, Nq, Nk, n_pad, D;
+  float scale_log2;     // sm_scale * log2(e)
+  bool causal, bf16;
+};
+
 hipError_t launch_varlen_plan(const int32_t* cu_q, const int32_t* cu_k, int B, int total_q, int total_k,
                               int max_q, int max_k, int n_pad, SeqSpan* out, int32_t* qp_owner, int n_owner,
                               hipStream_t st);
@@ -97,5 +130,10 @@ hipError_t launch_quant_qk(const QuantQKArgs& a, hipStream_t st);
 hipError_t launch_quant_v(const QuantVArgs& a, hipStream_t st);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
 hipError_t launch_debug_qk(const DebugQKArgs& a, hipStream_t st);
+// K channel mean alone (the smoothing statistics of sage_quant_qk), dense batches.
+hipError_t launch_k_mean(const void* k, TensorGeom kgeo, int B, int Hkv, int Nk, int D, bool bf16, double* ksum_part,
+                         float* k_mean, hipStream_t st);
+hipError_t launch_quant_fp4(const Fp4QuantArgs& a, hipStream_t st);
+hipError_t launch_attn_fp4(const Fp4AttnArgs& a, hipStream_t st);
 
 }  // namespace sage

@@ -16,5 +16,10 @@ hipError_t launch_quant_qk(const QuantQKArgs&, hipStream_t) { return hipErrorNoD
 hipError_t launch_quant_v(const QuantVArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_attn(const AttnArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_debug_qk(const DebugQKArgs&, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_k_mean(const void*, TensorGeom, int, int, int, int, bool, double*, float*, hipStream_t) {
+  return hipErrorNoDevice;
+}
+hipError_t launch_quant_fp4(const Fp4QuantArgs&, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_attn_fp4(const Fp4AttnArgs&, hipStream_t) { return hipErrorNoDevice; }
 
 }  // namespace sage

@@ -246,6 +246,56 @@ def test_noalloc_entry_point_checks_before_any_hip_call():
     assert sage.lib.sage_attn_fwd_noalloc(sp, FAKE, FAKE + G, FAKE + 2 * G, FAKE, 0, 0.1, 1, None) == bad   # o on q
 
 
+def test_fp4_workspace_holds_the_mx_buffers():
+    s = _shape()
+    B, Hq, Hkv, N, d = 2, 4, 2, 300, 128
+    npad = sage.sage_v_codes_stride(N)
+    need = (B * Hq * N * d // 2 + B * Hq * N * d // 32 + B * Hkv * N * d // 2 + B * Hkv * N * d // 32
+            + B * Hkv * d * 4 + B * Hkv * d * npad // 2 + B * Hkv * d * npad // 32)
+    assert sage.lib.sage_fp4_workspace_bytes(ctypes.byref(s)) >= need
+    assert sage.lib.sage_quant_fp4_workspace_bytes(ctypes.byref(s)) == sage.lib.sage_quant_qk_workspace_bytes(
+        ctypes.byref(s))
+    # the MX blocks are fixed: per-thread granularity is not offered, bad enums are invalid
+    assert sage.lib.sage_fp4_workspace_bytes(ctypes.byref(_shape(gran="per_thread"))) == 0
+    assert sage.lib.sage_fp4_workspace_bytes(ctypes.byref(_shape(d=96))) == 0
+
+
+@FAKE_ADDRESSES
+def test_fp4_entry_points_validate():
+    sp = ctypes.byref(_shape())
+    bad, ws = sage.SAGE_ERR_INVALID_ARGUMENT, FAKE + 2 ** 33
+    n = sage.lib.sage_fp4_workspace_bytes(sp)
+    q, k, v, o = (FAKE + i * G for i in range(4))
+    fwd = sage.lib.sage_attn_fwd_fp4
+    assert fwd(sp, q, k, v, o, 0, 0.1, ws, n - 1, None) == sage.SAGE_ERR_WORKSPACE
+    assert fwd(sp, None, k, v, o, 0, 0.1, ws, n, None) == bad
+    assert fwd(sp, q, k, v, o + 8, 0, 0.1, ws, n, None) == bad                      # misaligned o
+    assert fwd(sp, q, k, v, q, 0, 0.1, ws, n, None) == bad                          # o on q
+    assert fwd(sp, q, k, v, o, 2, 0.1, ws, n, None) == bad
+    assert fwd(sp, q, k, v, o, 0, float("nan"), ws, n, None) == bad
+    assert fwd(sp, q, k, v, o, 0, 0.1, ws + 16, n, None) == bad                     # workspace alignment
+    assert fwd(sp, q, k, v, o, 0, 0.1, k + 4096, n, None) == bad                    # workspace inside k
+    assert fwd(ctypes.byref(_shape(Nk=200)), q, k, v, o, 1, 0.1, ws, n, None) == sage.SAGE_ERR_UNSUPPORTED
+    assert fwd(ctypes.byref(_shape(gran="per_thread")), q, k, v, o, 0, 0.1, ws, n, None) == sage.SAGE_ERR_UNSUPPORTED
+    assert fwd(ctypes.byref(_shape(d=32)), q, k, v, o, 0, 0.1, ws, n, None) == sage.SAGE_ERR_UNSUPPORTED
+    assert fwd(ctypes.byref(_shape(Nq=0)), None, None, None, None, 0, 0.1, None, 0, None) == sage.SAGE_OK
+    # quantisation: null, misaligned and aliased outputs, small workspace
+    qc, qs, kc, ks, km, vc, vs = (FAKE + i * G for i in range(4, 11))
+    qw = sage.lib.sage_quant_fp4_workspace_bytes(sp)
+    quant = sage.lib.sage_quant_fp4
+    assert quant(sp, q, k, v, None, qs, kc, ks, km, vc, vs, ws, qw, None) == bad
+    assert quant(sp, q, k, v, qc, qs, kc, ks, km, vc, vs + 4, ws, qw, None) == bad   # v_scale needs 16 bytes
+    assert quant(sp, q, k, v, qc, qs, kc, ks, km, vc, vs, ws, qw - 1, None) == sage.SAGE_ERR_WORKSPACE
+    assert quant(sp, q, k, v, qc, qs, kc, ks, km, v + 4096, vs, ws, qw, None) == bad  # codes on v
+    assert quant(sp, q, k, v, qc, qs, kc, qc + 16, km, vc, vs, ws, qw, None) == bad   # k scale on q codes
+    # attention from codes: o may not cover what it reads; v_scale 16-byte aligned
+    codes = sage.lib.sage_attn_fwd_fp4_codes
+    for oo in (qs, ks, vs, vc + 4096):
+        assert codes(sp, qc, qs, kc, ks, vc, vs, oo, 0, 0.1, None) == bad
+    assert codes(sp, qc, qs, kc, ks, vc, vs + 4, o, 0, 0.1, None) == bad
+    assert codes(sp, qc, qs, kc, ks, None, vs, o, 0, 0.1, None) == bad
+
+
 def test_python_wrapper_rejects_unsupported_sdpa_arguments():
     import torch
     q = torch.zeros(1, 1, 4, 64, dtype=torch.float16)
