@@ -41,6 +41,7 @@ import workloads as W  # noqa: E402
 
 METRIC = "attention TOPS (4·B·H·N²·d/t) at N=32K d=128 + % of INT8/FP8 MFMA peak"
 PEAK_TOPS = 5000.0            # MI355X dense INT8 and dense FP8 MFMA peak (5.0 POP/s each)
+PEAK_FP4_TOPS = 10100.0       # MI355X dense FP4 (and FP6) MFMA peak, 10.1 PFLOP/s
 PEAK_HBM_GBS = 8000.0
 ALIASES = {"tiny": W.TINY, "mid": W.MID_OUTLIER, "gqa": W.GQA_CAUSAL, "long": W.LONG_D64, "peak": W.PEAK}
 KERNEL_SOURCES = ["quantized_attention_channel_amd/csrc/attn_kernel.hip",
@@ -114,6 +115,41 @@ class Plan:
         self.sage._check(self.sage.lib.sage_attn_fwd(*self.args_full), "sage_attn_fwd")
 
 
+class Fp4Plan:
+    """The FP4 microscaling variant: sage_quant_fp4 + sage_attn_fwd_fp4_codes
+    per step (the kernels sage_attn_fwd_fp4 enqueues)."""
+
+    def __init__(self, w: W.Workload, q, k, v):
+        import quantized_attention_channel_amd as sage
+        self.sage, self.w, self.pv = sage, w, "fp4"
+        self.shape = s = sage.shape_of(q, k, w.layout)
+        dev = q.device
+        self.o = torch.empty_like(q)
+        self.codes = c = sage.fp4_buffers(s, dev)
+        lib = sage.lib
+        self.ws = torch.empty(max(lib.sage_quant_fp4_workspace_bytes(ctypes.byref(s)), 256), dtype=torch.uint8,
+                              device=dev)
+        self.full_ws = torch.empty(max(sage.sage_fp4_workspace_bytes(s), 256), dtype=torch.uint8, device=dev)
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        P = sage._ptr
+        self.args_quant = (ctypes.byref(s), P(q), P(k), P(v), P(c["q_codes"]), P(c["q_scale"]), P(c["k_codes"]),
+                           P(c["k_scale"]), P(c["k_mean"]), P(c["v_codes"]), P(c["v_scale"]), P(self.ws),
+                           self.ws.numel(), self.stream)
+        self.args_attn = (ctypes.byref(s), P(c["q_codes"]), P(c["q_scale"]), P(c["k_codes"]), P(c["k_scale"]),
+                          P(c["v_codes"]), P(c["v_scale"]), P(self.o), int(w.causal), float(w.sm_scale), self.stream)
+        self.args_full = (ctypes.byref(s), P(q), P(k), P(v), P(self.o), int(w.causal), float(w.sm_scale),
+                          P(self.full_ws), self.full_ws.numel(), self.stream)
+
+    def quant(self):
+        self.sage._check(self.sage.lib.sage_quant_fp4(*self.args_quant), "sage_quant_fp4")
+
+    def attention(self):
+        self.sage._check(self.sage.lib.sage_attn_fwd_fp4_codes(*self.args_attn), "sage_attn_fwd_fp4_codes")
+
+    def fused_entry(self):
+        self.sage._check(self.sage.lib.sage_attn_fwd_fp4(*self.args_full), "sage_attn_fwd_fp4")
+
+
 def time_steps(plan: Plan, steps: int, warmup: int):
     for _ in range(warmup):
         plan.quant()
@@ -184,8 +220,12 @@ def cpu_baseline(w: W.Workload, pv: str, rows: int, qk_gran: str = "per_block"):
     t0 = time.perf_counter()
     blk = ((sage_ref.PER_THREAD_BLK_Q, sage_ref.PER_THREAD_BLK_K) if qk_gran == "per_thread"
            else (sage_ref.BLK_Q, sage_ref.BLK_K))
-    sage_ref.sage_attention(qn, kn, vn, dtype=w.dtype, is_causal=w.causal, sm_scale=w.sm_scale, pv=pv,
-                            layout=w.layout, rows=np.unique(sel), blk_q=blk[0], blk_k=blk[1])
+    if pv == "fp4":
+        sage_ref.sage_attention_fp4(qn, kn, vn, dtype=w.dtype, is_causal=w.causal, sm_scale=w.sm_scale,
+                                    layout=w.layout, rows=np.unique(sel))
+    else:
+        sage_ref.sage_attention(qn, kn, vn, dtype=w.dtype, is_causal=w.causal, sm_scale=w.sm_scale, pv=pv,
+                                layout=w.layout, rows=np.unique(sel), blk_q=blk[0], blk_k=blk[1])
     dt = time.perf_counter() - t0
     if w.causal:
         ops = float(sum(4.0 * (int(i) + 1) * w.d for i in np.unique(sel)))
@@ -253,7 +293,7 @@ def host_info():
 
 def measure(w: W.Workload, pv: str, steps: int, warmup: int, qk_gran: str = "per_block"):
     q, k, v = W.generate(w, device="cuda")
-    plan = Plan(w, pv, q, k, v, qk_gran)
+    plan = Fp4Plan(w, q, k, v) if pv == "fp4" else Plan(w, pv, q, k, v, qk_gran)
     wall_ms, gpu_ms, quant_ms, attn_ms = time_steps(plan, steps, warmup)
     fused_ms = time_fused_entry(plan, max(3, steps // 4))
     ops = counted_ops(w)
@@ -297,7 +337,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="peak", help="peak|tiny|mid|gqa|long or a full workload name")
-    ap.add_argument("--pv", default=None, help="fp8|fp16 (default: the workload's)")
+    ap.add_argument("--pv", default=None, help="fp8|fp16|fp4 (default: the workload's; fp4 = the FP4 "
+                    "microscaling variant, MXFP4 Q/K/P/V)")
     ap.add_argument("--causal", type=int, default=None, help="override the workload's causal flag")
     ap.add_argument("--qk-gran", default="per_block", choices=["per_block", "per_thread"],
                     help="granularity of the Q/K INT8 scales")
@@ -325,12 +366,17 @@ def main():
         w = w.with_(causal=bool(args.causal))
     pv = args.pv or w.pv
 
+    if pv == "fp4" and args.qk_gran != "per_block":
+        print("the FP4 variant has fixed MX blocks: --qk-gran must be per_block", file=sys.stderr)
+        sys.exit(2)
     r = measure(w, pv, args.steps, args.warmup, args.qk_gran)
     copy_gbps = copy_bandwidth()
     traffic, util = counters_traffic(w, pv, args.qk_gran)
-    roof = {"bound": "mfma", "achieved": round(r["attn_tops"], 2), "peak": PEAK_TOPS, "unit": "TFLOP/s",
-            "frac": round(r["attn_tops"] / PEAK_TOPS, 4), "traffic": traffic,
-            "kernel": "attn_fwd_fine_kernel" if args.qk_gran == "per_thread" else "attn_fwd_kernel",
+    peak = PEAK_FP4_TOPS if pv == "fp4" else PEAK_TOPS
+    roof = {"bound": "mfma", "achieved": round(r["attn_tops"], 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(r["attn_tops"] / peak, 4), "traffic": traffic,
+            "kernel": ("attn_fp4_kernel" if pv == "fp4" else
+                       "attn_fwd_fine_kernel" if args.qk_gran == "per_thread" else "attn_fwd_kernel"),
             "ops_per_launch": counted_ops(w),
             "mean_launch_ms": round(r["attn_ms"], 4)}
     if util:
@@ -338,12 +384,13 @@ def main():
     out = {
         "metric": METRIC, "value": round(r["tops"], 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(r["wall_ms"], 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "int8+fp8_e4m3" if pv == "fp8" else f"int8+{w.dtype}",
+        "vs_baseline": None,
+        "dtype": {"fp8": "int8+fp8_e4m3", "fp4": "mxfp4_e2m1"}.get(pv, f"int8+{w.dtype}"),
         "data": "synthetic: seeded normal Q/K/V, per-channel K offsets (workloads.py)",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
                    "causal": w.causal, "pv": pv, "layout": w.layout, "input_dtype": w.dtype,
                    "qk_gran": args.qk_gran},
-        "mfma_peak_frac": round(r["tops"] / PEAK_TOPS, 4),
+        "mfma_peak_frac": round(r["tops"] / peak, 4),
         "roofline": roof,
         "breakdown_ms": {"gpu_step": round(r["gpu_ms"], 4), "quant": round(r["quant_ms"], 4),
                          "attention": round(r["attn_ms"], 4), "sage_attn_fwd_single_call": round(r["fused_ms"], 4)},
@@ -352,15 +399,19 @@ def main():
                       "GBps": round(r["quant_bytes"] / (r["quant_ms"] * 1e-3) / 1e9, 1),
                       "frac_of_8TBps": round(r["quant_bytes"] / (r["quant_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
     }
-    if w is W.PEAK and args.qk_gran == "per_block" and not args.no_variants:
-        def variant(rv):
+    if w is W.PEAK and args.qk_gran == "per_block" and pv != "fp4" and not args.no_variants:
+        def variant(rv, pk=PEAK_TOPS):
             return {"value": round(rv["tops"], 2), "ms_per_step": round(rv["wall_ms"], 4),
                     "attention_tops": round(rv["attn_tops"], 2),
-                    "attention_frac": round(rv["attn_tops"] / PEAK_TOPS, 4),
+                    "attention_frac": round(rv["attn_tops"] / pk, 4),
                     "attention_ms": round(rv["attn_ms"], 4), "quant_ms": round(rv["quant_ms"], 4)}
         out["variants"] = {"causal": variant(measure(w.with_(causal=True), pv, args.steps, args.warmup)),
                            "per_thread": variant(measure(w, pv, args.steps, args.warmup, "per_thread")),
-                           "varlen": measure_varlen(W.VARLEN_PREFILL, args.steps, args.warmup)}
+                           "varlen": measure_varlen(W.VARLEN_PREFILL, args.steps, args.warmup),
+                           # the FP4 microscaling variant: attention_frac against the 10.1 PFLOP/s FP4 peak
+                           "fp4": variant(measure(w, "fp4", args.steps, args.warmup), PEAK_FP4_TOPS),
+                           "fp4_causal": variant(measure(w.with_(causal=True), "fp4", args.steps, args.warmup),
+                                                 PEAK_FP4_TOPS)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, pv, args.cpu_rows, args.qk_gran)
         out["cpu_baseline"].update(host_info())
