@@ -44,14 +44,23 @@ PEAK_TOPS = 5000.0            # MI355X dense INT8 and dense FP8 MFMA peak (5.0 P
 PEAK_FP4_TOPS = 10100.0       # MI355X dense FP4 (and FP6) MFMA peak, 10.1 PFLOP/s
 PEAK_HBM_GBS = 8000.0
 ALIASES = {"tiny": W.TINY, "mid": W.MID_OUTLIER, "gqa": W.GQA_CAUSAL, "long": W.LONG_D64, "peak": W.PEAK}
-KERNEL_SOURCES = ["quantized_attention_channel_amd/csrc/attn_kernel.hip",
-                  "quantized_attention_channel_amd/csrc/sage_device.h"]
-COUNTERS_MD = os.path.join(ROOT, "profiles", "attn_fwd_peak_counters.md")
+# The attention kernel's sources and the committed counter summary of each
+# path (INT8/FP8 and FP4): a summary counts only while its hash matches.
+KERNEL_SOURCES = {
+    "int8": ["quantized_attention_channel_amd/csrc/attn_kernel.hip",
+             "quantized_attention_channel_amd/csrc/attn_schedule.h",
+             "quantized_attention_channel_amd/csrc/sage_device.h"],
+    "fp4": ["quantized_attention_channel_amd/csrc/fp4_kernels.hip",
+            "quantized_attention_channel_amd/csrc/attn_schedule.h",
+            "quantized_attention_channel_amd/csrc/sage_device.h"],
+}
+COUNTERS_MD = {"int8": os.path.join(ROOT, "profiles", "attn_fwd_peak_counters.md"),
+               "fp4": os.path.join(ROOT, "profiles", "attn_fp4_peak_counters.md")}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(path: str = "int8") -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[path]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -132,11 +141,12 @@ class Fp4Plan:
         self.full_ws = torch.empty(max(sage.sage_fp4_workspace_bytes(s), 256), dtype=torch.uint8, device=dev)
         self.stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
         P = sage._ptr
-        self.args_quant = (ctypes.byref(s), P(q), P(k), P(v), P(c["q_codes"]), P(c["q_scale"]), P(c["k_codes"]),
+        self.args_quant = (ctypes.byref(s), P(q), P(k), P(v), float(w.sm_scale), P(c["q_codes"]), P(c["q_scale"]),
+                           P(c["k_codes"]),
                            P(c["k_scale"]), P(c["k_mean"]), P(c["v_codes"]), P(c["v_scale"]), P(self.ws),
                            self.ws.numel(), self.stream)
         self.args_attn = (ctypes.byref(s), P(c["q_codes"]), P(c["q_scale"]), P(c["k_codes"]), P(c["k_scale"]),
-                          P(c["v_codes"]), P(c["v_scale"]), P(self.o), int(w.causal), float(w.sm_scale), self.stream)
+                          P(c["v_codes"]), P(c["v_scale"]), P(self.o), int(w.causal), self.stream)
         self.args_full = (ctypes.byref(s), P(q), P(k), P(v), P(self.o), int(w.causal), float(w.sm_scale),
                           P(self.full_ws), self.full_ws.numel(), self.stream)
 
@@ -186,9 +196,11 @@ def counters_traffic(w: W.Workload, pv: str, qk_gran: str):
     """HBM bytes per attention launch and the vector/matrix utilisation from the
     committed rocprofv3 counter summary, or (None, None) when it is missing,
     the kernel sources changed since, or it was taken on another configuration."""
-    if not os.path.exists(COUNTERS_MD):
+    path = "fp4" if pv == "fp4" else "int8"
+    md = COUNTERS_MD[path]
+    if not os.path.exists(md):
         return None, None
-    text = open(COUNTERS_MD).read()
+    text = open(md).read()
     def grab(key):
         m = re.search(rf"^{key}:\s*([0-9A-Za-z_.+-]+)\s*$", text, flags=re.M)
         return m.group(1) if m else None
@@ -196,7 +208,7 @@ def counters_traffic(w: W.Workload, pv: str, qk_gran: str):
                    and grab("counters_pv") == pv and grab("counters_qk_gran") == qk_gran)
     vals = [grab(k) for k in ("fetch_kib_per_dispatch", "write_kib_per_dispatch", "copy_fetch_factor",
                               "copy_write_factor")]
-    if grab("kernel_source_sha256") != kernel_source_hash() or not same_config or any(v is None for v in vals):
+    if grab("kernel_source_sha256") != kernel_source_hash(path) or not same_config or any(v is None for v in vals):
         return None, None
     fetch, write, ff, fw = (float(v) for v in vals)
     util = {k: float(grab(k)) for k in ("valu_busy_pct", "mfma_util_pct") if grab(k) is not None}

@@ -294,9 +294,11 @@ sage_status sage_debug_qk_i32(const sage_shape* s, const int8_t* q_codes, const 
  * [-127, 127] (-127 for a block of zeros); each element is x / 2^exponent
  * rounded half to even, magnitudes above 6 saturating to 6. Codes are packed
  * two per byte, element 2i in the low nibble. K is smoothed by its channel mean
- * first, exactly as in sage_quant_qk (the same k_mean). The attention kernel
- * computes S = Q.K^T on the block-scaled FP4 matrix cores (fp32 sums), the
- * online softmax in the log2 domain over 128-key tiles, P~ to MXFP4 per query
+ * first, exactly as in sage_quant_qk (the same k_mean). Q is scaled before
+ * its quantisation by c = fp32(sm_scale * log2 e) (sm_scale as passed, the
+ * product in double, rounded once), so that the attention kernel's product
+ * S2 = (Q c).K^T on the block-scaled FP4 matrix cores (fp32 sums) is already
+ * in the log2 domain; then the online softmax over 128-key tiles, P~ to MXFP4 per query
  * row and 32 keys of the tile (the row sum adds the values that enter PV),
  * and PV with V in MXFP4, two-level accumulation, O / l in the epilogue.
  * s->qk_gran must be SAGE_QK_PER_BLOCK (0): the MX blocks are fixed; any
@@ -309,8 +311,9 @@ size_t sage_quant_fp4_workspace_bytes(const sage_shape* s);
  * mean and the partials). 0 for an invalid or unsupported shape. */
 size_t sage_fp4_workspace_bytes(const sage_shape* s);
 
-/* MXFP4 quantisation of Q, smoothed K and V, with N = sage_v_codes_stride(Nk):
- *   q_codes [B,Hq,Nq,d/2] u8    q_scale [B,Hq,Nq,d/32] u8: blocks of 32 channels per token
+/* MXFP4 quantisation of Q (times c, see above), smoothed K and V, with
+ * N = sage_v_codes_stride(Nk); sm_scale finite and > 0:
+ *   q_codes [B,Hq,Nq,d/2] u8    q_scale [B,Hq,Nq,d/32] u8: fp32(q * c), blocks of 32 channels per token
  *   k_codes [B,Hkv,Nk,d/2] u8   k_scale [B,Hkv,Nk,d/32] u8: the same on fp32(k - k_mean)
  *   k_mean  [B,Hkv,d] fp32      as in sage_quant_qk
  *   v_codes [B,Hkv,d,N/2] u8    V transposed (keys contiguous per channel), blocks
@@ -319,17 +322,17 @@ size_t sage_fp4_workspace_bytes(const sage_shape* s);
  *                               scales (16-byte aligned); blocks past Nk get 0
  * Codes are in canonical HND order whatever s->layout is. Skips Q when Nq == 0
  * and K/V when Nk == 0 (their pointers may then be NULL). */
-sage_status sage_quant_fp4(const sage_shape* s, const void* q, const void* k, const void* v,
+sage_status sage_quant_fp4(const sage_shape* s, const void* q, const void* k, const void* v, float sm_scale,
                            uint8_t* q_codes, uint8_t* q_scale, uint8_t* k_codes, uint8_t* k_scale,
                            float* k_mean, uint8_t* v_codes, uint8_t* v_scale,
                            void* workspace, size_t workspace_bytes, void* stream);
 
-/* The FP4 attention kernel alone, from codes as sage_quant_fp4 writes them;
- * o, is_causal and sm_scale as for sage_attn_fwd. Needs no workspace. */
+/* The FP4 attention kernel alone, from codes as sage_quant_fp4 writes them
+ * (the softmax temperature is already in the Q codes); o and is_causal as for
+ * sage_attn_fwd. Needs no workspace. */
 sage_status sage_attn_fwd_fp4_codes(const sage_shape* s, const uint8_t* q_codes, const uint8_t* q_scale,
                                     const uint8_t* k_codes, const uint8_t* k_scale, const uint8_t* v_codes,
-                                    const uint8_t* v_scale, void* o, int32_t is_causal, float sm_scale,
-                                    void* stream);
+                                    const uint8_t* v_scale, void* o, int32_t is_causal, void* stream);
 
 /* The whole FP4 forward (quantisation then attention) on `stream`; arguments
  * and errors as for sage_attn_fwd without pv_dtype, the workspace sized by

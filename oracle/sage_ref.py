@@ -71,8 +71,13 @@ Readings where the pages are silent (each also listed in the design notes):
   [R23] the P block scale follows the same rule as every other MX block (shared
        exponent floor(log2 max P~) - 2), and the row sum adds the P values that
        enter the PV product [R16]; the online softmax is unchanged [R14, R15].
-  [R24] scores: S = dequant(Q) . dequant(K)^T (exact here in fp64; the matrix
-       cores sum it in fp32), S2 = fp32(fp32(S) * fp32(sm_scale * log2 e)).
+  [R24] the softmax temperature and log2(e) scale Q before its quantisation:
+       Q' = fp32(Q * c), c = fp32(sm_scale * log2 e), goes to MXFP4, and the
+       product gives log2-domain scores directly: S2 = fp32(dequant(Q') .
+       dequant(K)^T) (exact here in fp64, rounded once; the matrix cores sum it
+       in fp32). In the INT8 method the same factor rides in the dequantisation
+       [R10]; here no per-score multiply is left (the MX scales are powers of
+       two and cannot carry it).
 """
 from __future__ import annotations
 
@@ -405,13 +410,21 @@ def sage_attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, dtype: str, is
 # FP4 microscaling variant (SageAttention3: heatdrop.ai review, "Key
 # highlights"; cnnetsun.cn guide, 序列长度优化技巧) [R22-R24]
 # ---------------------------------------------------------------------------
-def quant_qk_fp4(q: np.ndarray, k: np.ndarray, *, k_mean=None):
-    """Q and smoothed K to MXFP4 along the head dimension [R22]: one E8M0 scale
-    per token and 32 consecutive channels. Returns dict(q4, q_exp, qd, k4,
-    k_exp, kd, k_mean): codes [B,H,N,d] (one E2M1 code per byte), block
-    exponents [B,H,N,d/32], dequantised values (float64)."""
+def fp4_score_factor(sm_scale: float) -> np.float32:
+    """c = fp32(sm_scale * log2 e), applied to Q before its quantisation [R24].
+    sm_scale is taken as fp32 (the type the library's interface carries it in),
+    the product in fp64, rounded once to fp32."""
+    return np.float32(float(np.float32(sm_scale)) * LOG2E)
+
+
+def quant_qk_fp4(q: np.ndarray, k: np.ndarray, *, sm_scale: float, k_mean=None):
+    """Q' = fp32(Q * c) [R24] and smoothed K to MXFP4 along the head dimension
+    [R22]: one E8M0 scale per token and 32 consecutive channels. Returns
+    dict(q4, q_exp, qd, k4, k_exp, kd, k_mean): codes [B,H,N,d] (one E2M1 code
+    per byte), block exponents [B,H,N,d/32], dequantised values (float64)."""
     mu = k_channel_mean(k) if k_mean is None else np.asarray(k_mean, np.float32)
-    q4, qe, qd = mxfp4_quantize(np.asarray(q, np.float32), axis=3)
+    qs = (np.asarray(q, np.float32) * fp4_score_factor(sm_scale)).astype(np.float32)
+    q4, qe, qd = mxfp4_quantize(qs, axis=3)
     k4, ke, kd = mxfp4_quantize(smooth_k(k, mu), axis=3)
     return dict(q4=q4, q_exp=qe, qd=qd, k4=k4, k_exp=ke, kd=kd, k_mean=mu)
 
@@ -433,10 +446,11 @@ def sage_attention_fp4(q, k, v, *, dtype: str, is_causal: bool, sm_scale: float,
                        bkv=None, rows=None, parts=None, return_fp64: bool = False):
     """The FP4 microscaling variant of the forward, step by step [R22-R24].
 
-    K is smoothed as in the INT8 method; Q and K go to MXFP4 along the head
-    dimension, S = dequant(Q) dequant(K)^T (exact in fp64; the matrix cores
-    accumulate it in fp32), S2 = fp32(fp32(S) * fp32(sm_scale * log2 e)); the
-    online softmax is the method's (KV tiles of BKV keys, running max); P~ goes
+    K is smoothed as in the INT8 method; Q' = fp32(Q * fp32(sm_scale * log2 e))
+    and K go to MXFP4 along the head dimension, S2 = fp32(dequant(Q')
+    dequant(K)^T) (exact in fp64, rounded once; the matrix cores accumulate it
+    in fp32); the online softmax is the method's (KV tiles of BKV keys,
+    running max); P~ goes
     to MXFP4 per query row and 32 keys; the row sum adds the dequantised P
     [R16]; PV uses V in MXFP4 per channel and 32 keys, accumulated in two
     levels as before. ``parts``: optional dict from quant_qk_fp4 plus ``vd``.
@@ -453,16 +467,14 @@ def sage_attention_fp4(q, k, v, *, dtype: str, is_causal: bool, sm_scale: float,
     bkv = BKV[d] if bkv is None else bkv
     rows = np.arange(Nq) if rows is None else np.asarray(rows)
     if parts is None:
-        parts = quant_qk_fp4(q, k)
+        parts = quant_qk_fp4(q, k, sm_scale=sm_scale)
         parts["vd"] = quant_v_fp4(v)[2]
-    c = np.float32(float(sm_scale) * LOG2E)                                      # [R24]
     keys = np.arange(Nk)
     out = np.empty((B, Hq, len(rows), d), dtype=np.float64)
     for b in range(B):
         for h in range(Hq):
             g = h // G
-            s = parts["qd"][b, h, rows] @ parts["kd"][b, g].T                   # exact in fp64
-            s2 = (s.astype(np.float32) * c).astype(np.float32)
+            s2 = (parts["qd"][b, h, rows] @ parts["kd"][b, g].T).astype(np.float32)   # [R24]
             if is_causal:
                 s2 = np.where(keys[None, :] > rows[:, None], np.float32(-np.inf), s2)
             o, l = online_softmax_pv(s2, parts["vd"][b, g], bkv=bkv, p_codec=_p_codec_fp4,

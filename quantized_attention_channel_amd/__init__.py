@@ -72,10 +72,10 @@ _SIGNATURES = {
                                          _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "sage_quant_fp4_workspace_bytes": (ctypes.c_size_t, [_c_shape_p]),
     "sage_fp4_workspace_bytes": (ctypes.c_size_t, [_c_shape_p]),
-    "sage_quant_fp4": (ctypes.c_int, [_c_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                      _vp, ctypes.c_size_t, _vp]),
+    "sage_quant_fp4": (ctypes.c_int, [_c_shape_p, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _vp, _vp, ctypes.c_size_t, _vp]),
     "sage_attn_fwd_fp4_codes": (ctypes.c_int, [_c_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32,
-                                               ctypes.c_float, _vp]),
+                                               _vp]),
     "sage_attn_fwd_fp4": (ctypes.c_int, [_c_shape_p, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_float, _vp,
                                          ctypes.c_size_t, _vp]),
 }
@@ -446,26 +446,29 @@ def fp4_buffers(shape: SageShape, device) -> dict:
                 v_scale=torch.empty((B, Hkv, npad // 128, d, 4), **u8))
 
 
-def sage_quant_fp4(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout: str = "HND") -> dict:
-    """MXFP4 quantisation of Q, smoothed K and V; returns fp4_buffers' dict."""
+def sage_quant_fp4(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout: str = "HND",
+                   sm_scale: Optional[float] = None) -> dict:
+    """MXFP4 quantisation of Q (times sm_scale * log2 e), smoothed K and V;
+    returns fp4_buffers' dict."""
     _check_inputs(q, k, v)
     s = shape_of(q, k, tensor_layout)
     if tuple(v.shape) != tuple(k.shape) or v.dtype != q.dtype:
         raise ValueError("v must have k's shape and all inputs one dtype")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(s.head_dim)
     dev = q.device
     out = fp4_buffers(s, dev)
     ws = _workspace(int(lib.sage_quant_fp4_workspace_bytes(_ref(s))), dev)
-    _check(lib.sage_quant_fp4(_ref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(out["q_codes"]), _ptr(out["q_scale"]),
+    _check(lib.sage_quant_fp4(_ref(s), _ptr(q), _ptr(k), _ptr(v), float(sm_scale), _ptr(out["q_codes"]),
+                              _ptr(out["q_scale"]),
                               _ptr(out["k_codes"]), _ptr(out["k_scale"]), _ptr(out["k_mean"]), _ptr(out["v_codes"]),
                               _ptr(out["v_scale"]), _ptr(ws), ws.numel(), _stream(dev)), "sage_quant_fp4")
     return out
 
 
-def sage_attn_fwd_fp4_codes(shape: SageShape, codes: dict, o: torch.Tensor, *, is_causal: bool = False,
-                            sm_scale: Optional[float] = None) -> torch.Tensor:
-    """The FP4 attention kernel alone, from sage_quant_fp4's buffers. Writes into ``o``."""
-    if sm_scale is None:
-        sm_scale = 1.0 / math.sqrt(shape.head_dim)
+def sage_attn_fwd_fp4_codes(shape: SageShape, codes: dict, o: torch.Tensor, *, is_causal: bool = False) -> torch.Tensor:
+    """The FP4 attention kernel alone, from sage_quant_fp4's buffers (the
+    softmax temperature is already in the Q codes). Writes into ``o``."""
     in_dtype = {v: k for k, v in DTYPES.items()}.get(shape.dtype)
     if in_dtype is None:
         raise ValueError(f"shape.dtype must be one of {sorted(DTYPES.values())}, got {shape.dtype}")
@@ -481,8 +484,8 @@ def sage_attn_fwd_fp4_codes(shape: SageShape, codes: dict, o: torch.Tensor, *, i
         _expect(codes.get(name), name, torch.uint8, n, dev)
     _check(lib.sage_attn_fwd_fp4_codes(_ref(shape), _ptr(codes["q_codes"]), _ptr(codes["q_scale"]),
                                        _ptr(codes["k_codes"]), _ptr(codes["k_scale"]), _ptr(codes["v_codes"]),
-                                       _ptr(codes["v_scale"]), _ptr(o), int(bool(is_causal)), float(sm_scale),
-                                       _stream(dev)), "sage_attn_fwd_fp4_codes")
+                                       _ptr(codes["v_scale"]), _ptr(o), int(bool(is_causal)), _stream(dev)),
+           "sage_attn_fwd_fp4_codes")
     return o
 
 

@@ -10,10 +10,12 @@
 // and 32 channels, V per channel and 32 keys, P~ per query row and 32 keys of
 // its tile. Shared exponent of a block: floor(log2 amax) - 2 (the exponent of
 // E2M1's largest value), clamped to E8M0; elements x / 2^exponent rounded half
-// to even, saturating at 6.
+// to even, saturating at 6. Q is scaled by c = sm_scale * log2(e) before it
+// is quantised, so the product yields log2-domain scores with no per-score
+// multiply (the power-of-two block scales cannot carry c).
 //
 // Layouts (codes two per byte, element 2i in the low nibble):
-//   q_codes [B*Hq][Nq][D/2]    q_scale [B*Hq][Nq][D/32]       (E8M0 bytes)
+//   q_codes [B*Hq][Nq][D/2]    q_scale [B*Hq][Nq][D/32]       (E8M0 bytes; of Q * c)
 //   k_codes [B*Hkv][Nk][D/2]   k_scale [B*Hkv][Nk][D/32]
 //   v_codes [B*Hkv][D][n_pad/2] (V^T, keys contiguous, zero past Nk)
 //   v_scale [B*Hkv][n_pad/128][D][4] (per 128-key tile: each channel's four
@@ -66,7 +68,7 @@ __device__ __forceinline__ uint32_t pack8(const float (&x)[8], int byte) {
 template <typename T, int D, bool SMOOTH>
 __global__ __launch_bounds__(256) void quant_rows_fp4_kernel(const uint16_t* __restrict__ x, TensorGeom geo, int H,
                                                              int N, int64_t total_chunks,
-                                                             const float* __restrict__ mean,
+                                                             const float* __restrict__ mean, float mul,
                                                              uint32_t* __restrict__ codes,
                                                              uint8_t* __restrict__ scale) {
   constexpr int CPR = D / 8;      // chunks per row
@@ -91,7 +93,8 @@ __global__ __launch_bounds__(256) void quant_rows_fp4_kernel(const uint16_t* __r
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float f = T::to_f32((uint16_t)(((uint32_t)raw[e / 2]) >> (16 * (e & 1))));
-      if (SMOOTH) f = f - mean[bh * D + col + e];
+      if (SMOOTH) f = f - mean[bh * D + col + e];   // K: smoothed
+      else f = f * mul;                              // Q: times the score factor
       v[e] = f;
       amax = fmaxf(amax, fabsf(f));
     }
@@ -256,9 +259,11 @@ __device__ __forceinline__ f32x16 mfma_fp4(i32x4 a, i32x4 b, f32x16 c, int sa, i
 // S^T for the 128 keys of the staged tile against this wave's 32 queries.
 // qsc: this lane's Q scale bytes, its half's block of each 64-channel step in
 // bytes 0 and 2 (bytes 0 only at D = 64).
+// Every product chain starts from c0 (minus the running row max, one value
+// per lane), so the result is S2 - m.
 template <int D>
 __device__ __forceinline__ void qk_tile(const uint8_t* sk, const uint8_t* sks, const i32x4* qreg, int qsc, int lane,
-                                        f32x16* s) {
+                                        f32x16* s, const f32x16& c0) {
   const int g = lane >> 5, m = lane & 31;
 #pragma unroll
   for (int b = 0; b < kBlocks; ++b) {
@@ -267,7 +272,7 @@ __device__ __forceinline__ void qk_tile(const uint8_t* sk, const uint8_t* sks, c
     if constexpr (D == 128) ksc = (int)(*reinterpret_cast<const uint32_t*>(sks + row * 4) >> (8 * g));
     else ksc = (int)(*reinterpret_cast<const uint16_t*>(sks + row * 2) >> (8 * g));
     const i32x4 k0 = lds16(sk + k_lds_off<D>(row, g));
-    s[b] = mfma_fp4<0, 0>(k0, qreg[0], f32x16{}, ksc, qsc);
+    s[b] = mfma_fp4<0, 0>(k0, qreg[0], c0, ksc, qsc);
     if constexpr (D == 128) {
       const i32x4 k1 = lds16(sk + k_lds_off<D>(row, 2 + g));
       s[b] = mfma_fp4<2, 2>(k1, qreg[1], s[b], ksc, qsc);
@@ -291,10 +296,15 @@ struct PTile {
 };
 
 // Softmax phase of one KV tile (vector ALU work only): mask, online softmax in
-// the log2 domain, P~ to MXFP4. c = sm_scale * log2(e).
+// the log2 domain, P~ to MXFP4. The scores arrive as S2 - m (the product chain
+// started from -m, m the running row max; 0 on the first tile), so while no
+// row of the wave raises its max, P~ = exp2 of them directly. A row whose max
+// rises by delta takes P~ = exp2(x - delta), alpha = exp2(-delta), m += delta,
+// and the chain start of the next tiles moves with it; the subtraction runs
+// only on tiles where some row of the wave moved (a wave-uniform branch).
 template <bool CAUSAL, bool MASK>
-__device__ __forceinline__ void softmax_phase(f32x16* s, int lane, int k0, int qi, int nk, float c, float& m,
-                                              PTile& pt) {
+__device__ __forceinline__ void softmax_phase(f32x16* s, int lane, int k0, int qi, int nk, bool first, float& m,
+                                              f32x16& c0, PTile& pt) {
   const int g = lane >> 5;
   if (MASK) {
     const int lim = (CAUSAL ? min(nk, qi + 1) : nk) - k0 - 32 * g;
@@ -320,28 +330,34 @@ __device__ __forceinline__ void softmax_phase(f32x16* s, int lane, int k0, int q
     }
     bm[u] = fmaxf(a0, a1);
   }
-  const float m_new = fmaxf(m, pair_max(fmaxf(bm[0], bm[1]) * c));
-  pt.alpha = fast_exp2(m - m_new);
-  m = m_new;
-  const float nb = -m_new;
-  // Each block's scale from its largest P~, exp2(fp32(max S * c) - m): the
-  // product rounded first, as the row max was, so the block holding the row
-  // max has a largest P~ of exactly 1. (A fused multiply-add keeps the
-  // product's rounding error, which can leave that P~ an ulp below 1 and the
-  // block's shared exponent one lower.) The P~ themselves use the fused form;
-  // they differ from the rounded-product values by an ulp, and the max still
-  // maps to code 4.
+  const float mt = pair_max(fmaxf(bm[0], bm[1]));        // the tile's row max, relative to m
+  const float delta = first ? mt : fmaxf(mt, 0.0f);
+  pt.alpha = first ? 0.0f : fast_exp2(-delta);           // (O and l are still zero on the first tile)
+  // (the chain start is rewritten on every tile: kept inside the branch, its
+  //  sixteen registers become a merge of two values and cost more than the
+  //  moves)
+  m = (first ? 0.0f : m) + delta;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) c0[e] = -m;
+  if (__builtin_amdgcn_ballot_w64(delta != 0.0f) != 0) {
+#pragma unroll
+    for (int b = 0; b < kBlocks; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[b][e] -= delta;
+  }
+  // Each block's scale from its largest P~ (the same expression as that
+  // element's own P~: the block holding the row max gets exactly 1)
   int sb[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const float pmax = fast_exp2(bm[u] * c - m_new);
+    const float pmax = fast_exp2(bm[u] - delta);
     const int e = mx_scale_byte(pmax);
     sb[u] = e > 1 ? e : 1;          // (a block of zeros: any scale; keep the conversion's scale normal)
   }
 #pragma unroll
   for (int b = 0; b < kBlocks; ++b)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) s[b][e] = fast_exp2(__builtin_fmaf(s[b][e], c, nb));
+    for (int e = 0; e < 16; ++e) s[b][e] = fast_exp2(s[b][e]);
   // E2M1 codes: dword w of pk[u] holds elements 8w..8w+7 = block 2u + w/2,
   // entries 8(w%2)..+7; the conversion divides by 2^floor(log2 scale).
 #pragma unroll
@@ -364,6 +380,7 @@ __device__ __forceinline__ void softmax_phase(f32x16* s, int lane, int k0, int q
   pin(pt.psc);
   pin(pt.alpha);
   pin(m);
+  pin(c0);
 }
 
 template <int D>
@@ -463,8 +480,6 @@ __global__ __launch_bounds__(512, 1) void attn_fp4_kernel(Fp4AttnArgs a) {
     if constexpr (D == 128) qsc = __builtin_amdgcn_raw_buffer_load_b32(rqs, (uint32_t)qi * 4, 0, 0) >> (8 * g);
     else qsc = (__builtin_amdgcn_raw_buffer_load_b16(rqs, (uint32_t)qi * 2, 0, 0) >> (8 * g)) & 0xff;
   }
-  const float c = a.scale_log2;
-
   auto tiles_for = [&](int q_tile) {
     const int kv_end = CAUSAL ? min(nk, (q_tile + 1) * kBq) : nk;
     return (kv_end + kBkv - 1) / kBkv;
@@ -493,10 +508,14 @@ __global__ __launch_bounds__(512, 1) void attn_fp4_kernel(Fp4AttnArgs a) {
   RowState<D> st;
 #pragma unroll
   for (int cb = 0; cb < NT; ++cb) st.o[cb] = f32x16{};
-  st.m = -INFINITY;
+  st.m = 0.0f;
   st.l = 0.0f;
   f32x16 s[kBlocks];
   PTile pt;
+  // The start of every product chain, -m (opaque, so that it is not rebuilt
+  // per tile).
+  f32x16 c0 = {};
+  pin(c0);
 
   auto kbuf = [&](int p) { return smem + p * kK; };
   auto vbuf = [&](int p) { return smem + 2 * kK + p * kV; };
@@ -530,7 +549,7 @@ __global__ __launch_bounds__(512, 1) void attn_fp4_kernel(Fp4AttnArgs a) {
     if (do_pv) pv_phase<D>(vbuf(1 - P), vsbuf(1 - P), lane, pt, st, hook);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
-    if (do_qk) qk_tile<D>(kbuf(P), ksbuf(P), qreg, qsc, lane, s);
+    if (do_qk) qk_tile<D>(kbuf(P), ksbuf(P), qreg, qsc, lane, s, c0);
   };
   auto x_phase = [&](auto par, int t, bool do_pv, bool do_qk) __attribute__((always_inline)) {
     x_bufs(decltype(par)::value, do_pv, do_qk, NoHook{});
@@ -558,7 +577,7 @@ __global__ __launch_bounds__(512, 1) void attn_fp4_kernel(Fp4AttnArgs a) {
   };
   auto y_phase = [&](int t, auto masked) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(0);
-    softmax_phase<CAUSAL, decltype(masked)::value>(s, lane, t * kBkv, qi, nk, c, st.m, pt);
+    softmax_phase<CAUSAL, decltype(masked)::value>(s, lane, t * kBkv, qi, nk, t == 0, st.m, c0, pt);
   };
   static_assert(2 * NT >= St::kKLoads + 1 && 2 * NT >= St::kVLoads + 1, "one PV product per load instruction");
   run_pingpong(grp, n_g, n_wg, x_phase, x_phase_loading, x_phase_rt, y_phase, loads_k, loads_v, loads_k_rt,
@@ -606,14 +625,14 @@ static hipError_t launch_quant_fp4_t(const Fp4QuantArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
     const int64_t kchunks = (int64_t)a.B * a.Hkv * a.Nk * (D / 8);
     hipLaunchKernelGGL((fp4::quant_rows_fp4_kernel<T, D, true>), dim3(row_wgs(kchunks)),
-                       dim3(256), 0, st, (const uint16_t*)a.k, a.kgeo, a.Hkv, a.Nk, kchunks, a.k_mean,
+                       dim3(256), 0, st, (const uint16_t*)a.k, a.kgeo, a.Hkv, a.Nk, kchunks, a.k_mean, 1.0f,
                        (uint32_t*)a.k_codes, a.k_scale);
   }
   if (a.Nq > 0) {
     const int64_t qchunks = (int64_t)a.B * a.Hq * a.Nq * (D / 8);
     hipLaunchKernelGGL((fp4::quant_rows_fp4_kernel<T, D, false>), dim3(row_wgs(qchunks)),
                        dim3(256), 0, st, (const uint16_t*)a.q, a.qgeo, a.Hq, a.Nq, qchunks, (const float*)nullptr,
-                       (uint32_t*)a.q_codes, a.q_scale);
+                       a.q_mul, (uint32_t*)a.q_codes, a.q_scale);
   }
   if (a.n_pad > 0)
     hipLaunchKernelGGL((fp4::quant_v_fp4_kernel<T, D>), dim3(a.n_pad / kBkv, a.B * a.Hkv), dim3(256), 0, st,

@@ -473,9 +473,13 @@ sage_status check_fp4_shape(const sage_shape* s, Dims* d) {
   return SAGE_OK;
 }
 
-sage::Fp4QuantArgs fp4_quant_args(const Dims& d, const void* q, const void* k, const void* v, uint8_t* q_codes,
-                                  uint8_t* q_scale, uint8_t* k_codes, uint8_t* k_scale, float* k_mean,
-                                  uint8_t* v_codes, uint8_t* v_scale, double* ksum) {
+// The factor Q is scaled by before its quantisation: fp32(sm_scale * log2 e),
+// the product taken in double and rounded once.
+float fp4_score_factor(float sm_scale) { return (float)((double)sm_scale * 1.4426950408889634); }
+
+sage::Fp4QuantArgs fp4_quant_args(const Dims& d, const void* q, const void* k, const void* v, float sm_scale,
+                                  uint8_t* q_codes, uint8_t* q_scale, uint8_t* k_codes, uint8_t* k_scale,
+                                  float* k_mean, uint8_t* v_codes, uint8_t* v_scale, double* ksum) {
   sage::Fp4QuantArgs a{};
   a.q = q;
   a.k = k;
@@ -486,6 +490,7 @@ sage::Fp4QuantArgs fp4_quant_args(const Dims& d, const void* q, const void* k, c
   a.B = int(d.B), a.Hq = int(d.Hq), a.Hkv = int(d.Hkv), a.Nq = int(d.Nq), a.Nk = int(d.Nk), a.D = int(d.D);
   a.n_pad = int(round_up(d.Nk, sage::kVPad));
   a.bf16 = d.bf16;
+  a.q_mul = fp4_score_factor(sm_scale);
   a.q_codes = q_codes;
   a.q_scale = q_scale;
   a.k_codes = k_codes;
@@ -499,7 +504,7 @@ sage::Fp4QuantArgs fp4_quant_args(const Dims& d, const void* q, const void* k, c
 
 sage::Fp4AttnArgs fp4_attn_args(const Dims& d, const uint8_t* q_codes, const uint8_t* q_scale,
                                 const uint8_t* k_codes, const uint8_t* k_scale, const uint8_t* v_codes,
-                                const uint8_t* v_scale, void* o, int32_t is_causal, float sm_scale) {
+                                const uint8_t* v_scale, void* o, int32_t is_causal) {
   sage::Fp4AttnArgs a{};
   a.q4 = q_codes;
   a.q_sc = q_scale;
@@ -511,7 +516,6 @@ sage::Fp4AttnArgs fp4_attn_args(const Dims& d, const uint8_t* q_codes, const uin
   a.ogeo = geom(d, d.Hq, d.Nq);
   a.B = int(d.B), a.Hq = int(d.Hq), a.Hkv = int(d.Hkv), a.Nq = int(d.Nq), a.Nk = int(d.Nk), a.D = int(d.D);
   a.n_pad = int(round_up(d.Nk, sage::kVPad));
-  a.scale_log2 = sm_scale * sage::kLog2E;
   a.causal = is_causal != 0;
   a.bf16 = d.bf16;
   return a;
@@ -869,12 +873,14 @@ size_t sage_fp4_workspace_bytes(const sage_shape* s) {
   return check_fp4_shape(s, &d) == SAGE_OK ? fp4_layout_for(d).total : 0;
 }
 
-sage_status sage_quant_fp4(const sage_shape* s, const void* q, const void* k, const void* v, uint8_t* q_codes,
-                           uint8_t* q_scale, uint8_t* k_codes, uint8_t* k_scale, float* k_mean, uint8_t* v_codes,
-                           uint8_t* v_scale, void* workspace, size_t workspace_bytes, void* stream) {
+sage_status sage_quant_fp4(const sage_shape* s, const void* q, const void* k, const void* v, float sm_scale,
+                           uint8_t* q_codes, uint8_t* q_scale, uint8_t* k_codes, uint8_t* k_scale, float* k_mean,
+                           uint8_t* v_codes, uint8_t* v_scale, void* workspace, size_t workspace_bytes,
+                           void* stream) {
   Dims d;
   sage_status st = check_fp4_shape(s, &d);
   if (st != SAGE_OK) return st;
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_INVALID_ARGUMENT;
   if (d.B == 0 || (d.Nq == 0 && d.Nk == 0)) return SAGE_OK;
   const bool has_q = d.Nq > 0, has_k = d.Nk > 0;
   if (has_q && (!q || !q_codes || !q_scale)) return SAGE_ERR_INVALID_ARGUMENT;
@@ -892,8 +898,8 @@ sage_status sage_quant_fp4(const sage_shape* s, const void* q, const void* k, co
                {v_scale, has_k ? z.v_scale : 0}, {workspace, has_k ? qk_ws_bytes(d) : 0}},
               {{q, qin}, {k, kin}, {v, kin}}))
     return SAGE_ERR_INVALID_ARGUMENT;
-  sage::Fp4QuantArgs a = fp4_quant_args(d, q, k, v, q_codes, q_scale, k_codes, k_scale, k_mean, v_codes, v_scale,
-                                        static_cast<double*>(workspace));
+  sage::Fp4QuantArgs a = fp4_quant_args(d, q, k, v, sm_scale, q_codes, q_scale, k_codes, k_scale, k_mean, v_codes,
+                                        v_scale, static_cast<double*>(workspace));
   if (!has_q) a.Nq = 0;
   if (!has_k) a.Nk = 0, a.n_pad = 0;
   return from_hip(sage::launch_quant_fp4(a, static_cast<hipStream_t>(stream)));
@@ -901,13 +907,11 @@ sage_status sage_quant_fp4(const sage_shape* s, const void* q, const void* k, co
 
 sage_status sage_attn_fwd_fp4_codes(const sage_shape* s, const uint8_t* q_codes, const uint8_t* q_scale,
                                     const uint8_t* k_codes, const uint8_t* k_scale, const uint8_t* v_codes,
-                                    const uint8_t* v_scale, void* o, int32_t is_causal, float sm_scale,
-                                    void* stream) {
+                                    const uint8_t* v_scale, void* o, int32_t is_causal, void* stream) {
   Dims d;
   sage_status st = check_fp4_shape(s, &d);
   if (st != SAGE_OK) return st;
   if (is_causal != 0 && is_causal != 1) return SAGE_ERR_INVALID_ARGUMENT;
-  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_INVALID_ARGUMENT;
   if (d.B == 0 || d.Nq == 0) return SAGE_OK;
   if (d.Nk == 0) return SAGE_ERR_INVALID_ARGUMENT;
   if (is_causal && d.Nq != d.Nk) return SAGE_ERR_UNSUPPORTED;
@@ -921,7 +925,7 @@ sage_status sage_attn_fwd_fp4_codes(const sage_shape* s, const uint8_t* q_codes,
                {v_codes, z.v_codes}, {v_scale, z.v_scale}}))
     return SAGE_ERR_INVALID_ARGUMENT;
   return from_hip(sage::launch_attn_fp4(
-      fp4_attn_args(d, q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, o, is_causal, sm_scale),
+      fp4_attn_args(d, q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, o, is_causal),
       static_cast<hipStream_t>(stream)));
 }
 
@@ -942,13 +946,13 @@ sage_status sage_attn_fwd_fp4(const sage_shape* s, const void* q, const void* k,
     return SAGE_ERR_INVALID_ARGUMENT;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const sage::Fp4QuantArgs qa =
-      fp4_quant_args(d, q, k, v, at<uint8_t>(workspace, L.q_codes), at<uint8_t>(workspace, L.q_scale),
+      fp4_quant_args(d, q, k, v, sm_scale, at<uint8_t>(workspace, L.q_codes), at<uint8_t>(workspace, L.q_scale),
                      at<uint8_t>(workspace, L.k_codes), at<uint8_t>(workspace, L.k_scale),
                      at<float>(workspace, L.k_mean), at<uint8_t>(workspace, L.v_codes),
                      at<uint8_t>(workspace, L.v_scale), at<double>(workspace, L.ksum));
   if (sage::launch_quant_fp4(qa, hs) != hipSuccess) return SAGE_ERR_HIP;
   return from_hip(sage::launch_attn_fp4(fp4_attn_args(d, qa.q_codes, qa.q_scale, qa.k_codes, qa.k_scale,
-                                                      qa.v_codes, qa.v_scale, o, is_causal, sm_scale),
+                                                      qa.v_codes, qa.v_scale, o, is_causal),
                                         hs));
 }
 

@@ -99,6 +99,7 @@ struct Fp4QuantArgs {
   TensorGeom qgeo, kgeo, vgeo;
   int B, Hq, Hkv, Nq, Nk, n_pad, D;
   bool bf16;
+  float q_mul;         // Q is quantised as fp32(q * q_mul): the score factor sm_scale * log2(e)
   uint8_t* q_codes;    // [B*Hq][Nq][D/2]
   uint8_t* q_scale;    // [B*Hq][Nq][D/32]
   uint8_t* k_codes;    // [B*Hkv][Nk][D/2]
@@ -118,8 +119,7 @@ struct Fp4AttnArgs {
   const uint8_t* v_sc;
   void* o;
   TensorGeom ogeo;
-  int B, Hq, Hkv, Nq, Nk, n_pad, D;
-  float scale_log2;     // sm_scale * log2(e)
+  int B, Hq, Hkv, Nq, Nk, n_pad, D;   // (the score factor is already in the Q codes)
   bool causal, bf16;
 };
 

@@ -283,17 +283,20 @@ def test_fp4_entry_points_validate():
     qc, qs, kc, ks, km, vc, vs = (FAKE + i * G for i in range(4, 11))
     qw = sage.lib.sage_quant_fp4_workspace_bytes(sp)
     quant = sage.lib.sage_quant_fp4
-    assert quant(sp, q, k, v, None, qs, kc, ks, km, vc, vs, ws, qw, None) == bad
-    assert quant(sp, q, k, v, qc, qs, kc, ks, km, vc, vs + 4, ws, qw, None) == bad   # v_scale needs 16 bytes
-    assert quant(sp, q, k, v, qc, qs, kc, ks, km, vc, vs, ws, qw - 1, None) == sage.SAGE_ERR_WORKSPACE
-    assert quant(sp, q, k, v, qc, qs, kc, ks, km, v + 4096, vs, ws, qw, None) == bad  # codes on v
-    assert quant(sp, q, k, v, qc, qs, kc, qc + 16, km, vc, vs, ws, qw, None) == bad   # k scale on q codes
+    assert quant(sp, q, k, v, 0.1, None, qs, kc, ks, km, vc, vs, ws, qw, None) == bad
+    assert quant(sp, q, k, v, 0.1, qc, qs, kc, ks, km, vc, vs + 4, ws, qw, None) == bad   # v_scale needs 16 bytes
+    assert quant(sp, q, k, v, 0.1, qc, qs, kc, ks, km, vc, vs, ws, qw - 1, None) == sage.SAGE_ERR_WORKSPACE
+    assert quant(sp, q, k, v, 0.1, qc, qs, kc, ks, km, v + 4096, vs, ws, qw, None) == bad  # codes on v
+    assert quant(sp, q, k, v, 0.1, qc, qs, kc, qc + 16, km, vc, vs, ws, qw, None) == bad   # k scale on q codes
+    assert quant(sp, q, k, v, float("inf"), qc, qs, kc, ks, km, vc, vs, ws, qw, None) == bad
+    assert quant(sp, q, k, v, -0.1, qc, qs, kc, ks, km, vc, vs, ws, qw, None) == bad
     # attention from codes: o may not cover what it reads; v_scale 16-byte aligned
     codes = sage.lib.sage_attn_fwd_fp4_codes
     for oo in (qs, ks, vs, vc + 4096):
-        assert codes(sp, qc, qs, kc, ks, vc, vs, oo, 0, 0.1, None) == bad
-    assert codes(sp, qc, qs, kc, ks, vc, vs + 4, o, 0, 0.1, None) == bad
-    assert codes(sp, qc, qs, kc, ks, None, vs, o, 0, 0.1, None) == bad
+        assert codes(sp, qc, qs, kc, ks, vc, vs, oo, 0, None) == bad
+    assert codes(sp, qc, qs, kc, ks, vc, vs + 4, o, 0, None) == bad
+    assert codes(sp, qc, qs, kc, ks, None, vs, o, 0, None) == bad
+    assert codes(sp, qc, qs, kc, ks, vc, vs, o, 3, None) == bad
 
 
 def test_python_wrapper_rejects_unsupported_sdpa_arguments():

@@ -8,17 +8,23 @@ import workloads as W
 
 
 def test_counters_attach_only_to_their_own_configuration():
+    import os
     import re
-    text = open(bench.COUNTERS_MD).read()
-    recorded = re.search(r"^kernel_source_sha256:\s*(\S+)", text, flags=re.M).group(1)
-    traffic, util = bench.counters_traffic(W.PEAK, "fp8", "per_block")
-    if recorded == bench.kernel_source_hash():
-        assert traffic is not None and traffic > 0
-        assert set(util) == {"valu_busy_pct", "mfma_util_pct"} and all(0 < v <= 100 for v in util.values())
-    else:                                                  # sources changed since: no stale counters
-        assert (traffic, util) == (None, None)
+    for path, pv in (("int8", "fp8"), ("fp4", "fp4")):
+        if not os.path.exists(bench.COUNTERS_MD[path]):
+            assert bench.counters_traffic(W.PEAK, pv, "per_block") == (None, None)
+            continue
+        text = open(bench.COUNTERS_MD[path]).read()
+        recorded = re.search(r"^kernel_source_sha256:\s*(\S+)", text, flags=re.M).group(1)
+        traffic, util = bench.counters_traffic(W.PEAK, pv, "per_block")
+        if recorded == bench.kernel_source_hash(path):
+            assert traffic is not None and traffic > 0
+            assert set(util) == {"valu_busy_pct", "mfma_util_pct"} and all(0 < v <= 100 for v in util.values())
+        else:                                              # sources changed since: no stale counters
+            assert (traffic, util) == (None, None)
     for w, pv, gran in [(W.PEAK.with_(causal=True), "fp8", "per_block"), (W.PEAK, "fp16", "per_block"),
-                        (W.PEAK, "fp8", "per_thread"), (W.MID_OUTLIER, "fp8", "per_block")]:
+                        (W.PEAK, "fp8", "per_thread"), (W.MID_OUTLIER, "fp8", "per_block"),
+                        (W.PEAK.with_(causal=True), "fp4", "per_block")]:
         assert bench.counters_traffic(w, pv, gran) == (None, None)
 
 

@@ -46,9 +46,9 @@ def _unpack(packed):
     return out
 
 
-def check_fp4_stages(got, qn, kn, vn):
+def check_fp4_stages(got, qn, kn, vn, sm_scale):
     """Every MXFP4 stage bit for bit; returns the oracle's parts (with vd)."""
-    parts = sage_ref.quant_qk_fp4(qn, kn)
+    parts = sage_ref.quant_qk_fp4(qn, kn, sm_scale=sm_scale)
     v4, vexp, vd = sage_ref.quant_v_fp4(vn)
     N = kn.shape[2]
     assert np.array_equal(got["k_mean"].cpu().numpy().view(np.uint32), parts["k_mean"].view(np.uint32))
@@ -82,9 +82,9 @@ QUANT_CASES = [
 def test_fp4_quant_stages_bit_exact(sage, w):
     say("fp4 quant", w)
     q, k, v = W.generate(w)
-    got = sage.sage_quant_fp4(q.cuda(), k.cuda(), v.cuda(), tensor_layout=w.layout)
+    got = sage.sage_quant_fp4(q.cuda(), k.cuda(), v.cuda(), tensor_layout=w.layout, sm_scale=w.sm_scale)
     torch.cuda.synchronize()
-    check_fp4_stages(got, *(_hnd(t, w.layout) for t in (q, k, v)))
+    check_fp4_stages(got, *(_hnd(t, w.layout) for t in (q, k, v)), w.sm_scale)
 
 
 def test_fp4_quant_scale_edges(sage):
@@ -100,10 +100,13 @@ def test_fp4_quant_scale_edges(sage):
             np.tile([2.0 ** -130, -(2.0 ** -131)], d // 2), tie_row[::-1] * 3.0, tie_row * 1e4]
     x = np.array(rows, np.float32)
     t = torch.from_numpy(x).to(torch.bfloat16).reshape(1, 1, x.shape[0], d)
-    got = sage.sage_quant_fp4(t.cuda(), t.cuda(), t.cuda())
-    torch.cuda.synchronize()
-    tn = t.float().numpy()
-    check_fp4_stages(got, tn, tn, tn)
+    # score factor exactly 1 (Q's blocks hit the listed edges unscaled), then
+    # an ordinary one
+    for sm in (1.0 / sage_ref.LOG2E, 0.125):
+        got = sage.sage_quant_fp4(t.cuda(), t.cuda(), t.cuda(), sm_scale=sm)
+        torch.cuda.synchronize()
+        tn = t.float().numpy()
+        check_fp4_stages(got, tn, tn, tn, sm)
 
 
 ATTN_CASES = [
@@ -150,9 +153,9 @@ def test_fp4_codes_entry_equals_whole_forward(sage):
     w = W.TINY.with_(Hq=4, Hkv=2, N=300, d=128, dtype="bf16")
     q, k, v = (t.cuda() for t in W.generate(w))
     whole = sage.sage_attn_fwd_fp4(q, k, v, is_causal=True, sm_scale=w.sm_scale)
-    codes = sage.sage_quant_fp4(q, k, v)
+    codes = sage.sage_quant_fp4(q, k, v, sm_scale=w.sm_scale)
     o = torch.empty_like(q)
-    sage.sage_attn_fwd_fp4_codes(sage.shape_of(q, k, "HND"), codes, o, is_causal=True, sm_scale=w.sm_scale)
+    sage.sage_attn_fwd_fp4_codes(sage.shape_of(q, k, "HND"), codes, o, is_causal=True)
     torch.cuda.synchronize()
     assert torch.equal(o, whole)
     again = sage.sage_attn_fwd_fp4(q, k, v, is_causal=True, sm_scale=w.sm_scale)
@@ -198,7 +201,7 @@ def test_fp4_full_size_peak_workload(sage):
     q, k, v = W.generate(w)
     qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
     o = sage.sage_attn_fwd_fp4(qg, kg, vg, is_causal=w.causal, sm_scale=w.sm_scale, tensor_layout=w.layout)
-    codes = sage.sage_quant_fp4(qg, kg, vg, tensor_layout=w.layout)
+    codes = sage.sage_quant_fp4(qg, kg, vg, tensor_layout=w.layout, sm_scale=w.sm_scale)
     torch.cuda.synchronize()
     del qg, kg, vg
     rows = rows_per_head(w.N, w.B * w.Hq)
@@ -208,7 +211,7 @@ def test_fp4_full_size_peak_workload(sage):
     for h in range(w.Hq):
         sl = slice(h, h + 1)
         one = {name: t[:, sl] for name, t in codes.items()}
-        parts = check_fp4_stages(one, qa[:, sl], ka[:, sl], va[:, sl])
+        parts = check_fp4_stages(one, qa[:, sl], ka[:, sl], va[:, sl], w.sm_scale)
         r = sage_ref.sage_attention_fp4(qa[:, sl], ka[:, sl], va[:, sl], dtype=w.dtype, is_causal=w.causal,
                                         sm_scale=w.sm_scale, rows=rows[h], parts=parts)
         ref.append(r[0, 0])

@@ -226,10 +226,19 @@ def test_mx_representable_operands_pass_unchanged():
     q = _mx_exact((1, 2, 100, 64), 3, rng)
     v = _mx_exact((1, 2, 100, 64), 2, rng)
     k = _mx_exact((1, 2, 100, 64), 3, rng)
-    parts = sage_ref.quant_qk_fp4(q, k, k_mean=np.zeros((1, 2, 64), np.float32))
+    # sm_scale = 1 / log2(e): the score factor applied to Q is exactly 1
+    unit = 1.0 / sage_ref.LOG2E
+    assert sage_ref.fp4_score_factor(unit) == np.float32(1.0)
+    parts = sage_ref.quant_qk_fp4(q, k, sm_scale=unit, k_mean=np.zeros((1, 2, 64), np.float32))
     np.testing.assert_array_equal(parts["qd"], q)
     np.testing.assert_array_equal(parts["kd"], k)
     np.testing.assert_array_equal(sage_ref.quant_v_fp4(v)[2], v)
+    # the score factor scales Q before the quantisation: Q * 2 (a power of two)
+    # gives the same codes one exponent up, and dequantises to 2 Q exactly
+    two = sage_ref.quant_qk_fp4(q, k, sm_scale=2.0 * unit, k_mean=np.zeros((1, 2, 64), np.float32))
+    np.testing.assert_array_equal(two["q4"], parts["q4"])
+    np.testing.assert_array_equal(two["q_exp"], parts["q_exp"] + 1)
+    np.testing.assert_array_equal(two["qd"], 2.0 * q)
     # and the Q = 0 closed form then reaches the plain mean of V
     out = _fp4(np.zeros_like(q), k, v, False)
     np.testing.assert_allclose(out[0, 0], np.broadcast_to(v[0, 0].astype(np.float64).mean(axis=0), (100, 64)),
@@ -338,9 +347,10 @@ def test_planted_mistakes_are_caught(monkeypatch):
     # 7. Q blocked along the tokens instead of the channels
     orig_qk = sage_ref.quant_qk_fp4
     with monkeypatch.context() as m:
-        def qk_token_blocks(q, k, *, k_mean=None):
-            p = orig_qk(q, k, k_mean=k_mean)
-            p["q4"], p["q_exp"], p["qd"] = mx.mxfp4_quantize(np.asarray(q, np.float32), axis=2)
+        def qk_token_blocks(q, k, *, sm_scale, k_mean=None):
+            p = orig_qk(q, k, sm_scale=sm_scale, k_mean=k_mean)
+            qs = (np.asarray(q, np.float32) * sage_ref.fp4_score_factor(sm_scale)).astype(np.float32)
+            p["q4"], p["q_exp"], p["qd"] = mx.mxfp4_quantize(qs, axis=2)
             return p
         m.setattr(sage_ref, "quant_qk_fp4", qk_token_blocks)
         assert _fails(test_mx_representable_operands_pass_unchanged)
