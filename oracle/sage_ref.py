@@ -42,7 +42,12 @@ Readings where the pages are silent (each also listed in the design notes):
        multiplied with the unquantised V.
   [R14] the online softmax walks KV tiles of BKV keys from key 0 upward; BKV
        is part of the method's definition (P codes depend on the running max).
-  [R15] level-1 accumulation spans one KV tile; level 2 is O = alpha*O + R.
+  [R15] two-level accumulation: level 1 sums the products of a group of keys
+       (here one KV tile, R = P . V_tile; the GPU kernel's level 1 is one matrix
+       instruction, 64 keys in FP8 mode), level 2 is O = alpha*O + R in a wider
+       accumulator. The e4m3 products are exact and their sums fit in fp64, so
+       the span of level 1 changes no value here; on the GPU it changes fp32
+       rounding only.
   [R16] the row sum l accumulates the P values that enter the PV product (the
        e4m3 values of 448 * P~ in FP8 mode, the fp16/bf16-rounded P~ in FP16
        mode), so the output is normalised by the weights actually applied;
