@@ -250,6 +250,60 @@ def cpu_baseline(w: W.Workload, pv: str, rows: int, qk_gran: str = "per_block"):
                        f"TOPS counted as 4*rows*N*d{' (causal: visible keys only)' if w.causal else ''}")}
 
 
+def cpu_configs(rows_sample: int = 512):
+    """The oracle on the host cores for every workload (one JSON line each).
+
+    The tiny and the outlier workload run in full. The GQA causal, d = 64 and
+    peak workloads run their quantisation in full and attention for
+    `rows_sample` query rows of every (batch, head) plus the edge rows; their
+    whole-workload time is an extrapolation, t_quant + t_rows * (all visible
+    pairs / sampled visible pairs), and is labelled as such."""
+    import numpy as np
+    from oracle import sage_ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    for w in (W.TINY, W.MID_OUTLIER, W.GQA_CAUSAL, W.LONG_D64, W.PEAK):
+        full = w in (W.TINY, W.MID_OUTLIER)
+        q, k, v = W.generate(w)
+        qn, kn, vn = (sage_ref.as_hnd(t.float().numpy(), w.layout) for t in (q, k, v))
+        t0 = time.perf_counter()
+        parts = sage_ref.quant_qk(qn, kn)
+        if w.pv == "fp8":
+            parts["v8"], parts["v_scale"] = sage_ref.quant_v_fp8(vn)
+        t_quant = time.perf_counter() - t0
+        if full:
+            rows = np.arange(w.N)
+        else:
+            rows = np.unique(np.concatenate([np.linspace(0, w.N - 1, rows_sample).round().astype(np.int64),
+                                             [0, 1, w.N - 2, w.N - 1]]))
+        G = w.Hq // w.Hkv
+        t1 = time.perf_counter()
+        for b in range(w.B):
+            for h in range(w.Hq):
+                g = h // G
+                sub = {"q8": parts["q8"][b:b + 1, h:h + 1], "q_scale": parts["q_scale"][b:b + 1, h:h + 1],
+                       "k8": parts["k8"][b:b + 1, g:g + 1], "k_scale": parts["k_scale"][b:b + 1, g:g + 1]}
+                if w.pv == "fp8":
+                    sub["v8"], sub["v_scale"] = parts["v8"][b:b + 1, g:g + 1], parts["v_scale"][b:b + 1, g:g + 1]
+                sage_ref.sage_attention(qn[b:b + 1, h:h + 1], kn[b:b + 1, g:g + 1], vn[b:b + 1, g:g + 1],
+                                        dtype=w.dtype, is_causal=w.causal, sm_scale=w.sm_scale, pv=w.pv, rows=rows,
+                                        parts=sub)
+            print(f"  oracle {w.name}: batch {b} done ({time.perf_counter() - t1:.0f} s)", file=sys.stderr, flush=True)
+        t_rows = time.perf_counter() - t1
+        pairs = lambda r: float((r + 1).sum()) if w.causal else float(len(r)) * w.N   # visible (query, key) pairs
+        frac = pairs(rows) / pairs(np.arange(w.N))
+        t_total = t_quant + t_rows / frac
+        rec = {"workload": w.name, "pv": w.pv, "causal": w.causal, "cores": int(threads),
+               "quant_s": round(t_quant, 2), "attention_rows": int(len(rows)), "attention_s": round(t_rows, 2),
+               "kind": "measured in full" if full else "extrapolated: quant in full + sampled rows scaled by visible pairs",
+               "seconds_whole_workload": round(t_total, 1),
+               "TOPS": w.attention_ops() / t_total / 1e12}
+        print(json.dumps(rec), flush=True)
+
+
 def copy_calibration():
     """A plain device copy of known size, for scaling HBM byte counters."""
     n = 1 << 30
@@ -359,7 +413,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=8192)
     ap.add_argument("--copy-calibration", action="store_true", help="run only a 1 GiB device copy")
+    ap.add_argument("--cpu-configs", action="store_true",
+                    help="time only the CPU oracle on every workload (no GPU; several minutes)")
     args = ap.parse_args()
+    if args.cpu_configs:
+        cpu_configs()
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the quantised attention "
