@@ -38,22 +38,26 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
-    objs = [os.path.join(OBJ, s.replace(".hip", ".o")) for s in SOURCES]
-    cmds = [[HIPCC, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+def build(verbose: bool = False, defines=(), lib: str = LIB, obj: str = OBJ) -> str:
+    """Compile every source for gfx950 and link `lib`. `defines` (NAME=VALUE
+    strings) build a variant, e.g. the phase-trace diagnostic library, into its
+    own object directory and library path."""
+    os.makedirs(obj, exist_ok=True)
+    objs = [os.path.join(obj, s.replace(".hip", ".o")) for s in SOURCES]
+    dflags = [f"-D{d}" for d in defines]
+    cmds = [[HIPCC, *FLAGS, *dflags, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
     with cf.ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1)) as ex:
         outs = list(ex.map(_run, cmds))
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     # -z defs: a symbol left undefined (e.g. a kernel stub the host pass did not
     # emit) fails the link here instead of the first dlopen
     outs.append(_run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,-z,defs", "-o", tmp, *objs]))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
         for o in outs:
             if o.strip():
                 print(o, file=sys.stderr)
-    return LIB
+    return lib
 
 
 if __name__ == "__main__":

@@ -34,6 +34,10 @@
 #include "sage_device.h"
 #include "sage_launch.h"
 
+#ifndef SAGE_PHASE_TRACE
+#define SAGE_PHASE_TRACE 0   // 1: the diagnostic per-phase cycle trace build (phase_trace.py)
+#endif
+
 namespace sage {
 
 constexpr int kBq = 128;           // queries per group == the Q quantisation block
@@ -648,8 +652,36 @@ __device__ __forceinline__ void attn_fwd_body(AttnArgs a) {
     __builtin_amdgcn_s_setprio(0);
     softmax_phase<D, FP8, CAUSAL, decltype(masked)::value, FINE, T>(s, lane, t * kBkv, qi, nk, c, st.m, pt);
   };
+#if SAGE_PHASE_TRACE
+  // Diagnostic build only: per-wave shader-clock sums of the matrix phases,
+  // the softmax phases and the two barriers' waits, the pair count and the
+  // schedule's total; stored over the output at the end (see below).
+  uint64_t tr[6] = {0, 0, 0, 0, 0, 0};
+  const uint64_t tr_start = __builtin_readcyclecounter();
+  auto timed = [&](int slot, const auto& f) __attribute__((always_inline)) {
+    const uint64_t t0 = __builtin_readcyclecounter();
+    f();
+    tr[slot] += __builtin_readcyclecounter() - t0;
+  };
+  auto x_tr = [&](auto par, int t, bool pv, bool qk) __attribute__((always_inline)) {
+    timed(0, [&] { x_phase(par, t, pv, qk); });
+  };
+  auto xl_tr = [&](auto par, int t) __attribute__((always_inline)) { timed(0, [&] { x_phase_loading(par, t); }); };
+  auto xr_tr = [&](int t, bool pv, bool qk) __attribute__((always_inline)) {
+    timed(0, [&] { x_phase_rt(t, pv, qk); });
+  };
+  auto y_tr = [&](int t, auto masked) __attribute__((always_inline)) { timed(1, [&] { y_phase(t, masked); }); };
+  auto ba_tr = [&]() __attribute__((always_inline)) { timed(2, [] { barrier_only(); }); };
+  auto bw_tr = [&]() __attribute__((always_inline)) {
+    timed(3, [] { wait_loads_barrier(); });
+    tr[4] += 1;
+  };
+  run_pingpong(grp, n_g, n_wg, x_tr, xl_tr, xr_tr, y_tr, loads_k, loads_v, loads_k_rt, loads_v_rt, ba_tr, bw_tr);
+  tr[5] = __builtin_readcyclecounter() - tr_start;
+#else
   run_pingpong(grp, n_g, n_wg, x_phase, x_phase_loading, x_phase_rt, y_phase, loads_k, loads_v, loads_k_rt,
                loads_v_rt);
+#endif
   __builtin_amdgcn_s_setprio(0);
 
   // Epilogue: normalise, undo the V scale, round, store in the caller's layout.
@@ -681,6 +713,16 @@ __device__ __forceinline__ void attn_fwd_body(AttnArgs a) {
       }
     }
   }
+#if SAGE_PHASE_TRACE
+  // Each wave's six sums (low 32 bits) replace the output of the work-group's
+  // first query row of this head (dense HND batches): uint32 word 8*wave + i.
+  __syncthreads();
+  if (lane == 0 && !a.seq) {
+    uint32_t* row = reinterpret_cast<uint32_t*>(a.o) + ((int64_t)bh * a.Nq + 2 * qp * kBq) * (D / 2);
+#pragma unroll
+    for (int i = 0; i < 6; ++i) row[8 * wave + i] = (uint32_t)tr[i];
+  }
+#endif
 }
 
 // Per-block Q/K scales.

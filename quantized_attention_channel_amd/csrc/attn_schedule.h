@@ -43,11 +43,23 @@ __device__ __forceinline__ void wait_loads_barrier() { asm volatile("s_waitcnt v
 //                                   that may need masking (a group's last)
 //   loads_k(par, t) / loads_v(par, t) and their run-time-parity forms: group
 //   0 issues K(t+1), group 1 V(t).
-template <class XP, class XL, class XR, class YP, class LK, class LV, class LKR, class LVR>
+// The two barriers: the one between the phases of a pair, and the one that
+// ends a pair after waiting for this wave's loads. (A phase-trace build passes
+// timing wrappers.)
+struct PhaseBarrier {
+  __device__ __forceinline__ void operator()() const { barrier_only(); }
+};
+struct PairBarrier {
+  __device__ __forceinline__ void operator()() const { wait_loads_barrier(); }
+};
+
+template <class XP, class XL, class XR, class YP, class LK, class LV, class LKR, class LVR,
+          class BA = PhaseBarrier, class BW = PairBarrier>
 __device__ __forceinline__ void run_pingpong(int grp, int n, int n_wg, const XP& x_phase,
                                              const XL& x_phase_loading, const XR& x_phase_rt, const YP& y_phase,
                                              const LK& loads_k, const LV& loads_v, const LKR& loads_k_rt,
-                                             const LVR& loads_v_rt) {
+                                             const LVR& loads_v_rt, const BA& barrier_only = BA{},
+                                             const BW& wait_loads_barrier = BW{}) {
   using Even = std::integral_constant<int, 0>;
   using Odd = std::integral_constant<int, 1>;
   using Masked = std::true_type;
