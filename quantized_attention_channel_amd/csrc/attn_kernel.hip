@@ -120,16 +120,16 @@ struct TileStage {
                                                  int k0, int8_t* sk) {
 #pragma unroll
     for (int i = 0; i < kKLoads; ++i) {
-      const uint32_t start = (uint32_t)k0 * D + i * kPass;
-      const auto rk = make_rsrc(kbase + start, kbytes > start ? kbytes - start : 0u);
+      const uint32_t start = __builtin_amdgcn_readfirstlane((uint32_t)k0 * D + i * kPass);
+      const auto rk = make_rsrc(kbase + start, tail_bytes(kbytes, start));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(sk + (i * NW + wave) * 1024),
                                               16, koff, 0, 0, 0);
     }
   }
   static __device__ __forceinline__ void issue_k_pass(const int8_t* kbase, uint32_t kbytes, uint32_t koff, int wave,
                                                       int k0, int8_t* sk, int i) {
-    const uint32_t start = (uint32_t)k0 * D + i * kPass;
-    const auto rk = make_rsrc(kbase + start, kbytes > start ? kbytes - start : 0u);
+    const uint32_t start = __builtin_amdgcn_readfirstlane((uint32_t)k0 * D + i * kPass);
+    const auto rk = make_rsrc(kbase + start, tail_bytes(kbytes, start));
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(sk + (i * NW + wave) * 1024),
                                             16, koff, 0, 0, 0);
   }

@@ -219,7 +219,7 @@ struct Stage {
   static __device__ __forceinline__ void k_pass(const uint8_t* kbase, uint32_t kbytes, uint32_t koff, int w, int t,
                                                 uint8_t* sk, int i) {
     const uint32_t start = (uint32_t)t * kKBytes + i * kPass;
-    const auto r = make_rsrc(kbase + start, kbytes > start ? kbytes - start : 0u);
+    const auto r = make_rsrc(kbase + start, tail_bytes(kbytes, start));
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(sk + (i * 4 + w) * 1024),
                                             16, koff, 0, 0, 0);
   }
@@ -227,7 +227,7 @@ struct Stage {
                                                   uint8_t* sks) {
     if (w < kSWaves) {
       const uint32_t start = (uint32_t)t * kSBytes;
-      const auto r = make_rsrc(ksbase + start, ksbytes > start ? ksbytes - start : 0u);
+      const auto r = make_rsrc(ksbase + start, tail_bytes(ksbytes, start));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(sks + w * 256), 4,
                                               (uint32_t)(w * 64 + lane) * 4, 0, 0, 0);
     }

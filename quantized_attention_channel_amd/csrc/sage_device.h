@@ -49,6 +49,14 @@ struct BF16 {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+// Bytes left in [0, bytes) from `start` on (0 past the end), as a wave-uniform
+// (scalar) value. Every field of a buffer resource must be scalar: the
+// compiler implements the saturating subtraction with a vector instruction,
+// and a resource built from a vector value makes it wrap each load in a loop
+// over the lanes' distinct resources.
+__device__ __forceinline__ uint32_t tail_bytes(uint32_t bytes, uint32_t start) {
+  return __builtin_amdgcn_readfirstlane(bytes > start ? bytes - start : 0u);
+}
 __device__ __forceinline__ i32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
