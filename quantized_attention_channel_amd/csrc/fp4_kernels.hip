@@ -366,7 +366,9 @@ __device__ __forceinline__ void softmax_phase(f32x16* s, int lane, int k0, int q
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const int b = 2 * u + (w >> 1), e0 = 8 * (w & 1);
-      uint32_t d = 0u;
+      // (all four bytes are written: start from an input's register, which
+      //  needs no clearing)
+      uint32_t d = __builtin_bit_cast(uint32_t, s[b][e0 + 0]);
       d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, s[b][e0 + 0], s[b][e0 + 1], scale, 0);
       d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, s[b][e0 + 2], s[b][e0 + 3], scale, 1);
       d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, s[b][e0 + 4], s[b][e0 + 5], scale, 2);
