@@ -440,6 +440,10 @@ __device__ __forceinline__ void attn_fwd_body(AttnArgs a) {
   using Stage = TileStage<D, FP8, kWaves>;
   constexpr int kKBytes = kBkv * D, kVBytes = D * Stage::kVRowB;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kKBytes + 2 * kVBytes];
+#if SAGE_PHASE_TRACE >= 2
+  const uint64_t tr_entry = __builtin_readcyclecounter();
+  const uint64_t rt_entry = __builtin_amdgcn_s_memrealtime();
+#endif
 
   // Work decomposition. Work-groups are dealt round-robin to the 8 XCDs; give
   // each XCD a contiguous range of (head, query) work so the work-groups that
@@ -656,8 +660,11 @@ __device__ __forceinline__ void attn_fwd_body(AttnArgs a) {
   // Diagnostic build only: per-wave shader-clock sums of the matrix phases,
   // the softmax phases and the two barriers' waits, the pair count and the
   // schedule's total; stored over the output at the end (see below).
-  uint64_t tr[6] = {0, 0, 0, 0, 0, 0};
+  uint64_t tr[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   const uint64_t tr_start = __builtin_readcyclecounter();
+#if SAGE_PHASE_TRACE >= 2
+  tr[6] = tr_start - tr_entry;                   // from kernel entry: work split, Q and first K tile loaded
+#endif
   auto timed = [&](int slot, const auto& f) __attribute__((always_inline)) {
     const uint64_t t0 = __builtin_readcyclecounter();
     f();
@@ -677,7 +684,8 @@ __device__ __forceinline__ void attn_fwd_body(AttnArgs a) {
     tr[4] += 1;
   };
   run_pingpong(grp, n_g, n_wg, x_tr, xl_tr, xr_tr, y_tr, loads_k, loads_v, loads_k_rt, loads_v_rt, ba_tr, bw_tr);
-  tr[5] = __builtin_readcyclecounter() - tr_start;
+  const uint64_t tr_sched_end = __builtin_readcyclecounter();
+  tr[5] = tr_sched_end - tr_start;
 #else
   run_pingpong(grp, n_g, n_wg, x_phase, x_phase_loading, x_phase_rt, y_phase, loads_k, loads_v, loads_k_rt,
                loads_v_rt);
@@ -714,13 +722,36 @@ __device__ __forceinline__ void attn_fwd_body(AttnArgs a) {
     }
   }
 #if SAGE_PHASE_TRACE
-  // Each wave's six sums (low 32 bits) replace the output of the work-group's
-  // first query row of this head (dense HND batches): uint32 word 8*wave + i.
+  // Each wave's sums (low 32 bits) replace the output of the work-group's
+  // first query row of this head (dense HND batches, d = 128): uint32 word
+  // 8*wave + i. Level 2 adds slot 6 (cycles before the schedule), slot 7 (the
+  // epilogue's issue time) and, from wave 0 in the second row, the
+  // work-group's entry and exit times (the 100 MHz constant clock) and its
+  // compute unit (XCC, shader engine, CU); its extra live values cost the
+  // schedule some cycles per pair, so level 1 is the one for the phases.
+#if SAGE_PHASE_TRACE >= 2
+  tr[7] = __builtin_readcyclecounter() - tr_sched_end;
+#else
+  (void)tr_sched_end;
+#endif
   __syncthreads();
-  if (lane == 0 && !a.seq) {
-    uint32_t* row = reinterpret_cast<uint32_t*>(a.o) + ((int64_t)bh * a.Nq + 2 * qp * kBq) * (D / 2);
+  if constexpr (D == 128) {
+    if (lane == 0 && !a.seq) {
+      uint32_t* row = reinterpret_cast<uint32_t*>(a.o) + ((int64_t)bh * a.Nq + 2 * qp * kBq) * (D / 2);
 #pragma unroll
-    for (int i = 0; i < 6; ++i) row[8 * wave + i] = (uint32_t)tr[i];
+      for (int i = 0; i < 8; ++i) row[8 * wave + i] = (uint32_t)tr[i];
+#if SAGE_PHASE_TRACE >= 2
+      const uint64_t rt_exit = __builtin_amdgcn_s_memrealtime();
+      if (wave == 0 && 2 * qp * kBq + 1 < a.Nq) {
+        row += D / 2;
+        row[0] = (uint32_t)rt_entry;
+        row[1] = (uint32_t)(rt_entry >> 32);
+        row[2] = (uint32_t)rt_exit;
+        row[3] = (uint32_t)(rt_exit >> 32);
+        row[4] = __smid();
+      }
+#endif
+    }
   }
 #endif
 }
