@@ -6,7 +6,8 @@
   sides (fp32 inputs, exact power-of-two scaling, round half to even).
 * The attention output is compared with sage_ref.sage_attention_fp4 on every
   row at small sizes (several tiles, ragged tails, GQA, causal, both layouts
-  and dtypes) and on one row per work-group and head at the benchmark's size,
+  and dtypes) and on one row per work-group and head at the full size of every
+  large workload,
   at the method's bars (cosine >= 0.9999 and relative L1 <= 1e-3 against the
   oracle). Against fp64 exact attention the variant is checked to land where
   the oracle lands (FP4 is a coarser method: its own accuracy is the bound).
@@ -191,12 +192,16 @@ def test_sageattn_fp4_routes_to_the_variant(sage):
 
 
 # ------------------------------------------------------------------ full size
+FULL_SIZE = [W.MID_OUTLIER, W.GQA_CAUSAL, W.LONG_D64, W.PEAK]
+
+
 @pytest.mark.timeout(900)
-def test_fp4_full_size_peak_workload(sage):
-    """The benchmark's workload (B=1, H=32, N=32768, d=128, fp16): MXFP4 stages
-    bit for bit per head, and the output on one row of every work-group of every
-    head plus the edge rows, per head and pooled."""
-    w = W.PEAK
+@pytest.mark.parametrize("w", FULL_SIZE, ids=lambda w: w.name)
+def test_fp4_full_size_workloads(sage, w):
+    """Every large workload (the outlier workload, GQA causal NHD bf16, d = 64,
+    and the benchmark's peak workload): the MXFP4 stages bit for bit for every
+    (batch, head), and the output on one row of every work-group of every head
+    plus the edge rows, per head and pooled."""
     say("fp4 full workload", w.name)
     q, k, v = W.generate(w)
     qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
@@ -206,24 +211,28 @@ def test_fp4_full_size_peak_workload(sage):
     del qg, kg, vg
     rows = rows_per_head(w.N, w.B * w.Hq)
     o_all = _hnd(o, w.layout)
-    got, ref, ex = [], [], []
     qa, ka, va = (_hnd(t, w.layout) for t in (q, k, v))
-    for h in range(w.Hq):
-        sl = slice(h, h + 1)
-        one = {name: t[:, sl] for name, t in codes.items()}
-        parts = check_fp4_stages(one, qa[:, sl], ka[:, sl], va[:, sl], w.sm_scale)
-        r = sage_ref.sage_attention_fp4(qa[:, sl], ka[:, sl], va[:, sl], dtype=w.dtype, is_causal=w.causal,
-                                        sm_scale=w.sm_scale, rows=rows[h], parts=parts)
-        ref.append(r[0, 0])
-        got.append(o_all[0, h, rows[h]])
-        ex.append(exact.exact_attention(qa[:, sl], ka[:, sl], va[:, sl], is_causal=w.causal, sm_scale=w.sm_scale,
-                                        rows=rows[h])[0, 0])
-        if h % 8 == 7:
-            say(f"   heads 0..{h} checked")
+    G = w.Hq // w.Hkv
+    got, ref, ex = [], [], []
+    for b in range(w.B):
+        bs = slice(b, b + 1)
+        for h in range(w.Hq):
+            hs, ks = slice(h, h + 1), slice(h // G, h // G + 1)
+            one = {"q_codes": codes["q_codes"][bs, hs], "q_scale": codes["q_scale"][bs, hs]}
+            one.update({n: codes[n][bs, ks] for n in ("k_codes", "k_scale", "k_mean", "v_codes", "v_scale")})
+            qn, kn, vn = qa[bs, hs], ka[bs, ks], va[bs, ks]
+            parts = check_fp4_stages(one, qn, kn, vn, w.sm_scale)
+            r_h = rows[b * w.Hq + h]
+            r = sage_ref.sage_attention_fp4(qn, kn, vn, dtype=w.dtype, is_causal=w.causal, sm_scale=w.sm_scale,
+                                            rows=r_h, parts=parts)
+            ref.append(r[0, 0])
+            got.append(o_all[b, h, r_h])
+            ex.append(exact.exact_attention(qn, kn, vn, is_causal=w.causal, sm_scale=w.sm_scale, rows=r_h)[0, 0])
+        say(f"   batch {b}: {w.Hq} heads checked")
     assert all(np.isfinite(g).all() for g in got)
     wc, wr = check_heads(got, ref)
-    G, R, E = (np.concatenate([np.ravel(x) for x in xs]) for xs in (got, ref, ex))
-    c, r, ce, ceo = cos(G, R), rel_l1(G, R), cos(G, E), cos(R, E)
+    Gt, R, E = (np.concatenate([np.ravel(x) for x in xs]) for xs in (got, ref, ex))
+    c, r, ce, ceo = cos(Gt, R), rel_l1(Gt, R), cos(Gt, E), cos(R, E)
     say(f"   {sum(len(x) for x in rows)} rows: cos={c:.7f} rel_l1={r:.2e} worst head cos={wc:.7f} rel_l1={wr:.2e};"
         f" vs fp64: HIP {ce:.5f} oracle {ceo:.5f}")
     assert c >= COS_ORACLE and r <= RL1_ORACLE
