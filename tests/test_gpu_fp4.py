@@ -237,3 +237,32 @@ def test_fp4_full_size_workloads(sage, w):
         f" vs fp64: HIP {ce:.5f} oracle {ceo:.5f}")
     assert c >= COS_ORACLE and r <= RL1_ORACLE
     assert abs(ce - ceo) <= 1e-3
+
+
+# ------------------------------------------------------------------ the longest sequence the ABI accepts
+@pytest.mark.parametrize("d,causal", [(128, False), (64, True)], ids=["d128_noncausal", "d64_causal"])
+def test_fp4_maximum_sequence_length(sage, d, causal):
+    """N = 2^20 keys and queries (the ABI's limit): every MXFP4 stage in full,
+    the output on rows at both ends and in between (buffer offsets, tile
+    counts, the V^T padding and its tile-major scales at their largest)."""
+    n = 1 << 20
+    w = W.PEAK.with_(B=1, Hq=1, Hkv=1, N=n, d=d, causal=causal)
+    say("fp4 maximum length", n, d, "causal" if causal else "")
+    q, k, v = W.generate(w)
+    qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
+    o = sage.sage_attn_fwd_fp4(qg, kg, vg, is_causal=causal, sm_scale=w.sm_scale)
+    codes = sage.sage_quant_fp4(qg, kg, vg, sm_scale=w.sm_scale)
+    torch.cuda.synchronize()
+    del qg, kg, vg
+    qn, kn, vn = (_hnd(t, "HND") for t in (q, k, v))
+    parts = check_fp4_stages(codes, qn, kn, vn, w.sm_scale)
+    rows = np.array([0, 1, 127, 128, n // 2 + 77, n - 129, n - 1])
+    got = o.float().cpu().numpy()[:, :, rows]
+    ref = sage_ref.sage_attention_fp4(qn, kn, vn, dtype=w.dtype, is_causal=causal, sm_scale=w.sm_scale,
+                                      rows=rows, parts=parts)
+    ex = exact.exact_attention(qn, kn, vn, is_causal=causal, sm_scale=w.sm_scale, rows=rows)
+    c, r, ce, ceo = cos(got, ref), rel_l1(got, ref), cos(got, ex), cos(ref, ex)
+    say(f"   cos={c:.7f} rel_l1={r:.2e}; vs fp64: HIP {ce:.5f} oracle {ceo:.5f}")
+    assert np.isfinite(got).all()
+    assert c >= COS_ORACLE and r <= RL1_ORACLE
+    assert abs(ce - ceo) <= 1e-3
