@@ -21,7 +21,7 @@ from typing import Optional
 
 import torch
 
-from . import DTYPES, sage_attn_fwd
+from . import DTYPES, sageattn
 
 _LIB = "sage_mi355x"
 
@@ -29,9 +29,10 @@ _LIB = "sage_mi355x"
 @torch.library.custom_op(f"{_LIB}::attn_fwd", mutates_args=())
 def attn_fwd_op(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bool, sm_scale: float,
                 pv_dtype: str, tensor_layout: str, qk_gran: str) -> torch.Tensor:
-    """Quantised attention forward (a fresh output tensor shaped like q)."""
-    return sage_attn_fwd(q.contiguous(), k.contiguous(), v.contiguous(), is_causal=is_causal, sm_scale=sm_scale,
-                         pv_dtype=pv_dtype, tensor_layout=tensor_layout, qk_gran=qk_gran)
+    """Quantised attention forward (a fresh output tensor shaped like q); pv_dtype
+    "fp8" or "fp16", or "fp4" for the FP4 microscaling variant."""
+    return sageattn(q, k, v, tensor_layout=tensor_layout, is_causal=is_causal, sm_scale=sm_scale,
+                    pv_dtype=pv_dtype, qk_quant_gran=qk_gran)
 
 
 @attn_fwd_op.register_fake
@@ -83,6 +84,10 @@ class patch_sdpa:
     """
 
     def __init__(self, pv_dtype: str = "fp8", qk_quant_gran: str = "per_block", passthrough: bool = False):
+        if pv_dtype not in ("fp8", "fp16", "fp4"):
+            raise ValueError(f"pv_dtype must be fp8, fp16 or fp4, got {pv_dtype!r}")
+        if pv_dtype == "fp4" and qk_quant_gran != "per_block":
+            raise ValueError("the FP4 variant has fixed MX blocks; qk_quant_gran must be per_block")
         self.pv_dtype, self.qk_gran, self.passthrough = pv_dtype, qk_quant_gran, passthrough
         self.routed = 0
         self.passed = 0

@@ -72,11 +72,18 @@ def test_patch_restores_and_guards_on_the_cpu():
     assert F.scaled_dot_product_attention is orig
 
 
+def test_patch_rejects_settings_the_kernels_do_not_have():
+    with pytest.raises(ValueError, match="pv_dtype"):
+        patch_sdpa(pv_dtype="fp6")
+    with pytest.raises(ValueError, match="MX blocks"):
+        patch_sdpa(pv_dtype="fp4", qk_quant_gran="per_thread")
+
+
 # ------------------------------------------------------------------ GPU
 @pytest.mark.gpu
 @pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")
 @pytest.mark.parametrize("causal,gqa,pv,gran", [(False, False, "fp8", "per_block"), (True, True, "fp8", "per_block"),
-                                               (True, False, "fp16", "per_thread")])
+                                               (True, False, "fp16", "per_thread"), (True, True, "fp4", "per_block")])
 def test_patched_sdpa_routes_to_the_kernels(causal, gqa, pv, gran):
     g = torch.Generator().manual_seed(3)
     hkv = 2 if gqa else 4
@@ -85,7 +92,10 @@ def test_patched_sdpa_routes_to_the_kernels(causal, gqa, pv, gran):
     v = torch.randn(2, hkv, 300, 128, generator=g).half().cuda()
     with torch.no_grad(), patch_sdpa(pv_dtype=pv, qk_quant_gran=gran) as p:
         got = F.scaled_dot_product_attention(q, k, v, is_causal=causal, enable_gqa=gqa)
-    want = sage.sage_attn_fwd(q, k, v, is_causal=causal, sm_scale=128 ** -0.5, pv_dtype=pv, qk_gran=gran)
+    if pv == "fp4":
+        want = sage.sage_attn_fwd_fp4(q, k, v, is_causal=causal, sm_scale=128 ** -0.5)
+    else:
+        want = sage.sage_attn_fwd(q, k, v, is_causal=causal, sm_scale=128 ** -0.5, pv_dtype=pv, qk_gran=gran)
     torch.cuda.synchronize()
     assert p.routed == 1 and torch.equal(got, want)
     # and against the oracle (SDPA's default scale 1/sqrt(d)), not only the library itself
@@ -98,12 +108,18 @@ def _against_oracle(got, q, k, v, *, causal, sm_scale, pv, gran, dtype="fp16"):
     blk = ((sage_ref.PER_THREAD_BLK_Q, sage_ref.PER_THREAD_BLK_K) if gran == "per_thread"
            else (sage_ref.BLK_Q, sage_ref.BLK_K))
     qn, kn, vn = (t.float().cpu().numpy() for t in (q, k, v))
-    ref = sage_ref.sage_attention(qn, kn, vn, dtype=dtype, is_causal=causal, sm_scale=sm_scale, pv=pv,
-                                  blk_q=blk[0], blk_k=blk[1])
+    if pv == "fp4":
+        ref = sage_ref.sage_attention_fp4(qn, kn, vn, dtype=dtype, is_causal=causal, sm_scale=sm_scale)
+    else:
+        ref = sage_ref.sage_attention(qn, kn, vn, dtype=dtype, is_causal=causal, sm_scale=sm_scale, pv=pv,
+                                      blk_q=blk[0], blk_k=blk[1])
     g = got.float().cpu().numpy()
     assert cos(g, ref) >= COS_ORACLE and rel_l1(g, ref) <= RL1_ORACLE and worst_head_cos(g, ref) >= COS_ORACLE
     ex = exact.exact_attention(qn, kn, vn, is_causal=causal, sm_scale=sm_scale)
-    assert cos(g, ex) >= COS_EXACT
+    if pv == "fp4":     # (a coarser method: the kernel lands where the oracle lands)
+        assert abs(cos(g, ex) - cos(ref, ex)) <= 1e-3
+    else:
+        assert cos(g, ex) >= COS_EXACT
 
 
 @pytest.mark.gpu
@@ -137,6 +153,22 @@ def test_captured_graph_equals_eager():
     out = torch.compile(g_, backend="aot_eager", fullgraph=True)(q, k, v)
     torch.cuda.synchronize()
     _against_oracle(out, q * 2, k, v, causal=True, sm_scale=0.0625, pv="fp8", gran="per_block", dtype="bf16")
+
+
+@pytest.mark.gpu
+@pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")
+def test_compiled_fp4_operator_against_oracle():
+    """The FP4 variant through the custom operator inside a torch.compile graph."""
+    g = torch.Generator().manual_seed(7)
+    q, k, v = (torch.randn(1, 2, 333, 128, generator=g).half().cuda() for _ in range(3))
+
+    def f(q, k, v):
+        return torch.ops.sage_mi355x.attn_fwd(q, k, v, True, 0.09, "fp4", "HND", "per_block")
+
+    out = torch.compile(f, backend="aot_eager", fullgraph=True)(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(out, sage.sage_attn_fwd_fp4(q, k, v, is_causal=True, sm_scale=0.09))
+    _against_oracle(out, q, k, v, causal=True, sm_scale=0.09, pv="fp4", gran="per_block")
 
 
 @pytest.mark.gpu
