@@ -369,18 +369,25 @@ def measure(w: W.Workload, pv: str, steps: int, warmup: int, qk_gran: str = "per
 
 
 def measure_varlen(w: W.VarlenWorkload, steps: int, warmup: int):
-    """One sage_attn_fwd_varlen call per step (quantisation and attention of
-    every sequence of the packed batch), timed with HIP events."""
+    """One sage_attn_fwd_varlen (or, pv "fp4", sage_attn_fwd_fp4_varlen) call
+    per step (quantisation and attention of every sequence of the packed
+    batch), timed with HIP events."""
     import quantized_attention_channel_amd as sage
     q, k, v, cq, ck = W.generate_varlen(w, device="cuda")
     mq, mk = max(w.lens_q), max(w.lens_k)
     shape = sage.varlen_shape_of(q, k, cq, mq, mk)
-    ws = torch.empty(max(sage.sage_varlen_workspace_bytes(shape, w.pv), 256), dtype=torch.uint8, device="cuda")
+    need = sage.sage_fp4_varlen_workspace_bytes(shape) if w.pv == "fp4" else \
+        sage.sage_varlen_workspace_bytes(shape, w.pv)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
     o = torch.empty_like(q)
 
     def run():
-        sage.sage_attn_fwd_varlen(q, k, v, cq, ck, mq, mk, is_causal=w.causal, sm_scale=w.sm_scale,
-                                  pv_dtype=w.pv, out=o, workspace=ws)
+        if w.pv == "fp4":
+            sage.sage_attn_fwd_fp4_varlen(q, k, v, cq, ck, mq, mk, is_causal=w.causal, sm_scale=w.sm_scale,
+                                          out=o, workspace=ws)
+        else:
+            sage.sage_attn_fwd_varlen(q, k, v, cq, ck, mq, mk, is_causal=w.causal, sm_scale=w.sm_scale,
+                                      pv_dtype=w.pv, out=o, workspace=ws)
     for _ in range(warmup):
         run()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -482,7 +489,9 @@ def main():
                            # the FP4 microscaling variant: attention_frac against the 10.1 PFLOP/s FP4 peak
                            "fp4": variant(measure(w, "fp4", args.steps, args.warmup), PEAK_FP4_TOPS),
                            "fp4_causal": variant(measure(w.with_(causal=True), "fp4", args.steps, args.warmup),
-                                                 PEAK_FP4_TOPS)}
+                                                 PEAK_FP4_TOPS),
+                           "fp4_varlen": measure_varlen(W.VARLEN_PREFILL.with_(pv="fp4"), args.steps,
+                                                        args.warmup)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, pv, args.cpu_rows, args.qk_gran)
         out["cpu_baseline"].update(host_info())

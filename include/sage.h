@@ -341,6 +341,52 @@ sage_status sage_attn_fwd_fp4(const sage_shape* s, const void* q, const void* k,
                               int32_t is_causal, float sm_scale, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/* ---- The FP4 variant over a packed variable-length batch (heatdrop.ai
+ * review, "Key highlights": variable sequence lengths within a batch, and the
+ * FP4 microscaling variant above). Every sequence is quantised and attended
+ * to as a batch of one: its own K channel mean, MX blocks of 32 channels per
+ * token for Q and K, V blocks of 32 keys from the sequence's first key, causal
+ * masking top-left within the sequence. Shape and cu_seqlens rules as for
+ * sage_attn_fwd_varlen; s->qk_gran must be SAGE_QK_PER_BLOCK (0), any other
+ * valid value returns SAGE_ERR_UNSUPPORTED. */
+
+/* Workspace bytes sage_attn_fwd_fp4_varlen needs (span table, work list, all
+ * MXFP4 codes and scales, the K means, the partials); 0 for an invalid or
+ * unsupported shape. */
+size_t sage_fp4_varlen_workspace_bytes(const sage_varlen_shape* s);
+
+/* The whole FP4 forward over a packed batch: q [total_q, Hq, d], k and v
+ * [total_k, Hkv, d], o [total_q, Hq, d] (s->dtype), is_causal 0 or 1, sm_scale
+ * finite and > 0. B == 0 or total_q == 0 is a no-op. Alignment as for
+ * sage_attn_fwd_varlen. */
+sage_status sage_attn_fwd_fp4_varlen(const sage_varlen_shape* s, const void* q, const void* k, const void* v,
+                                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* o,
+                                     int32_t is_causal, float sm_scale, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
+/* Workspace bytes sage_quant_fp4_varlen needs (span table, work list and the
+ * K channel-sum partials); 0 for an invalid or unsupported shape. */
+size_t sage_quant_fp4_varlen_workspace_bytes(const sage_varlen_shape* s);
+
+/* The MXFP4 stages of sage_attn_fwd_fp4_varlen on their own. Outputs, with
+ * n_pad as for sage_quant_varlen and sequence b's key columns from p_b there:
+ *   q_codes [Hq][total_q][d/2] u8    q_scale [Hq][total_q][d/32] u8 (Q times c, as in sage_quant_fp4)
+ *   k_codes [Hkv][total_k][d/2] u8   k_scale [Hkv][total_k][d/32] u8 (K minus its sequence's mean)
+ *   k_mean  [B][Hkv][d] fp32         0 for a sequence without keys
+ *   v_codes [Hkv][d][n_pad/2] u8     V transposed; the columns p_b .. p_b + nk_b rounded up to 128
+ *                                    hold sequence b (keys past nk_b are code 0), others are not written
+ *   v_scale [Hkv][n_pad/128][d][4] u8  per 128-column tile, each channel's four block scales (blocks
+ *                                    past nk_b get 0), the tiles of sequence b as for v_codes
+ * With total_q == 0 the Q outputs are not written (q and they may be NULL);
+ * with total_k == 0 neither are the K and V outputs. Alignment: tensors and
+ * codes 16 bytes (v_scale too), scales, means and cu_seqlens 4 bytes,
+ * workspace 256 bytes. */
+sage_status sage_quant_fp4_varlen(const sage_varlen_shape* s, const void* q, const void* k, const void* v,
+                                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, float sm_scale,
+                                  uint8_t* q_codes, uint8_t* q_scale, uint8_t* k_codes, uint8_t* k_scale,
+                                  float* k_mean, uint8_t* v_codes, uint8_t* v_scale, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 /* Static description of a status code (never NULL). Part of the error
  * convention above, not of the method. */
 const char* sage_status_string(sage_status st);

@@ -11,7 +11,9 @@ Entry points (same names as the C ABI):
   sage_attn_fwd_codes, sage_debug_qk_i32, sage_varlen_workspace_bytes,
   sage_attn_fwd_varlen, sage_quant_varlen, sage_quant_varlen_workspace_bytes,
   sage_attn_fwd_noalloc, sage_quant_fp4, sage_quant_fp4_workspace_bytes,
-  sage_fp4_workspace_bytes, sage_attn_fwd_fp4_codes, sage_attn_fwd_fp4.
+  sage_fp4_workspace_bytes, sage_attn_fwd_fp4_codes, sage_attn_fwd_fp4,
+  sage_fp4_varlen_workspace_bytes, sage_attn_fwd_fp4_varlen,
+  sage_quant_fp4_varlen_workspace_bytes, sage_quant_fp4_varlen.
 User-facing wrapper:
   sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None,
            pv_dtype="fp8", qk_quant_gran="per_block") -- the call shape the
@@ -21,9 +23,9 @@ User-facing wrapper:
   sageattn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
                   max_seqlen_k, ...) -- packed variable-length batches
   (heatdrop.ai review, "Key highlights").
-  pv_dtype="fp4" in sageattn selects the FP4 microscaling variant (MXFP4 Q, K,
-  P and V; heatdrop.ai review, "Key highlights"; cnnetsun.cn guide,
-  序列长度优化技巧).
+  pv_dtype="fp4" in sageattn and sageattn_varlen selects the FP4 microscaling
+  variant (MXFP4 Q, K, P and V; heatdrop.ai review, "Key highlights";
+  cnnetsun.cn guide, 序列长度优化技巧).
 """
 from __future__ import annotations
 
@@ -78,6 +80,12 @@ _SIGNATURES = {
                                                _vp]),
     "sage_attn_fwd_fp4": (ctypes.c_int, [_c_shape_p, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_float, _vp,
                                          ctypes.c_size_t, _vp]),
+    "sage_fp4_varlen_workspace_bytes": (ctypes.c_size_t, [_c_shape_p]),
+    "sage_attn_fwd_fp4_varlen": (ctypes.c_int, [_c_shape_p, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32,
+                                                ctypes.c_float, _vp, ctypes.c_size_t, _vp]),
+    "sage_quant_fp4_varlen_workspace_bytes": (ctypes.c_size_t, [_c_shape_p]),
+    "sage_quant_fp4_varlen": (ctypes.c_int, [_c_shape_p, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp,
+                                             _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
 }
 # the workspace limit of sage_attn_fwd_noalloc (SAGE_NOALLOC_MAX_WORKSPACE_BYTES in sage.h)
 NOALLOC_MAX_WORKSPACE_BYTES = 32 * 1024 * 1024
@@ -507,6 +515,70 @@ def sage_attn_fwd_fp4(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, is_c
     return o
 
 
+def _check_varlen_inputs(q, k, v, cu_seqlens_q, cu_seqlens_k):
+    _check_inputs(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    if cu_seqlens_k.numel() != cu_seqlens_q.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    if tuple(v.shape) != tuple(k.shape) or v.dtype != q.dtype or k.dtype != q.dtype:
+        raise ValueError("v must have k's shape and all inputs one dtype")
+
+
+def sage_fp4_varlen_workspace_bytes(shape: SageVarlenShape) -> int:
+    return int(lib.sage_fp4_varlen_workspace_bytes(_ref(shape)))
+
+
+def sage_attn_fwd_fp4_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                             cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int, *,
+                             is_causal: bool = False, sm_scale: Optional[float] = None,
+                             out: Optional[torch.Tensor] = None,
+                             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The FP4 microscaling forward over a packed batch: q [total_q, Hq, d],
+    k/v [total_k, Hkv, d], int32 cu_seqlens of B + 1 offsets. Returns o like q."""
+    _check_varlen_inputs(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    s = varlen_shape_of(q, k, cu_seqlens_q, max_seqlen_q, max_seqlen_k)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(s.head_dim)
+    dev = q.device
+    o = _out_like(q, out)
+    ws = _workspace_for(workspace, sage_fp4_varlen_workspace_bytes(s), dev)
+    _check(lib.sage_attn_fwd_fp4_varlen(_ref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q),
+                                        _ptr(cu_seqlens_k), _ptr(o), int(bool(is_causal)), float(sm_scale),
+                                        _ptr(ws), ws.numel(), _stream(dev)), "sage_attn_fwd_fp4_varlen")
+    return o
+
+
+def sage_quant_fp4_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                          cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int, *,
+                          sm_scale: Optional[float] = None) -> dict:
+    """The MXFP4 stages of a packed batch, per sequence (see sage.h):
+    q_codes [Hq,total_q,d/2], q_scale [Hq,total_q,d/32], k_codes and k_scale
+    likewise over Hkv and total_k, k_mean [B,Hkv,d], v_codes [Hkv,d,n_pad/2]
+    and v_scale [Hkv,n_pad/128,d,4] (n_pad = varlen_v_codes_stride)."""
+    _check_varlen_inputs(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    s = varlen_shape_of(q, k, cu_seqlens_q, max_seqlen_q, max_seqlen_k)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(s.head_dim)
+    B, dev, d = s.batch, q.device, s.head_dim
+    npad = varlen_v_codes_stride(s.total_k, B)
+    u8 = dict(dtype=torch.uint8, device=dev)
+    out = {"q_codes": torch.zeros((s.heads_q, s.total_q, d // 2), **u8),
+           "q_scale": torch.zeros((s.heads_q, s.total_q, d // 32), **u8),
+           "k_codes": torch.zeros((s.heads_kv, s.total_k, d // 2), **u8),
+           "k_scale": torch.zeros((s.heads_kv, s.total_k, d // 32), **u8),
+           "k_mean": torch.zeros((B, s.heads_kv, d), dtype=torch.float32, device=dev),
+           "v_codes": torch.zeros((s.heads_kv, d, npad // 2), **u8),
+           "v_scale": torch.zeros((s.heads_kv, npad // 128, d, 4), **u8)}
+    ws = _workspace_for(None, int(lib.sage_quant_fp4_varlen_workspace_bytes(_ref(s))), dev)
+    _check(lib.sage_quant_fp4_varlen(_ref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                                     float(sm_scale), _ptr(out["q_codes"]), _ptr(out["q_scale"]),
+                                     _ptr(out["k_codes"]), _ptr(out["k_scale"]), _ptr(out["k_mean"]),
+                                     _ptr(out["v_codes"]), _ptr(out["v_scale"]), _ptr(ws), ws.numel(),
+                                     _stream(dev)), "sage_quant_fp4_varlen")
+    return out
+
+
 def sage_debug_qk_i32(q_codes: torch.Tensor, k_codes: torch.Tensor) -> torch.Tensor:
     """INT32 S for canonical-order codes [B,Hq,Nq,d] x [B,Hkv,Nk,d] -> [B,Hq,Nq,Nk]."""
     _check_inputs(q_codes, k_codes)
@@ -564,6 +636,12 @@ def sageattn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_
     cu_seqlens offsets, maximum lengths)."""
     if qk_quant_gran not in QK_GRANS:
         raise ValueError(f"qk_quant_gran must be one of {sorted(QK_GRANS)}, got {qk_quant_gran!r}")
+    if pv_dtype == "fp4":
+        if qk_quant_gran != "per_block":
+            raise ValueError("the FP4 variant has fixed MX blocks; qk_quant_gran must be per_block")
+        return sage_attn_fwd_fp4_varlen(q.contiguous(), k.contiguous(), v.contiguous(), cu_seqlens_q.contiguous(),
+                                        cu_seqlens_k.contiguous(), max_seqlen_q, max_seqlen_k,
+                                        is_causal=is_causal, sm_scale=sm_scale)
     return sage_attn_fwd_varlen(q.contiguous(), k.contiguous(), v.contiguous(), cu_seqlens_q.contiguous(),
                                 cu_seqlens_k.contiguous(), max_seqlen_q, max_seqlen_k, is_causal=is_causal,
                                 sm_scale=sm_scale, pv_dtype=pv_dtype, qk_gran=qk_quant_gran)
@@ -572,6 +650,7 @@ def sageattn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_
 __all__ = ["sageattn", "sageattn_varlen", "sage_attn_fwd_varlen", "sage_varlen_workspace_bytes",
            "SageVarlenShape", "varlen_shape_of", "sage_attn_fwd", "sage_attn_fwd_codes", "sage_quant_qk", "sage_quant_v",
            "sage_transpose_v", "sage_debug_qk_i32", "sage_quant_fp4", "sage_attn_fwd_fp4",
-           "sage_attn_fwd_fp4_codes", "sage_fp4_workspace_bytes", "fp4_buffers",
+           "sage_attn_fwd_fp4_codes", "sage_fp4_workspace_bytes", "fp4_buffers", "sage_attn_fwd_fp4_varlen",
+           "sage_quant_fp4_varlen", "sage_fp4_varlen_workspace_bytes", "varlen_v_codes_stride",
            "sage_block_sizes", "sage_v_codes_stride", "sage_workspace_bytes", "make_shape", "shape_of",
            "SageError", "SageShape", "QK_GRANS", "lib", "LIB_PATH"]

@@ -20,6 +20,11 @@
 //   v_codes [B*Hkv][D][n_pad/2] (V^T, keys contiguous, zero past Nk)
 //   v_scale [B*Hkv][n_pad/128][D][4] (per 128-key tile: each channel's four
 //           32-key blocks, so one tile's scales are one contiguous run)
+// Packed variable-length batches (tokens of all sequences concatenated): the
+// codes and their scales are [H][total][.], k_mean [sequence][Hkv][D], and V^T
+// [Hkv][D][n_pad/2] with each sequence's keys from column kp0 of its span (a
+// multiple of 128), so its tiles and their scale runs never straddle two
+// sequences.
 #include <type_traits>
 
 #include "attn_schedule.h"
@@ -65,12 +70,15 @@ __device__ __forceinline__ uint32_t pack8(const float (&x)[8], int byte) {
 // Q or K rows: thread = one 16-byte chunk (8 channels) of one token row; the
 // four threads of a 32-channel block are adjacent lanes. Chunks are numbered
 // over [B*H][N][D/8] (the codes' order), ITER per thread.
+// Packed batches (seq set, K only): the rows are [H][total_k] and a token's
+// smoothing mean is its sequence's (the last span starting at or before it).
 template <typename T, int D, bool SMOOTH>
 __global__ __launch_bounds__(256) void quant_rows_fp4_kernel(const uint16_t* __restrict__ x, TensorGeom geo, int H,
                                                              int N, int64_t total_chunks,
                                                              const float* __restrict__ mean, float mul,
                                                              uint32_t* __restrict__ codes,
-                                                             uint8_t* __restrict__ scale) {
+                                                             uint8_t* __restrict__ scale,
+                                                             const SeqSpan* __restrict__ seq, int n_seq) {
   constexpr int CPR = D / 8;      // chunks per row
   constexpr int ITER = 4;
   // (a work-group covers whole 4-chunk blocks: 256 is a multiple of 4, and a
@@ -88,12 +96,21 @@ __global__ __launch_bounds__(256) void quant_rows_fp4_kernel(const uint16_t* __r
     const int b = (int)(bh / H), h = (int)(bh % H);
     const i32x4 raw = *reinterpret_cast<const i32x4*>(x + (int64_t)b * geo.batch_stride +
                                                       (int64_t)h * geo.head_stride + (int64_t)t * geo.tok_stride + col);
+    int64_t mrow = bh;                               // row of the smoothing mean
+    if (SMOOTH && seq) {
+      int lo = 0, hi = n_seq - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (seq[mid].k0 <= t) lo = mid; else hi = mid - 1;
+      }
+      mrow = (int64_t)lo * H + h;
+    }
     float v[8];
     float amax = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float f = T::to_f32((uint16_t)(((uint32_t)raw[e / 2]) >> (16 * (e & 1))));
-      if (SMOOTH) f = f - mean[bh * D + col + e];   // K: smoothed
+      if (SMOOTH) f = f - mean[mrow * D + col + e]; // K: smoothed
       else f = f * mul;                              // Q: times the score factor
       v[e] = f;
       amax = fmaxf(amax, fabsf(f));
@@ -110,10 +127,13 @@ __global__ __launch_bounds__(256) void quant_rows_fp4_kernel(const uint16_t* __r
 // staged in LDS; each thread then quantises one (channel, 32-key block) run
 // (lanes = consecutive channels: conflict-free column reads), and the codes
 // leave as 64-byte channel rows of V^T and one 4*D-byte run of scales.
+// (packed batches, seq set: blockIdx.y is (sequence, kv head); the
+//  sequence's tiles go to its columns from kp0, tiles past its keys exit)
 template <typename T, int D>
 __global__ __launch_bounds__(256) void quant_v_fp4_kernel(const uint16_t* __restrict__ v, TensorGeom geo, int H,
                                                           int N, int n_pad, uint8_t* __restrict__ vt,
-                                                          uint8_t* __restrict__ vscale) {
+                                                          uint8_t* __restrict__ vscale,
+                                                          const SeqSpan* __restrict__ seq) {
   constexpr int ROWS = kBkv;
   constexpr int CROW = 80;                     // bytes per staged code row (64 + 16: spreads the writes)
   __shared__ __attribute__((aligned(16))) uint16_t tile[ROWS * D];
@@ -124,12 +144,24 @@ __global__ __launch_bounds__(256) void quant_v_fp4_kernel(const uint16_t* __rest
   const int b = bh / H, h = bh % H;
   const int tt = blockIdx.x;                   // tile
   const int t0 = tt * kBkv;
-  const int64_t base = (int64_t)b * geo.batch_stride + (int64_t)h * geo.head_stride;
+  int64_t base = (int64_t)b * geo.batch_stride + (int64_t)h * geo.head_stride;
+  int n = N;
+  int64_t vrow = bh;                           // V^T row block and the first column of this tile
+  int64_t col0 = t0, tile0 = tt;
+  if (seq) {
+    const SeqSpan sp = seq[b];
+    n = sp.nk;
+    if (t0 >= n) return;                       // (the whole work-group)
+    base += (int64_t)sp.k0 * geo.tok_stride;
+    vrow = h;
+    col0 = sp.kp0 + t0;
+    tile0 = sp.kp0 / kBkv + tt;
+  }
   for (int ci = tid; ci < ROWS * D / 8; ci += 256) {
     const int r = ci / (D / 8), c = (ci % (D / 8)) * 8;
     const int t = t0 + r;
     i32x4 raw = {0, 0, 0, 0};
-    if (t < N) raw = *reinterpret_cast<const i32x4*>(v + base + (int64_t)t * geo.tok_stride + c);
+    if (t < n) raw = *reinterpret_cast<const i32x4*>(v + base + (int64_t)t * geo.tok_stride + c);
     *reinterpret_cast<i32x4*>(tile + r * D + c) = raw;
   }
   __syncthreads();
@@ -155,13 +187,13 @@ __global__ __launch_bounds__(256) void quant_v_fp4_kernel(const uint16_t* __rest
     stile[c * 4 + j] = (uint8_t)byte;
   }
   __syncthreads();
-  uint8_t* dst = vt + (int64_t)bh * D * (n_pad / 2) + tt * (kBkv / 2);
+  uint8_t* dst = vt + vrow * D * (n_pad / 2) + col0 / 2;
   for (int ci = tid; ci < D * 4; ci += 256) {
     const int c = ci / 4, j = ci % 4;
     *reinterpret_cast<i32x4*>(dst + (int64_t)c * (n_pad / 2) + 16 * j) =
         *reinterpret_cast<const i32x4*>(ctile + c * CROW + 16 * j);
   }
-  uint8_t* sdst = vscale + ((int64_t)bh * (n_pad / kBkv) + tt) * (D * 4);
+  uint8_t* sdst = vscale + (vrow * (n_pad / kBkv) + tile0) * (D * 4);
   for (int ci = tid; ci < D * 4 / 16; ci += 256)
     *reinterpret_cast<i32x4*>(sdst + 16 * ci) = *reinterpret_cast<const i32x4*>(stile + 16 * ci);
 }
@@ -450,18 +482,56 @@ __global__ __launch_bounds__(512, 1) void attn_fp4_kernel(Fp4AttnArgs a) {
   uint8_t* const sks0 = smem + 2 * kK + 2 * kV;
   uint8_t* const svs0 = sks0 + 2 * kS;
 
-  // Work decomposition (dense batches), as in the INT8 kernel: XCD-contiguous
-  // (head, query pair) ranges, causal pairs longest first.
-  const int n_qp = (a.Nq + 2 * kBq - 1) / (2 * kBq);
-  const int total = n_qp * a.B * a.Hq;
-  int id = blockIdx.x;
-  if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
-  const int bh = id / n_qp;
-  int qp = id % n_qp;
-  if (CAUSAL) qp = n_qp - 1 - qp;
+  // Work decomposition, as in the INT8 kernel. Dense batches: XCD-contiguous
+  // (head, query pair) ranges, causal pairs longest first. Packed batches: XCD
+  // x takes heads [x Hq/8, (x+1) Hq/8) of every sequence and walks the work
+  // list of query pairs (sequence by sequence, each from its longest pair).
+  int bh, qp;
+  if (a.seq) {
+    int heads = a.Hq, h0 = 0, j = blockIdx.x;
+    if ((a.Hq & 7) == 0) {
+      heads = a.Hq >> 3;
+      h0 = (blockIdx.x & 7) * heads;
+      j = blockIdx.x >> 3;
+    }
+    const int qpi = j / heads;
+    const int sb = qpi < a.n_owner ? a.qp_owner[qpi] : -1;
+    if (sb < 0) return;                                          // past the work list
+    qp = (a.seq[sb].nq + 2 * kBq - 1) / (2 * kBq) - 1 - (qpi - a.seq[sb].qp0);
+    bh = sb * a.Hq + h0 + j % heads;
+  } else {
+    const int n_qp = (a.Nq + 2 * kBq - 1) / (2 * kBq);
+    const int total = n_qp * a.B * a.Hq;
+    int id = blockIdx.x;
+    if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
+    bh = id / n_qp;
+    qp = id % n_qp;
+    if (CAUSAL) qp = n_qp - 1 - qp;
+  }
   const int b = bh / a.Hq, h = bh % a.Hq;
-  const int bhk = b * a.Hkv + h / (a.Hq / a.Hkv);
-  const int nq = a.Nq, nk = a.Nk;
+  const int hk = h / (a.Hq / a.Hkv);
+  const int bhk = b * a.Hkv + hk;
+  // Rows of this work-group's queries and keys in the codes ([B*H][N] or, packed,
+  // [H][total] from the sequence's first token), its V^T column and scale-tile
+  // offsets, and its first output token.
+  int nq = a.Nq, nk = a.Nk;
+  int64_t q_row = (int64_t)bh * a.Nq, k_row = (int64_t)bhk * a.Nk;
+  int64_t v_off = (int64_t)bhk * a.D * (a.n_pad / 2), v_len = (int64_t)a.D * (a.n_pad / 2);
+  int64_t vs_tile = (int64_t)bhk * (a.n_pad / kBkv), vs_tiles = a.n_pad / kBkv;
+  int64_t o_tok = 0;
+  if (a.seq) {
+    const SeqSpan sp = a.seq[b];
+    nq = sp.nq;
+    nk = sp.nk;
+    if (2 * qp * kBq >= nq) return;                              // no rows of this sequence here
+    q_row = (int64_t)h * a.total_q + sp.q0;
+    k_row = (int64_t)hk * a.total_k + sp.k0;
+    v_off = (int64_t)hk * a.D * (a.n_pad / 2) + sp.kp0 / 2;
+    v_len = (int64_t)a.D * (a.n_pad / 2) - sp.kp0 / 2;
+    vs_tile = (int64_t)hk * (a.n_pad / kBkv) + sp.kp0 / kBkv;
+    vs_tiles = a.n_pad / kBkv - sp.kp0 / kBkv;
+    o_tok = sp.q0;
+  }
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);
@@ -475,10 +545,10 @@ __global__ __launch_bounds__(512, 1) void attn_fp4_kernel(Fp4AttnArgs a) {
   i32x4 qreg[D / 64];
   int qsc;
   {
-    const auto rq = make_rsrc(a.q4 + (int64_t)bh * nq * (D / 2), (uint32_t)nq * (D / 2));
+    const auto rq = make_rsrc(a.q4 + q_row * (D / 2), (uint32_t)nq * (D / 2));
 #pragma unroll
     for (int kk = 0; kk < D / 64; ++kk) qreg[kk] = buf_load16(rq, (uint32_t)qi * (D / 2) + 32 * kk + 16 * g);
-    const auto rqs = make_rsrc(a.q_sc + (int64_t)bh * nq * (D / kMx), (uint32_t)nq * (D / kMx));
+    const auto rqs = make_rsrc(a.q_sc + q_row * (D / kMx), (uint32_t)nq * (D / kMx));
     if constexpr (D == 128) qsc = __builtin_amdgcn_raw_buffer_load_b32(rqs, (uint32_t)qi * 4, 0, 0) >> (8 * g);
     else qsc = (__builtin_amdgcn_raw_buffer_load_b16(rqs, (uint32_t)qi * 2, 0, 0) >> (8 * g)) & 0xff;
   }
@@ -490,12 +560,12 @@ __global__ __launch_bounds__(512, 1) void attn_fp4_kernel(Fp4AttnArgs a) {
   const int n_g = grp_live ? tiles_for(qt) : 0;
   const int n_wg = ((2 * qp + 1) * kBq < nq) ? tiles_for(2 * qp + 1) : tiles_for(2 * qp);
 
-  const uint8_t* kbase = a.k4 + (int64_t)bhk * nk * (D / 2);
+  const uint8_t* kbase = a.k4 + k_row * (D / 2);
   const uint32_t kbytes = (uint32_t)nk * (D / 2);
-  const uint8_t* ksbase = a.k_sc + (int64_t)bhk * nk * (D / kMx);
+  const uint8_t* ksbase = a.k_sc + k_row * (D / kMx);
   const uint32_t ksbytes = (uint32_t)nk * (D / kMx);
-  const auto rv = make_rsrc(a.v4 + (int64_t)bhk * D * (a.n_pad / 2), (uint32_t)D * (a.n_pad / 2));
-  const auto rvs = make_rsrc(a.v_sc + (int64_t)bhk * a.n_pad * (D / kMx), (uint32_t)a.n_pad * (D / kMx));
+  const auto rv = make_rsrc(a.v4 + v_off, (uint32_t)v_len);
+  const auto rvs = make_rsrc(a.v_sc + vs_tile * (kBkv * D / kMx), (uint32_t)(vs_tiles * (kBkv * D / kMx)));
   uint32_t koff, voff;
   St::init(koff, voff, wv4, lane, a.n_pad);
 
@@ -592,7 +662,7 @@ __global__ __launch_bounds__(512, 1) void attn_fp4_kernel(Fp4AttnArgs a) {
     const float l = st.l;
     const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
     uint16_t* orow = reinterpret_cast<uint16_t*>(a.o) + (int64_t)b * a.ogeo.batch_stride +
-                     (int64_t)h * a.ogeo.head_stride + (int64_t)qi * a.ogeo.tok_stride;
+                     (int64_t)h * a.ogeo.head_stride + (o_tok + qi) * a.ogeo.tok_stride;
 #pragma unroll
     for (int cb = 0; cb < NT; ++cb) {
 #pragma unroll
@@ -619,26 +689,33 @@ static unsigned row_wgs(int64_t chunks) {
   return (unsigned)(n < (int64_t(1) << 20) ? n : (int64_t(1) << 20));
 }
 
+// Packed batches (a.seq set): the Q and K rows are quantised as one [H][total]
+// batch (K's mean looked up per token), V per (sequence, kv head) over the
+// longest sequence's tiles.
 template <typename T, int D>
 static hipError_t launch_quant_fp4_t(const Fp4QuantArgs& a, hipStream_t st) {
   hipError_t e = hipSuccess;
-  if (a.Nk > 0) {
-    e = launch_k_mean(a.k, a.kgeo, a.B, a.Hkv, a.Nk, a.D, a.bf16, a.ksum_part, a.k_mean, st);
+  const bool packed = a.seq != nullptr;
+  if (a.Nk > 0 && (!packed || a.total_k > 0)) {
+    e = launch_k_mean(a.k, a.kgeo, a.B, a.Hkv, a.Nk, a.D, a.bf16, a.ksum_part, a.k_mean, st, a.seq);
     if (e != hipSuccess) return e;
-    const int64_t kchunks = (int64_t)a.B * a.Hkv * a.Nk * (D / 8);
+    const int kn = packed ? a.total_k : a.Nk;
+    const int64_t kchunks = (int64_t)(packed ? 1 : a.B) * a.Hkv * kn * (D / 8);
     hipLaunchKernelGGL((fp4::quant_rows_fp4_kernel<T, D, true>), dim3(row_wgs(kchunks)),
-                       dim3(256), 0, st, (const uint16_t*)a.k, a.kgeo, a.Hkv, a.Nk, kchunks, a.k_mean, 1.0f,
-                       (uint32_t*)a.k_codes, a.k_scale);
+                       dim3(256), 0, st, (const uint16_t*)a.k, a.kgeo, a.Hkv, kn, kchunks, a.k_mean, 1.0f,
+                       (uint32_t*)a.k_codes, a.k_scale, a.seq, a.B);
   }
-  if (a.Nq > 0) {
-    const int64_t qchunks = (int64_t)a.B * a.Hq * a.Nq * (D / 8);
+  if (a.Nq > 0 && (!packed || a.total_q > 0)) {
+    const int qn = packed ? a.total_q : a.Nq;
+    const int64_t qchunks = (int64_t)(packed ? 1 : a.B) * a.Hq * qn * (D / 8);
     hipLaunchKernelGGL((fp4::quant_rows_fp4_kernel<T, D, false>), dim3(row_wgs(qchunks)),
-                       dim3(256), 0, st, (const uint16_t*)a.q, a.qgeo, a.Hq, a.Nq, qchunks, (const float*)nullptr,
-                       a.q_mul, (uint32_t*)a.q_codes, a.q_scale);
+                       dim3(256), 0, st, (const uint16_t*)a.q, a.qgeo, a.Hq, qn, qchunks, (const float*)nullptr,
+                       a.q_mul, (uint32_t*)a.q_codes, a.q_scale, (const SeqSpan*)nullptr, 0);
   }
-  if (a.n_pad > 0)
-    hipLaunchKernelGGL((fp4::quant_v_fp4_kernel<T, D>), dim3(a.n_pad / kBkv, a.B * a.Hkv), dim3(256), 0, st,
-                       (const uint16_t*)a.v, a.vgeo, a.Hkv, a.Nk, a.n_pad, a.v_codes, a.v_scale);
+  const int v_tiles = !packed ? a.n_pad / kBkv : a.total_k > 0 ? (a.Nk + kBkv - 1) / kBkv : 0;
+  if (v_tiles > 0)
+    hipLaunchKernelGGL((fp4::quant_v_fp4_kernel<T, D>), dim3(v_tiles, a.B * a.Hkv), dim3(256), 0, st,
+                       (const uint16_t*)a.v, a.vgeo, a.Hkv, a.Nk, a.n_pad, a.v_codes, a.v_scale, a.seq);
   return hipGetLastError();
 }
 
@@ -650,8 +727,8 @@ hipError_t launch_quant_fp4(const Fp4QuantArgs& a, hipStream_t st) {
 template <int D, bool CAUSAL, typename T>
 static hipError_t launch_attn_fp4_t(const Fp4AttnArgs& a, hipStream_t st) {
   const int n_qp = (a.Nq + 2 * fp4::kBq - 1) / (2 * fp4::kBq);
-  hipLaunchKernelGGL((fp4::attn_fp4_kernel<D, CAUSAL, T>), dim3(n_qp * a.B * a.Hq), dim3(64 * fp4::kWaves), 0, st,
-                     a);
+  const int grid = a.seq ? a.n_owner * a.Hq : n_qp * a.B * a.Hq;   // packed: the work list per head
+  hipLaunchKernelGGL((fp4::attn_fp4_kernel<D, CAUSAL, T>), dim3(grid), dim3(64 * fp4::kWaves), 0, st, a);
   return hipGetLastError();
 }
 

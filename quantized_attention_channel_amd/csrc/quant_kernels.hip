@@ -475,25 +475,25 @@ hipError_t launch_quant_qk(const QuantQKArgs& a, hipStream_t st) {
 
 template <typename T, int D>
 static hipError_t launch_k_mean_t(const void* k, TensorGeom kgeo, int B, int Hkv, int Nk, double* ksum_part,
-                                  float* k_mean, hipStream_t st) {
+                                  float* k_mean, hipStream_t st, const SeqSpan* seq) {
   const int chunks = (Nk + kStatChunk - 1) / kStatChunk;
   const int bhk = B * Hkv;
   hipLaunchKernelGGL((channel_stats_kernel<T, D, true, false>), dim3(chunks, bhk), dim3(256), 0, st,
                      (const uint16_t*)k, (const uint16_t*)nullptr, kgeo, Hkv, Nk, chunks, ksum_part, (float*)nullptr,
-                     (const SeqSpan*)nullptr);
+                     seq);
   hipLaunchKernelGGL((channel_finalize_kernel<D, true, false>), dim3(bhk), dim3(D), 0, st, Nk, chunks, ksum_part,
-                     (const float*)nullptr, k_mean, (float*)nullptr, (float*)nullptr, Hkv, (const SeqSpan*)nullptr);
+                     (const float*)nullptr, k_mean, (float*)nullptr, (float*)nullptr, Hkv, seq);
   return hipGetLastError();
 }
 
 hipError_t launch_k_mean(const void* k, TensorGeom kgeo, int B, int Hkv, int Nk, int D, bool bf16, double* ksum_part,
-                         float* k_mean, hipStream_t st) {
+                         float* k_mean, hipStream_t st, const SeqSpan* seq) {
   if (Nk <= 0) return hipSuccess;
   if (bf16)
-    return D == 64 ? launch_k_mean_t<BF16, 64>(k, kgeo, B, Hkv, Nk, ksum_part, k_mean, st)
-                   : launch_k_mean_t<BF16, 128>(k, kgeo, B, Hkv, Nk, ksum_part, k_mean, st);
-  return D == 64 ? launch_k_mean_t<F16, 64>(k, kgeo, B, Hkv, Nk, ksum_part, k_mean, st)
-                 : launch_k_mean_t<F16, 128>(k, kgeo, B, Hkv, Nk, ksum_part, k_mean, st);
+    return D == 64 ? launch_k_mean_t<BF16, 64>(k, kgeo, B, Hkv, Nk, ksum_part, k_mean, st, seq)
+                   : launch_k_mean_t<BF16, 128>(k, kgeo, B, Hkv, Nk, ksum_part, k_mean, st, seq);
+  return D == 64 ? launch_k_mean_t<F16, 64>(k, kgeo, B, Hkv, Nk, ksum_part, k_mean, st, seq)
+                 : launch_k_mean_t<F16, 128>(k, kgeo, B, Hkv, Nk, ksum_part, k_mean, st, seq);
 }
 
 template <typename T, int D>

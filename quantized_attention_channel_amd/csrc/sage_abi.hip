@@ -521,6 +521,103 @@ sage::Fp4AttnArgs fp4_attn_args(const Dims& d, const uint8_t* q_codes, const uin
   return a;
 }
 
+// FP4 variant of a packed batch: codes and scales [H][total][.], k_mean
+// [sequence][Hkv][D], V^T codes [Hkv][D][n_pad/2] and scales
+// [Hkv][n_pad/128][D][4] (each sequence from its span's column kp0).
+struct Fp4VSizes {
+  size_t q_codes, q_scale, k_codes, k_scale, k_mean, v_codes, v_scale, ksum, spans, qp_owner;
+};
+
+Fp4VSizes fp4_varlen_sizes(const VDims& d) {
+  Fp4VSizes z;
+  z.q_codes = size_t(d.Hq * d.total_q * d.D / 2);
+  z.q_scale = size_t(d.Hq * d.total_q * d.D / 32);
+  z.k_codes = size_t(d.Hkv * d.total_k * d.D / 2);
+  z.k_scale = size_t(d.Hkv * d.total_k * d.D / 32);
+  z.k_mean = size_t(d.B * d.Hkv * d.D) * 4;
+  z.v_codes = size_t(d.Hkv * d.D * d.n_pad / 2);
+  z.v_scale = size_t(d.Hkv * d.D * d.n_pad / 32);
+  z.ksum = size_t(d.B * d.Hkv * cdiv(d.max_k, kStatChunk) * d.D) * 8;
+  z.spans = size_t(d.B) * sizeof(sage::SeqSpan);
+  z.qp_owner = size_t(sage::varlen_qpair_bound(d.total_q, d.B)) * 4;
+  return z;
+}
+
+// Whole forward: every buffer in the workspace. Quantisation alone: the span
+// table, the work list and the K sums (the codes go to the caller).
+struct Fp4VLayout {
+  size_t spans, qp_owner, q_codes, q_scale, k_codes, k_scale, k_mean, v_codes, v_scale, ksum, total;
+};
+
+Fp4VLayout fp4_varlen_layout_for(const VDims& d, bool quant_only) {
+  const Fp4VSizes z = fp4_varlen_sizes(d);
+  Fp4VLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  L.spans = take(z.spans);
+  L.qp_owner = take(z.qp_owner);
+  L.ksum = take(z.ksum);
+  if (!quant_only) {
+    L.q_codes = take(z.q_codes);
+    L.q_scale = take(z.q_scale);
+    L.k_codes = take(z.k_codes);
+    L.k_scale = take(z.k_scale);
+    L.k_mean = take(z.k_mean);
+    L.v_codes = take(z.v_codes);
+    L.v_scale = take(z.v_scale);
+  }
+  L.total = off;
+  return L;
+}
+
+sage_status check_fp4_varlen_shape(const sage_varlen_shape* s, VDims* d) {
+  sage_status st = check_varlen_shape(s, d);
+  if (st != SAGE_OK) return st;
+  if (d->fine) return SAGE_ERR_UNSUPPORTED;
+  return SAGE_OK;
+}
+
+// The plan kernel, then the MXFP4 stages of a packed batch.
+sage_status fp4_varlen_quant_launch(const VDims& d, const void* q, const void* k, const void* v, const int32_t* cu_q,
+                                    const int32_t* cu_k, float sm_scale, sage::SeqSpan* spans, int32_t* qp_owner,
+                                    uint8_t* q_codes, uint8_t* q_scale, uint8_t* k_codes, uint8_t* k_scale,
+                                    float* k_mean, uint8_t* v_codes, uint8_t* v_scale, double* ksum, bool run_q,
+                                    bool run_kv, hipStream_t hs) {
+  const int n_owner = int(sage::varlen_qpair_bound(d.total_q, d.B));
+  hipError_t e = sage::launch_varlen_plan(cu_q, cu_k, int(d.B), int(d.total_q), int(d.total_k), int(d.max_q),
+                                          int(d.max_k), int(d.n_pad), spans, qp_owner, n_owner, hs);
+  if (e != hipSuccess) return SAGE_ERR_HIP;
+  sage::Fp4QuantArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.qgeo = packed_geom(d.Hq, d.D);
+  a.kgeo = packed_geom(d.Hkv, d.D);
+  a.vgeo = packed_geom(d.Hkv, d.D);
+  a.B = int(d.B), a.Hq = int(d.Hq), a.Hkv = int(d.Hkv), a.Nq = int(d.max_q), a.Nk = int(d.max_k), a.D = int(d.D);
+  a.n_pad = int(d.n_pad);
+  a.bf16 = d.bf16;
+  a.q_mul = fp4_score_factor(sm_scale);
+  a.q_codes = q_codes;
+  a.q_scale = q_scale;
+  a.k_codes = k_codes;
+  a.k_scale = k_scale;
+  a.k_mean = k_mean;
+  a.v_codes = v_codes;
+  a.v_scale = v_scale;
+  a.ksum_part = ksum;
+  a.seq = spans;
+  a.total_q = int(d.total_q);
+  a.total_k = int(d.total_k);
+  if (!run_q) a.Nq = 0;
+  if (!run_kv) a.Nk = 0;
+  return from_hip(sage::launch_quant_fp4(a, hs));
+}
+
 }  // namespace
 
 extern "C" {
@@ -954,6 +1051,103 @@ sage_status sage_attn_fwd_fp4(const sage_shape* s, const void* q, const void* k,
   return from_hip(sage::launch_attn_fp4(fp4_attn_args(d, qa.q_codes, qa.q_scale, qa.k_codes, qa.k_scale,
                                                       qa.v_codes, qa.v_scale, o, is_causal),
                                         hs));
+}
+
+size_t sage_fp4_varlen_workspace_bytes(const sage_varlen_shape* s) {
+  VDims d;
+  return check_fp4_varlen_shape(s, &d) == SAGE_OK ? fp4_varlen_layout_for(d, false).total : 0;
+}
+
+sage_status sage_attn_fwd_fp4_varlen(const sage_varlen_shape* s, const void* q, const void* k, const void* v,
+                                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* o,
+                                     int32_t is_causal, float sm_scale, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  VDims d;
+  sage_status st = check_fp4_varlen_shape(s, &d);
+  if (st != SAGE_OK) return st;
+  if (is_causal != 0 && is_causal != 1) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (d.B == 0 || d.total_q == 0 || d.max_q == 0) return SAGE_OK;
+  if (!q || !k || !v || !o || !cu_seqlens_q || !cu_seqlens_k || !workspace) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(cu_seqlens_q, 4) ||
+      !aligned(cu_seqlens_k, 4) || !aligned(workspace, 256))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  const Fp4VLayout L = fp4_varlen_layout_for(d, false);
+  if (workspace_bytes < L.total) return SAGE_ERR_WORKSPACE;
+  const size_t qbytes = size_t(d.total_q * d.Hq * d.D) * 2, kvbytes = size_t(d.total_k * d.Hkv * d.D) * 2;
+  const size_t cubytes = size_t(d.B + 1) * 4;
+  if (aliased({{o, qbytes}, {workspace, L.total}},
+              {{q, qbytes}, {k, kvbytes}, {v, kvbytes}, {cu_seqlens_q, cubytes}, {cu_seqlens_k, cubytes}}))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  sage::SeqSpan* spans = at<sage::SeqSpan>(workspace, L.spans);
+  int32_t* qp_owner = at<int32_t>(workspace, L.qp_owner);
+  st = fp4_varlen_quant_launch(d, q, k, v, cu_seqlens_q, cu_seqlens_k, sm_scale, spans, qp_owner,
+                               at<uint8_t>(workspace, L.q_codes), at<uint8_t>(workspace, L.q_scale),
+                               at<uint8_t>(workspace, L.k_codes), at<uint8_t>(workspace, L.k_scale),
+                               at<float>(workspace, L.k_mean), at<uint8_t>(workspace, L.v_codes),
+                               at<uint8_t>(workspace, L.v_scale), at<double>(workspace, L.ksum), true,
+                               d.max_k > 0 && d.total_k > 0, hs);
+  if (st != SAGE_OK) return st;
+  sage::Fp4AttnArgs a{};
+  a.q4 = at<uint8_t>(workspace, L.q_codes);
+  a.q_sc = at<uint8_t>(workspace, L.q_scale);
+  a.k4 = at<uint8_t>(workspace, L.k_codes);
+  a.k_sc = at<uint8_t>(workspace, L.k_scale);
+  a.v4 = at<uint8_t>(workspace, L.v_codes);
+  a.v_sc = at<uint8_t>(workspace, L.v_scale);
+  a.o = o;
+  a.ogeo = packed_geom(d.Hq, d.D);
+  a.B = int(d.B), a.Hq = int(d.Hq), a.Hkv = int(d.Hkv), a.Nq = int(d.max_q), a.Nk = int(d.max_k), a.D = int(d.D);
+  a.n_pad = int(d.n_pad);
+  a.causal = is_causal != 0;
+  a.bf16 = d.bf16;
+  a.seq = spans;
+  a.total_q = int(d.total_q);
+  a.total_k = int(d.total_k);
+  a.qp_owner = qp_owner;
+  a.n_owner = int(sage::varlen_qpair_bound(d.total_q, d.B));
+  return from_hip(sage::launch_attn_fp4(a, hs));
+}
+
+size_t sage_quant_fp4_varlen_workspace_bytes(const sage_varlen_shape* s) {
+  VDims d;
+  return check_fp4_varlen_shape(s, &d) == SAGE_OK ? fp4_varlen_layout_for(d, true).total : 0;
+}
+
+sage_status sage_quant_fp4_varlen(const sage_varlen_shape* s, const void* q, const void* k, const void* v,
+                                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, float sm_scale,
+                                  uint8_t* q_codes, uint8_t* q_scale, uint8_t* k_codes, uint8_t* k_scale,
+                                  float* k_mean, uint8_t* v_codes, uint8_t* v_scale, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  VDims d;
+  sage_status st = check_fp4_varlen_shape(s, &d);
+  if (st != SAGE_OK) return st;
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (d.B == 0) return SAGE_OK;
+  const bool has_q = d.total_q > 0 && d.max_q > 0, has_k = d.total_k > 0 && d.max_k > 0;
+  if (!cu_seqlens_q || !cu_seqlens_k || !workspace) return SAGE_ERR_INVALID_ARGUMENT;
+  if (has_q && (!q || !q_codes || !q_scale)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (has_k && (!k || !v || !k_codes || !k_scale || !k_mean || !v_codes || !v_scale)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4) || !aligned(workspace, 256)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (has_q && (!aligned(q, 16) || !aligned(q_codes, 16) || !aligned(q_scale, 4))) return SAGE_ERR_INVALID_ARGUMENT;
+  if (has_k && (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_codes, 16) || !aligned(k_scale, 4) ||
+                !aligned(k_mean, 4) || !aligned(v_codes, 16) || !aligned(v_scale, 16)))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  const Fp4VLayout L = fp4_varlen_layout_for(d, true);
+  if (workspace_bytes < L.total) return SAGE_ERR_WORKSPACE;
+  const Fp4VSizes z = fp4_varlen_sizes(d);
+  const size_t qin = has_q ? size_t(d.Hq * d.total_q * d.D) * 2 : 0, kin = has_k ? size_t(d.Hkv * d.total_k * d.D) * 2 : 0;
+  const size_t cubytes = size_t(d.B + 1) * 4;
+  if (aliased({{q_codes, has_q ? z.q_codes : 0}, {q_scale, has_q ? z.q_scale : 0}, {k_codes, has_k ? z.k_codes : 0},
+               {k_scale, has_k ? z.k_scale : 0}, {k_mean, has_k ? z.k_mean : 0}, {v_codes, has_k ? z.v_codes : 0},
+               {v_scale, has_k ? z.v_scale : 0}, {workspace, L.total}},
+              {{q, qin}, {k, kin}, {v, kin}, {cu_seqlens_q, cubytes}, {cu_seqlens_k, cubytes}}))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  return fp4_varlen_quant_launch(d, q, k, v, cu_seqlens_q, cu_seqlens_k, sm_scale,
+                                 at<sage::SeqSpan>(workspace, L.spans), at<int32_t>(workspace, L.qp_owner), q_codes,
+                                 q_scale, k_codes, k_scale, k_mean, v_codes, v_scale, at<double>(workspace, L.ksum),
+                                 has_q, has_k, static_cast<hipStream_t>(stream));
 }
 
 sage_status sage_debug_qk_i32(const sage_shape* s, const int8_t* q_codes, const int8_t* k_codes, int32_t* s_out,

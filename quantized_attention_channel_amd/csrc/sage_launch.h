@@ -108,6 +108,8 @@ struct Fp4QuantArgs {
   uint8_t* v_codes;    // [B*Hkv][D][n_pad/2]
   uint8_t* v_scale;    // [B*Hkv][n_pad/128][D][4]
   double* ksum_part;   // [B*Hkv][ceil(Nk/256)][D]
+  const SeqSpan* seq;  // packed batches only: codes [H][total][.], k_mean [B][Hkv][D],
+  int total_q, total_k;  // V^T [Hkv][D][n_pad/2] with each sequence's keys from column kp0
 };
 
 struct Fp4AttnArgs {
@@ -121,6 +123,10 @@ struct Fp4AttnArgs {
   TensorGeom ogeo;
   int B, Hq, Hkv, Nq, Nk, n_pad, D;   // (the score factor is already in the Q codes)
   bool causal, bf16;
+  const SeqSpan* seq;                 // packed batches only (as for AttnArgs)
+  int total_q, total_k;
+  const int32_t* qp_owner;
+  int n_owner;
 };
 
 hipError_t launch_varlen_plan(const int32_t* cu_q, const int32_t* cu_k, int B, int total_q, int total_k,
@@ -130,9 +136,10 @@ hipError_t launch_quant_qk(const QuantQKArgs& a, hipStream_t st);
 hipError_t launch_quant_v(const QuantVArgs& a, hipStream_t st);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
 hipError_t launch_debug_qk(const DebugQKArgs& a, hipStream_t st);
-// K channel mean alone (the smoothing statistics of sage_quant_qk), dense batches.
+// K channel mean alone (the smoothing statistics of sage_quant_qk); packed
+// batches pass their span table (B sequences, Nk the longest).
 hipError_t launch_k_mean(const void* k, TensorGeom kgeo, int B, int Hkv, int Nk, int D, bool bf16, double* ksum_part,
-                         float* k_mean, hipStream_t st);
+                         float* k_mean, hipStream_t st, const SeqSpan* seq = nullptr);
 hipError_t launch_quant_fp4(const Fp4QuantArgs& a, hipStream_t st);
 hipError_t launch_attn_fp4(const Fp4AttnArgs& a, hipStream_t st);
 

@@ -16,7 +16,8 @@ hipError_t launch_quant_qk(const QuantQKArgs&, hipStream_t) { return hipErrorNoD
 hipError_t launch_quant_v(const QuantVArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_attn(const AttnArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_debug_qk(const DebugQKArgs&, hipStream_t) { return hipErrorNoDevice; }
-hipError_t launch_k_mean(const void*, TensorGeom, int, int, int, int, bool, double*, float*, hipStream_t) {
+hipError_t launch_k_mean(const void*, TensorGeom, int, int, int, int, bool, double*, float*, hipStream_t,
+                         const SeqSpan*) {
   return hipErrorNoDevice;
 }
 hipError_t launch_quant_fp4(const Fp4QuantArgs&, hipStream_t) { return hipErrorNoDevice; }

@@ -376,6 +376,68 @@ def test_attn_fwd_varlen_validation(case, kw, want):
     assert _vattn(**kw) == want, case
 
 
+def test_fp4_varlen_workspace_holds_the_mx_buffers():
+    s = _vshape()
+    npad = sage.varlen_v_codes_stride(700, 3)
+    need = (4 * 500 * 128 // 2 + 4 * 500 * 128 // 32 + 2 * 700 * 128 // 2 + 2 * 700 * 128 // 32
+            + 3 * 2 * 128 * 4 + 2 * 128 * npad // 2 + 2 * 128 * npad // 32 + 3 * 32)
+    assert sage.sage_fp4_varlen_workspace_bytes(s) >= need
+    assert 0 < sage.lib.sage_quant_fp4_varlen_workspace_bytes(ctypes.byref(s)) < need
+    # fixed MX blocks: per-thread granularity is unsupported, bad shapes invalid
+    for bad in (_vshape(gran=1), _vshape(d=96), _vshape(Hq=3)):
+        assert sage.sage_fp4_varlen_workspace_bytes(bad) == 0
+        assert sage.lib.sage_quant_fp4_varlen_workspace_bytes(ctypes.byref(bad)) == 0
+    assert sage.lib.sage_fp4_varlen_workspace_bytes(None) == 0
+
+
+@FAKE_ADDRESSES
+def test_fp4_varlen_entry_points_validate():
+    s = _vshape()
+    sp = ctypes.byref(s)
+    bad, ws = sage.SAGE_ERR_INVALID_ARGUMENT, FAKE + 2 ** 33
+    q, k, v, o = FAKE, FAKE + G, FAKE + 2 * G, FAKE + 3 * G
+    cq, ck = FAKE + 2 ** 34, FAKE + 2 ** 34 + 64
+    n = sage.sage_fp4_varlen_workspace_bytes(s)
+    fwd = sage.lib.sage_attn_fwd_fp4_varlen
+    assert fwd(sp, q, k, v, cq, ck, o, 0, 0.1, ws, n - 1, None) == sage.SAGE_ERR_WORKSPACE
+    assert fwd(sp, None, k, v, cq, ck, o, 0, 0.1, ws, n, None) == bad
+    assert fwd(sp, q, k, v, None, ck, o, 0, 0.1, ws, n, None) == bad
+    assert fwd(sp, q, k, v, cq + 2, ck, o, 0, 0.1, ws, n, None) == bad               # misaligned cu_seqlens
+    assert fwd(sp, q, k, v, cq, ck, o + 8, 0, 0.1, ws, n, None) == bad               # misaligned o
+    assert fwd(sp, q, k, v, cq, ck, q + 4096, 0, 0.1, ws, n, None) == bad            # o on q
+    assert fwd(sp, q, k, v, cq, ck, o, 0, 0.1, cq - 256, n, None) == bad             # workspace on cu_seqlens
+    assert fwd(sp, q, k, v, cq, ck, o, 2, 0.1, ws, n, None) == bad
+    assert fwd(sp, q, k, v, cq, ck, o, 0, float("nan"), ws, n, None) == bad
+    assert fwd(ctypes.byref(_vshape(gran=1)), q, k, v, cq, ck, o, 0, 0.1, ws, n, None) == sage.SAGE_ERR_UNSUPPORTED
+    assert fwd(ctypes.byref(_vshape(d=96)), q, k, v, cq, ck, o, 0, 0.1, ws, n, None) == sage.SAGE_ERR_UNSUPPORTED
+    assert fwd(ctypes.byref(_vshape(tq=0)), None, None, None, None, None, None, 0, 0.1, None, 0, None) == sage.SAGE_OK
+    # quantisation alone
+    qc, qs, kc, ks, km, vc, vs = (FAKE + i * G for i in range(4, 11))
+    qw = sage.lib.sage_quant_fp4_varlen_workspace_bytes(sp)
+    quant = sage.lib.sage_quant_fp4_varlen
+    args = [sp, q, k, v, cq, ck, 0.1, qc, qs, kc, ks, km, vc, vs, ws, qw, None]
+
+    def call(**change):
+        a = list(args)
+        for i, val in change.items():
+            a[int(i[1:])] = val
+        return quant(*a)
+    assert call(a15=qw - 1) == sage.SAGE_ERR_WORKSPACE
+    assert call(a7=None) == bad                                                    # q_codes
+    assert call(a13=vs + 4) == bad                                                 # v_scale needs 16 bytes
+    assert call(a12=v + 4096) == bad                                               # v codes on v
+    assert call(a10=qc + 16) == bad                                                # k scale on q codes
+    assert call(a14=ck - 64) == bad                                                # workspace on cu_seqlens
+    assert call(a6=-0.1) == bad
+    assert call(a0=ctypes.byref(_vshape(gran=1))) == sage.SAGE_ERR_UNSUPPORTED
+    # no keys: the K and V outputs may be NULL (the call then reaches the device)
+    nok = ctypes.byref(_vshape(tk=0, mk=0))
+    assert quant(nok, q, None, None, cq, ck, 0.1, qc, qs, None, None, None, None, None, ws,
+                 sage.lib.sage_quant_fp4_varlen_workspace_bytes(nok), None) == sage.SAGE_ERR_HIP
+    assert quant(ctypes.byref(_vshape(B=0)), None, None, None, cq, ck, 0.1, *([None] * 7), ws, 0,
+                 None) == sage.SAGE_OK
+
+
 def _plan_model(cq, ck, total_q, total_k, max_q, max_k, n_pad, owner=None):
     """The span rules of the plan kernel: clamp, pack the padded keys, and list
     each sequence's query pairs (256 queries) in a work list of bounded size."""
