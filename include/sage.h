@@ -200,7 +200,8 @@ size_t sage_varlen_workspace_bytes(const sage_varlen_shape* s, int32_t pv_dtype)
  * arguments are as for sage_attn_fwd. Limits: 1 <= Hq, Hkv with Hq % Hkv == 0,
  * head_dim in {64, 128}, B * Hq <= 2^24, total_k + 127 * B <= 2^24 - 128 (the
  * padded key columns of the transposed V), (total_q / 256 + B) * Hq <= 2^30
- * (the attention work list). B == 0 or total_q == 0 is a no-op.
+ * (the attention work list). B == 0 or total_q == 0 is a no-op. With
+ * total_k == 0 every output row is zero and k, v may be NULL.
  * cu_seqlens pointers must be 4-byte aligned; q, k, v, o 16-byte aligned. */
 sage_status sage_attn_fwd_varlen(const sage_varlen_shape* s, const void* q, const void* k, const void* v,
                                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* o,
@@ -357,7 +358,8 @@ size_t sage_fp4_varlen_workspace_bytes(const sage_varlen_shape* s);
 
 /* The whole FP4 forward over a packed batch: q [total_q, Hq, d], k and v
  * [total_k, Hkv, d], o [total_q, Hq, d] (s->dtype), is_causal 0 or 1, sm_scale
- * finite and > 0. B == 0 or total_q == 0 is a no-op. Alignment as for
+ * finite and > 0. B == 0 or total_q == 0 is a no-op; with total_k == 0 every
+ * output row is zero and k, v may be NULL. Alignment as for
  * sage_attn_fwd_varlen. */
 sage_status sage_attn_fwd_fp4_varlen(const sage_varlen_shape* s, const void* q, const void* k, const void* v,
                                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* o,

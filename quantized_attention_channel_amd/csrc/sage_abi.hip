@@ -780,7 +780,9 @@ sage_status sage_attn_fwd_varlen(const sage_varlen_shape* s, const void* q, cons
   if (is_causal != 0 && is_causal != 1) return SAGE_ERR_INVALID_ARGUMENT;
   if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_INVALID_ARGUMENT;
   if (d.B == 0 || d.total_q == 0 || d.max_q == 0) return SAGE_OK;
-  if (!q || !k || !v || !o || !cu_seqlens_q || !cu_seqlens_k || !workspace) return SAGE_ERR_INVALID_ARGUMENT;
+  const bool has_k = d.total_k > 0 && d.max_k > 0;   // (else every output row is zero; k, v may be NULL)
+  if (!q || !o || !cu_seqlens_q || !cu_seqlens_k || !workspace || (has_k && (!k || !v)))
+    return SAGE_ERR_INVALID_ARGUMENT;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(cu_seqlens_q, 4) ||
       !aligned(cu_seqlens_k, 4) || !aligned(workspace, 256))
     return SAGE_ERR_INVALID_ARGUMENT;
@@ -807,7 +809,7 @@ sage_status sage_attn_fwd_varlen(const sage_varlen_shape* s, const void* q, cons
   bufs.v_inv = at<float>(workspace, L.v_inv);
   bufs.ksum = at<double>(workspace, L.ksum);
   bufs.vmax = at<float>(workspace, L.vmax);
-  st = varlen_quant_launch(d, fp8, q, k, v, cu_seqlens_q, cu_seqlens_k, bufs, true, d.max_k > 0, hs);
+  st = varlen_quant_launch(d, fp8, q, k, v, cu_seqlens_q, cu_seqlens_k, bufs, true, has_k, hs);
   if (st != SAGE_OK) return st;
 
   sage::AttnArgs aa{};
@@ -1068,7 +1070,9 @@ sage_status sage_attn_fwd_fp4_varlen(const sage_varlen_shape* s, const void* q, 
   if (is_causal != 0 && is_causal != 1) return SAGE_ERR_INVALID_ARGUMENT;
   if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_INVALID_ARGUMENT;
   if (d.B == 0 || d.total_q == 0 || d.max_q == 0) return SAGE_OK;
-  if (!q || !k || !v || !o || !cu_seqlens_q || !cu_seqlens_k || !workspace) return SAGE_ERR_INVALID_ARGUMENT;
+  const bool has_k = d.total_k > 0 && d.max_k > 0;   // (else every output row is zero; k, v may be NULL)
+  if (!q || !o || !cu_seqlens_q || !cu_seqlens_k || !workspace || (has_k && (!k || !v)))
+    return SAGE_ERR_INVALID_ARGUMENT;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(cu_seqlens_q, 4) ||
       !aligned(cu_seqlens_k, 4) || !aligned(workspace, 256))
     return SAGE_ERR_INVALID_ARGUMENT;
@@ -1086,8 +1090,8 @@ sage_status sage_attn_fwd_fp4_varlen(const sage_varlen_shape* s, const void* q, 
                                at<uint8_t>(workspace, L.q_codes), at<uint8_t>(workspace, L.q_scale),
                                at<uint8_t>(workspace, L.k_codes), at<uint8_t>(workspace, L.k_scale),
                                at<float>(workspace, L.k_mean), at<uint8_t>(workspace, L.v_codes),
-                               at<uint8_t>(workspace, L.v_scale), at<double>(workspace, L.ksum), true,
-                               d.max_k > 0 && d.total_k > 0, hs);
+                               at<uint8_t>(workspace, L.v_scale), at<double>(workspace, L.ksum), true, has_k,
+                               hs);
   if (st != SAGE_OK) return st;
   sage::Fp4AttnArgs a{};
   a.q4 = at<uint8_t>(workspace, L.q_codes);

@@ -363,6 +363,8 @@ def _vattn(shape, q=FAKE, k=FAKE + 2 ** 30, v=FAKE + 2 ** 31, cq=FAKE + 2 ** 34,
     ("null cu_seqlens_k", dict(shape=_vshape(), ck=None), sage.SAGE_ERR_INVALID_ARGUMENT),
     ("misaligned cu_seqlens", dict(shape=_vshape(), cq=FAKE + 2 ** 34 + 2), sage.SAGE_ERR_INVALID_ARGUMENT),
     ("null o", dict(shape=_vshape(), o=None), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("null k with keys", dict(shape=_vshape(), k=None), sage.SAGE_ERR_INVALID_ARGUMENT),
+    ("null k, v without keys reach the device", dict(shape=_vshape(tk=0), k=None, v=None), sage.SAGE_ERR_HIP),
     ("misaligned v", dict(shape=_vshape(), v=FAKE + 2 ** 31 + 8), sage.SAGE_ERR_INVALID_ARGUMENT),
     ("small workspace", dict(shape=_vshape(), ws_bytes=4096), sage.SAGE_ERR_WORKSPACE),
     ("o aliases q", dict(shape=_vshape(), o=FAKE + 4096), sage.SAGE_ERR_INVALID_ARGUMENT),
@@ -411,6 +413,10 @@ def test_fp4_varlen_entry_points_validate():
     assert fwd(ctypes.byref(_vshape(gran=1)), q, k, v, cq, ck, o, 0, 0.1, ws, n, None) == sage.SAGE_ERR_UNSUPPORTED
     assert fwd(ctypes.byref(_vshape(d=96)), q, k, v, cq, ck, o, 0, 0.1, ws, n, None) == sage.SAGE_ERR_UNSUPPORTED
     assert fwd(ctypes.byref(_vshape(tq=0)), None, None, None, None, None, None, 0, 0.1, None, 0, None) == sage.SAGE_OK
+    assert fwd(sp, q, None, v, cq, ck, o, 0, 0.1, ws, n, None) == bad                  # null k with keys
+    nok = _vshape(tk=0, mk=0)
+    assert fwd(ctypes.byref(nok), q, None, None, cq, ck, o, 0, 0.1, ws, sage.sage_fp4_varlen_workspace_bytes(nok),
+               None) == sage.SAGE_ERR_HIP                                                # no keys: reaches the device
     # quantisation alone
     qc, qs, kc, ks, km, vc, vs = (FAKE + i * G for i in range(4, 11))
     qw = sage.lib.sage_quant_fp4_varlen_workspace_bytes(sp)

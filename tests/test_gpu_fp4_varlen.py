@@ -212,3 +212,40 @@ def test_fp4_varlen_serving_mix_full_size():
         say(f"   seq {b} (len {q1 - q0}): cos={c:.7f} rel_l1={r:.2e}; vs fp64: HIP {ce:.5f} oracle {ce_oracle:.5f}")
         assert c >= COS_ORACLE and r <= RL1_ORACLE
         assert abs(ce - ce_oracle) <= 1e-3
+
+
+# ------------------------------------------------------------------ bounds and degenerate batches
+@pytest.mark.parametrize("fp4", [False, True])
+def test_varlen_loose_bounds_give_the_same_output(fp4):
+    """max_seqlen_q/k are bounds, not the exact maxima: looser bounds (a larger
+    work list, more V tiles per sequence) change nothing in the output."""
+    w = CASES[2]
+    q, k, v, cq, ck = (t.cuda() for t in W.generate_varlen(w))
+    mq, mk = max(w.lens_q), max(w.lens_k)
+    say("varlen loose bounds", "fp4" if fp4 else "fp8", mq, mk)
+    if fp4:
+        run = lambda a, b: sage.sage_attn_fwd_fp4_varlen(q, k, v, cq, ck, a, b, is_causal=True)
+    else:
+        run = lambda a, b: sage.sage_attn_fwd_varlen(q, k, v, cq, ck, a, b, is_causal=True)
+    exact_bounds = run(mq, mk)
+    loose = run(3 * mq + 5, 2 * mk + 129)
+    torch.cuda.synchronize()
+    assert torch.equal(exact_bounds, loose)
+
+
+@pytest.mark.parametrize("fp4", [False, True])
+def test_varlen_without_any_keys_gives_zero_rows(fp4):
+    """Queries but not a single key in the batch (total_k = 0): every output
+    row is exactly zero, as for a sequence without keys."""
+    w = W.VarlenWorkload("no_keys", (5, 300, 1), (0, 0, 0), Hq=4, Hkv=2, d=128, dtype="bf16", causal=False,
+                         pv="fp4" if fp4 else "fp8")
+    say("varlen without keys", w.pv)
+    q, k, v, cq, ck = (t.cuda() for t in W.generate_varlen(w))
+    assert k.shape[0] == 0
+    for max_k in (0, 64):
+        if fp4:
+            o = sage.sage_attn_fwd_fp4_varlen(q, k, v, cq, ck, 300, max_k)
+        else:
+            o = sage.sage_attn_fwd_varlen(q, k, v, cq, ck, 300, max_k)
+        torch.cuda.synchronize()
+        assert o.shape == q.shape and not o.float().abs().sum().item(), max_k
