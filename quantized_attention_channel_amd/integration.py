@@ -5,6 +5,10 @@
   so graph capture such as ``torch.compile`` traces through it as one opaque
   node (thu-ml/SageAttention repo card, "How it works", and the heatdrop.ai
   review, "Key highlights": torch.compile support).
+* ``attn_fwd_varlen_op``: the same for packed variable-length batches
+  (``torch.ops.sage_mi355x.attn_fwd_varlen``; heatdrop.ai review, "Key
+  highlights": variable sequence lengths within a batch), for serving code
+  that keeps the tokens of all requests in one [total, heads, head_dim] tensor.
 * ``patch_sdpa``: a guarded drop-in for ``torch.nn.functional.
   scaled_dot_product_attention``. The heatdrop.ai review ("Caveats") warns that
   replacing that function wholesale breaks many models, because some of their
@@ -21,7 +25,7 @@ from typing import Optional
 
 import torch
 
-from . import DTYPES, sageattn
+from . import DTYPES, sageattn, sageattn_varlen
 
 _LIB = "sage_mi355x"
 
@@ -37,6 +41,23 @@ def attn_fwd_op(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bo
 
 @attn_fwd_op.register_fake
 def _attn_fwd_fake(q, k, v, is_causal, sm_scale, pv_dtype, tensor_layout, qk_gran):
+    return torch.empty_like(q, memory_format=torch.contiguous_format)
+
+
+@torch.library.custom_op(f"{_LIB}::attn_fwd_varlen", mutates_args=())
+def attn_fwd_varlen_op(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                       cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int, is_causal: bool,
+                       sm_scale: float, pv_dtype: str, qk_gran: str) -> torch.Tensor:
+    """Quantised attention over a packed batch: q [total_q, Hq, d], k and v
+    [total_k, Hkv, d], int32 cu_seqlens of B + 1 offsets; a fresh output shaped
+    like q. pv_dtype "fp8", "fp16" or "fp4"."""
+    return sageattn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, is_causal=is_causal,
+                           sm_scale=sm_scale, pv_dtype=pv_dtype, qk_quant_gran=qk_gran)
+
+
+@attn_fwd_varlen_op.register_fake
+def _attn_fwd_varlen_fake(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, is_causal, sm_scale,
+                          pv_dtype, qk_gran):
     return torch.empty_like(q, memory_format=torch.contiguous_format)
 
 
@@ -116,4 +137,4 @@ class patch_sdpa:
         return False
 
 
-__all__ = ["attn_fwd_op", "sdpa_supported", "patch_sdpa"]
+__all__ = ["attn_fwd_op", "attn_fwd_varlen_op", "sdpa_supported", "patch_sdpa"]

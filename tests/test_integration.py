@@ -13,7 +13,7 @@ import torch
 import torch.nn.functional as F
 
 import quantized_attention_channel_amd as sage
-from quantized_attention_channel_amd.integration import attn_fwd_op, patch_sdpa, sdpa_supported
+from quantized_attention_channel_amd.integration import attn_fwd_op, attn_fwd_varlen_op, patch_sdpa, sdpa_supported
 
 
 def _meta(*shape, dtype=torch.float16):
@@ -24,6 +24,14 @@ def test_operator_is_registered_with_a_fake_implementation():
     assert hasattr(torch.ops.sage_mi355x, "attn_fwd")
     q, k = _meta(2, 8, 100, 64), _meta(2, 4, 300, 64)
     out = torch.ops.sage_mi355x.attn_fwd(q, k, k, False, 0.125, "fp8", "HND", "per_block")
+    assert out.shape == q.shape and out.dtype == q.dtype and out.device.type == "meta"
+
+
+def test_varlen_operator_is_registered_with_a_fake_implementation():
+    assert hasattr(torch.ops.sage_mi355x, "attn_fwd_varlen")
+    q, k = _meta(700, 8, 128, dtype=torch.bfloat16), _meta(900, 2, 128, dtype=torch.bfloat16)
+    cu = torch.empty(4, dtype=torch.int32, device="meta")
+    out = torch.ops.sage_mi355x.attn_fwd_varlen(q, k, k, cu, cu, 400, 500, True, 0.088, "fp4", "per_block")
     assert out.shape == q.shape and out.dtype == q.dtype and out.device.type == "meta"
 
 
@@ -196,3 +204,48 @@ def test_compiled_model_against_oracle(backend):
         raise
     torch.cuda.synchronize()
     _against_oracle(o, q, k, v, causal=False, sm_scale=d ** -0.5, pv="fp16", gran="per_block")
+
+
+@pytest.mark.gpu
+@pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")
+@pytest.mark.parametrize("pv", ["fp8", "fp4"])
+def test_compiled_varlen_operator_against_oracle(pv):
+    """The packed-batch operator inside a torch.compile graph (aot_eager), with
+    torch work on both sides of it: passes torch.library's checks, equals
+    sageattn_varlen bit for bit, and meets the parity bars against the oracle
+    run per sequence."""
+    import numpy as np
+    import workloads as W
+    from oracle import sage_ref
+    from tests.parity_util import COS_ORACLE, RL1_ORACLE, cos, rel_l1
+    w = W.VarlenWorkload("compiled", (300, 1, 129, 0, 77), (300, 1, 129, 0, 77), Hq=4, Hkv=2, d=128,
+                         dtype="bf16", causal=True, pv=pv)
+    q, k, v, cq, ck = (t.cuda() for t in W.generate_varlen(w))
+    mq = mk = max(w.lens_q)
+    torch.library.opcheck(attn_fwd_varlen_op, (q, k, v, cq, ck, mq, mk, True, w.sm_scale, pv, "per_block"),
+                          test_utils=("test_schema", "test_faketensor"))
+
+    def f(q, k, v):
+        o = torch.ops.sage_mi355x.attn_fwd_varlen(q * 1.5, k, v, cq, ck, mq, mk, True, w.sm_scale, pv, "per_block")
+        return o, o.float().sum(dim=-1)
+
+    o, rowsum = torch.compile(f, backend="aot_eager", fullgraph=True)(q, k, v)
+    want = sage.sageattn_varlen(q * 1.5, k, v, cq, ck, mq, mk, is_causal=True, sm_scale=w.sm_scale, pv_dtype=pv)
+    torch.cuda.synchronize()
+    assert torch.equal(o, want) and torch.equal(rowsum, want.float().sum(dim=-1))
+    qn, kn, vn = ((q * 1.5).float().cpu().numpy(), k.float().cpu().numpy(), v.float().cpu().numpy())
+    got = o.float().cpu().numpy().astype(np.float64)
+    cqs, cks = cq.tolist(), ck.tolist()
+    if pv == "fp4":
+        ref = np.zeros(qn.shape, np.float64)
+        for b in range(w.B):
+            q0, q1, k0, k1 = cqs[b], cqs[b + 1], cks[b], cks[b + 1]
+            if q1 > q0 and k1 > k0:
+                seq = [np.ascontiguousarray(x[a:e].transpose(1, 0, 2))[None]
+                       for x, a, e in ((qn, q0, q1), (kn, k0, k1), (vn, k0, k1))]
+                r = sage_ref.sage_attention_fp4(*seq, dtype=w.dtype, is_causal=True, sm_scale=w.sm_scale)
+                ref[q0:q1] = r[0].transpose(1, 0, 2)
+    else:
+        ref = sage_ref.sage_attention_varlen(qn, kn, vn, cqs, cks, dtype=w.dtype, is_causal=True,
+                                             sm_scale=w.sm_scale, pv=pv)
+    assert cos(got, ref) >= COS_ORACLE and rel_l1(got, ref) <= RL1_ORACLE
