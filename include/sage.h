@@ -330,7 +330,9 @@ sage_status sage_quant_fp4(const sage_shape* s, const void* q, const void* k, co
 
 /* The FP4 attention kernel alone, from codes as sage_quant_fp4 writes them
  * (the softmax temperature is already in the Q codes); o and is_causal as for
- * sage_attn_fwd. Needs no workspace. */
+ * sage_attn_fwd. Needs no workspace. The kernel reads k_scale in whole 4-byte
+ * words: at d = 64 with B * Hkv * Nk odd, the buffer must stay readable for
+ * the 2 bytes past its last scale byte (their values are not used). */
 sage_status sage_attn_fwd_fp4_codes(const sage_shape* s, const uint8_t* q_codes, const uint8_t* q_scale,
                                     const uint8_t* k_codes, const uint8_t* k_scale, const uint8_t* v_codes,
                                     const uint8_t* v_scale, void* o, int32_t is_causal, void* stream);

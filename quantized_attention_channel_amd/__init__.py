@@ -447,8 +447,12 @@ def fp4_buffers(shape: SageShape, device) -> dict:
     B, Hq, Hkv, Nq, Nk, d = shape.batch, shape.heads_q, shape.heads_kv, shape.seq_q, shape.seq_k, shape.head_dim
     npad = sage_v_codes_stride(Nk)
     u8 = dict(dtype=torch.uint8, device=device)
+    nks = B * Hkv * Nk * (d // 32)
+    # (the attention kernel reads the K scales in whole 4-byte words: keep the
+    #  storage readable up to the next multiple of 4 bytes)
+    k_scale = torch.empty(nks + (-nks) % 4, **u8)[:nks].view(B, Hkv, Nk, d // 32)
     return dict(q_codes=torch.empty((B, Hq, Nq, d // 2), **u8), q_scale=torch.empty((B, Hq, Nq, d // 32), **u8),
-                k_codes=torch.empty((B, Hkv, Nk, d // 2), **u8), k_scale=torch.empty((B, Hkv, Nk, d // 32), **u8),
+                k_codes=torch.empty((B, Hkv, Nk, d // 2), **u8), k_scale=k_scale,
                 k_mean=torch.empty((B, Hkv, d), dtype=torch.float32, device=device),
                 v_codes=torch.empty((B, Hkv, d, npad // 2), **u8),
                 v_scale=torch.empty((B, Hkv, npad // 128, d, 4), **u8))
@@ -490,6 +494,9 @@ def sage_attn_fwd_fp4_codes(shape: SageShape, codes: dict, o: torch.Tensor, *, i
     _expect(o, "o", in_dtype, B * Hq * Nq * d, dev)
     for name, n in sizes.items():
         _expect(codes.get(name), name, torch.uint8, n, dev)
+    ks = codes["k_scale"]
+    if ks.untyped_storage().nbytes() - ks.storage_offset() < sizes["k_scale"] + (-sizes["k_scale"]) % 4:
+        raise ValueError("k_scale is read in whole 4-byte words: its storage needs 2 more bytes (see fp4_buffers)")
     _check(lib.sage_attn_fwd_fp4_codes(_ref(shape), _ptr(codes["q_codes"]), _ptr(codes["q_scale"]),
                                        _ptr(codes["k_codes"]), _ptr(codes["k_scale"]), _ptr(codes["v_codes"]),
                                        _ptr(codes["v_scale"]), _ptr(o), int(bool(is_causal)), _stream(dev)),

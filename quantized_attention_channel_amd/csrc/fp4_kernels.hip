@@ -563,7 +563,12 @@ __global__ __launch_bounds__(512, 1) void attn_fp4_kernel(Fp4AttnArgs a) {
   const uint8_t* kbase = a.k4 + k_row * (D / 2);
   const uint32_t kbytes = (uint32_t)nk * (D / 2);
   const uint8_t* ksbase = a.k_sc + k_row * (D / kMx);
-  const uint32_t ksbytes = (uint32_t)nk * (D / kMx);
+  // The K scales are staged in 4-byte words. At d = 64 a key has two scale
+  // bytes, so with an odd key count the last key shares its word with two bytes
+  // past the range, and a range check on that word would return it as zero:
+  // the range is rounded up to whole words (the two extra bytes land in the
+  // slot of key nk, which is masked; the buffers hold them, see sage.h).
+  const uint32_t ksbytes = ((uint32_t)nk * (D / kMx) + 3u) & ~3u;
   const auto rv = make_rsrc(a.v4 + v_off, (uint32_t)v_len);
   const auto rvs = make_rsrc(a.v_sc + vs_tile * (kBkv * D / kMx), (uint32_t)(vs_tiles * (kBkv * D / kMx)));
   uint32_t koff, voff;

@@ -1020,7 +1020,7 @@ sage_status sage_attn_fwd_fp4_codes(const sage_shape* s, const uint8_t* q_codes,
     return SAGE_ERR_INVALID_ARGUMENT;
   const Fp4Sizes z = fp4_sizes(d);
   if (aliased({{o, size_t(d.B * d.Hq * d.Nq * d.D) * 2}},
-              {{q_codes, z.q_codes}, {q_scale, z.q_scale}, {k_codes, z.k_codes}, {k_scale, z.k_scale},
+              {{q_codes, z.q_codes}, {q_scale, z.q_scale}, {k_codes, z.k_codes}, {k_scale, (z.k_scale + 3) & ~size_t(3)},
                {v_codes, z.v_codes}, {v_scale, z.v_scale}}))
     return SAGE_ERR_INVALID_ARGUMENT;
   return from_hip(sage::launch_attn_fp4(

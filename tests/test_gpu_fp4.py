@@ -121,6 +121,10 @@ ATTN_CASES = [
     (W.TINY.with_(Hq=2, Hkv=2, N=640, d=128, outliers=4), False),
     (W.TINY.with_(Hq=2, Hkv=2, N=129, d=64), True),
     (W.TINY.with_(Hq=1, Hkv=1, N=1, d=128), False),
+    # d = 64 with an odd key count, seen by every row: the last key's two K scale
+    # bytes share a 4-byte word with the bytes past the head's range
+    (W.TINY.with_(Hq=2, Hkv=1, N=257, d=64, dtype="bf16"), False),
+    (W.TINY.with_(B=2, Hq=2, Hkv=1, N=129, d=64, layout="NHD", k_off_var=40.0), False),
 ]
 
 
@@ -162,6 +166,29 @@ def test_fp4_codes_entry_equals_whole_forward(sage):
     again = sage.sage_attn_fwd_fp4(q, k, v, is_causal=True, sm_scale=w.sm_scale)
     torch.cuda.synchronize()
     assert torch.equal(again, whole), "deterministic"
+
+
+def test_fp4_codes_entry_at_d64_with_an_odd_scale_count(sage):
+    """d = 64 and B * Hkv * Nk odd: the K scales end 2 bytes into a 4-byte word.
+    The codes entry point (buffers from fp4_buffers, padded to whole words)
+    equals the whole forward and the oracle; a K scale tensor without the
+    padding is refused by the binding before any library call."""
+    w = W.TINY.with_(Hq=2, Hkv=1, N=257, d=64)
+    q, k, v = (t.cuda() for t in W.generate(w))
+    whole = sage.sage_attn_fwd_fp4(q, k, v, sm_scale=w.sm_scale)
+    codes = sage.sage_quant_fp4(q, k, v, sm_scale=w.sm_scale)
+    o = torch.empty_like(q)
+    shape = sage.shape_of(q, k, "HND")
+    sage.sage_attn_fwd_fp4_codes(shape, codes, o)
+    torch.cuda.synchronize()
+    assert torch.equal(o, whole)
+    ref = sage_ref.sage_attention_fp4(*(t.float().cpu().numpy() for t in (q, k, v)), dtype=w.dtype, is_causal=False,
+                                      sm_scale=w.sm_scale)
+    got = o.float().cpu().numpy()
+    assert cos(got, ref) >= COS_ORACLE and rel_l1(got, ref) <= RL1_ORACLE
+    exact_size = dict(codes, k_scale=codes["k_scale"].clone())
+    with pytest.raises(ValueError, match="4-byte words"):
+        sage.sage_attn_fwd_fp4_codes(shape, exact_size, o)
 
 
 def test_fp4_zero_q_gives_mean_of_quantised_values(sage):

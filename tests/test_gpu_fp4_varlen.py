@@ -38,6 +38,10 @@ CASES = [
                      causal=False, pv="fp4"),
     W.VarlenWorkload("fp4_cross_d64_causal", (200, 50, 129), (100, 300, 129), Hq=2, Hkv=2, d=64, dtype="bf16",
                      causal=True, pv="fp4"),
+    # d = 64, odd key counts seen by every row (the last key's K scales end
+    # 2 bytes into a 4-byte word)
+    W.VarlenWorkload("fp4_cross_d64_odd_keys", (5, 300, 64, 40), (701, 1, 33, 257), Hq=4, Hkv=2, d=64,
+                     dtype="fp16", causal=False, pv="fp4"),
 ]
 
 

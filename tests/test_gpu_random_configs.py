@@ -118,3 +118,71 @@ def test_random_varlen_quant_stages(i):
     w, gran = VARLEN[i]
     say("random varlen quant stages", i, w.lens_q, w.lens_k, w.Hq, w.Hkv, w.d, w.dtype, w.pv, gran)
     check_varlen_quant(w, gran)
+
+
+# ------------------------------------------------------------------ the FP4 microscaling variant
+def _fp4_dense_config(i):
+    r = random.Random(7000 + i)
+    hkv = r.choice([1, 2, 3])
+    causal = r.random() < 0.5
+    nk = r.choice([1, r.randint(2, 300), r.randint(300, 1500)])
+    nq = nk if causal else r.choice([1, r.randint(2, 400), r.randint(400, 1500)])
+    return dict(B=r.choice([1, 2]), Hkv=hkv, Hq=hkv * r.choice([1, 2, 4]), nq=nq, nk=nk, d=r.choice([64, 128]),
+                dtype=r.choice(["fp16", "bf16"]), layout=r.choice(["HND", "NHD"]), causal=causal,
+                k_off_var=r.choice([0.0, 4.0, 40.0]))
+
+
+FP4_DENSE = [_fp4_dense_config(i) for i in range(12)]
+
+
+@pytest.mark.parametrize("i", range(len(FP4_DENSE)))
+def test_random_fp4_dense_config(i):
+    """The FP4 variant on a random dense configuration: every row against the
+    oracle's FP4 attention at the bars, and as close to fp64 attention as the
+    oracle (MXFP4 is the coarser method)."""
+    c = FP4_DENSE[i]
+    say("random fp4 dense", i, c)
+    n = max(c["nq"], c["nk"])
+    w = W.TINY.with_(B=c["B"], Hq=c["Hq"], Hkv=c["Hkv"], N=n, d=c["d"], dtype=c["dtype"], layout=c["layout"],
+                     k_off_var=c["k_off_var"], seed=7000 + i)
+    q, k, v = W.generate(w)
+    q, k, v = _cut(q, c["nq"], c["layout"]), _cut(k, c["nk"], c["layout"]), _cut(v, c["nk"], c["layout"])
+    o = sage.sage_attn_fwd_fp4(q.cuda(), k.cuda(), v.cuda(), is_causal=c["causal"], sm_scale=w.sm_scale,
+                               tensor_layout=c["layout"])
+    torch.cuda.synchronize()
+    got = sage_ref.as_hnd(o.float().cpu().numpy(), c["layout"])
+    qn, kn, vn = (sage_ref.as_hnd(t.float().numpy(), c["layout"]) for t in (q, k, v))
+    ref = sage_ref.sage_attention_fp4(qn, kn, vn, dtype=c["dtype"], is_causal=c["causal"], sm_scale=w.sm_scale)
+    ex = exact.exact_attention(qn, kn, vn, is_causal=c["causal"], sm_scale=w.sm_scale)
+    cc, r, ce, ce_oracle = cos(got, ref), rel_l1(got, ref), cos(got, ex), cos(ref, ex)
+    say(f"   cos={cc:.7f} rel_l1={r:.2e}; vs fp64: HIP {ce:.5f} oracle {ce_oracle:.5f}")
+    assert np.isfinite(got).all()
+    assert cc >= COS_ORACLE and r <= RL1_ORACLE and abs(ce - ce_oracle) <= 1e-3
+
+
+FP4_VARLEN = [_varlen_config(100 + i)[0] for i in range(12)]
+
+
+@pytest.mark.parametrize("i", range(len(FP4_VARLEN)))
+def test_random_fp4_varlen_config(i):
+    """The FP4 variant on a random packed mix: every sequence's MXFP4 stages bit
+    for bit, every row against the oracle's FP4 attention run per sequence."""
+    from tests.test_gpu_fp4_varlen import check_fp4_varlen_quant, oracle_fp4_varlen
+    w = FP4_VARLEN[i].with_(pv="fp4")
+    say("random fp4 varlen", i, w.lens_q, w.lens_k, w.Hq, w.Hkv, w.d, w.dtype, w.causal)
+    check_fp4_varlen_quant(w)
+    q, k, v, cq, ck = W.generate_varlen(w)
+    o = sage.sage_attn_fwd_fp4_varlen(q.cuda(), k.cuda(), v.cuda(), cq.cuda(), ck.cuda(), max(w.lens_q),
+                                      max(w.lens_k), is_causal=w.causal, sm_scale=w.sm_scale)
+    torch.cuda.synchronize()
+    got = o.float().cpu().numpy().astype(np.float64)
+    qn, kn, vn = (t.float().numpy() for t in (q, k, v))
+    ref = oracle_fp4_varlen(qn, kn, vn, cq.tolist(), ck.tolist(), dtype=w.dtype, is_causal=w.causal,
+                            sm_scale=w.sm_scale)
+    assert np.isfinite(got).all()
+    for b in range(w.B):
+        if w.lens_k[b] == 0:
+            assert not got[cq[b]:cq[b + 1]].any()
+    cc, r = cos(got, ref), rel_l1(got, ref)
+    say(f"   cos={cc:.7f} rel_l1={r:.2e}")
+    assert cc >= COS_ORACLE and r <= RL1_ORACLE
