@@ -132,7 +132,7 @@ def _fp4_dense_config(i):
                 k_off_var=r.choice([0.0, 4.0, 40.0]))
 
 
-FP4_DENSE = [_fp4_dense_config(i) for i in range(12)]
+FP4_DENSE = [_fp4_dense_config(i) for i in range(24)]
 
 
 @pytest.mark.parametrize("i", range(len(FP4_DENSE)))
@@ -160,7 +160,7 @@ def test_random_fp4_dense_config(i):
     assert cc >= COS_ORACLE and r <= RL1_ORACLE and abs(ce - ce_oracle) <= 1e-3
 
 
-FP4_VARLEN = [_varlen_config(100 + i)[0] for i in range(12)]
+FP4_VARLEN = [_varlen_config(100 + i)[0] for i in range(24)]
 
 
 @pytest.mark.parametrize("i", range(len(FP4_VARLEN)))
