@@ -186,3 +186,58 @@ def test_random_fp4_varlen_config(i):
     cc, r = cos(got, ref), rel_l1(got, ref)
     say(f"   cos={cc:.7f} rel_l1={r:.2e}")
     assert cc >= COS_ORACLE and r <= RL1_ORACLE
+
+
+# ------------------------------------------------------------------ longer random shapes, every path
+def _long_config(i):
+    r = random.Random(9000 + i)
+    hkv = r.choice([1, 2])
+    causal = r.random() < 0.5
+    nk = r.randint(1500, 6000)
+    nq = nk if causal else r.choice([r.randint(1, 300), r.randint(1500, 6000)])
+    pv = r.choice(["fp8", "fp16", "fp4"])
+    return dict(B=1, Hkv=hkv, Hq=hkv * r.choice([1, 2]), nq=nq, nk=nk, d=r.choice([64, 128]),
+                dtype=r.choice(["fp16", "bf16"]), layout=r.choice(["HND", "NHD"]), causal=causal, pv=pv,
+                gran="per_block" if pv == "fp4" else r.choice(["per_block", "per_thread"]),
+                k_off_var=r.choice([0.0, 4.0, 40.0]))
+
+
+LONG = [_long_config(i) for i in range(12)]
+
+
+@pytest.mark.parametrize("i", range(len(LONG)))
+def test_random_long_config(i):
+    """Longer random shapes (1.5k to 6k keys, ragged tails) on every path
+    (FP8 or FP16 PV at either granularity, or the FP4 variant): every row
+    against the oracle."""
+    c = LONG[i]
+    say("random long", i, c)
+    n = max(c["nq"], c["nk"])
+    w = W.TINY.with_(B=c["B"], Hq=c["Hq"], Hkv=c["Hkv"], N=n, d=c["d"], dtype=c["dtype"], layout=c["layout"],
+                     k_off_var=c["k_off_var"], seed=9000 + i)
+    q, k, v = W.generate(w)
+    q, k, v = _cut(q, c["nq"], c["layout"]), _cut(k, c["nk"], c["layout"]), _cut(v, c["nk"], c["layout"])
+    qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
+    if c["pv"] == "fp4":
+        o = sage.sage_attn_fwd_fp4(qg, kg, vg, is_causal=c["causal"], sm_scale=w.sm_scale, tensor_layout=c["layout"])
+    else:
+        o = sage.sage_attn_fwd(qg, kg, vg, is_causal=c["causal"], sm_scale=w.sm_scale, pv_dtype=c["pv"],
+                               tensor_layout=c["layout"], qk_gran=c["gran"])
+    torch.cuda.synchronize()
+    got = sage_ref.as_hnd(o.float().cpu().numpy(), c["layout"])
+    qn, kn, vn = (sage_ref.as_hnd(t.float().numpy(), c["layout"]) for t in (q, k, v))
+    ex = exact.exact_attention(qn, kn, vn, is_causal=c["causal"], sm_scale=w.sm_scale)
+    if c["pv"] == "fp4":
+        ref = sage_ref.sage_attention_fp4(qn, kn, vn, dtype=c["dtype"], is_causal=c["causal"], sm_scale=w.sm_scale)
+    else:
+        bq, bk = GRAN_BLK[c["gran"]]
+        ref = sage_ref.sage_attention(qn, kn, vn, dtype=c["dtype"], is_causal=c["causal"], sm_scale=w.sm_scale,
+                                      pv=c["pv"], blk_q=bq, blk_k=bk)
+    cc, r, ce, ce_oracle = cos(got, ref), rel_l1(got, ref), cos(got, ex), cos(ref, ex)
+    say(f"   cos={cc:.7f} rel_l1={r:.2e}; vs fp64: HIP {ce:.6f} oracle {ce_oracle:.6f}")
+    assert np.isfinite(got).all()
+    assert cc >= COS_ORACLE and r <= RL1_ORACLE
+    if c["pv"] == "fp4":
+        assert abs(ce - ce_oracle) <= 1e-3
+    else:
+        assert ce >= COS_EXACT
