@@ -241,3 +241,50 @@ def test_random_long_config(i):
         assert abs(ce - ce_oracle) <= 1e-3
     else:
         assert ce >= COS_EXACT
+
+
+# ------------------------------------------------------------------ quantisation stages on random shapes
+def _quant_config(i):
+    r = random.Random(11000 + i)
+    hkv = r.choice([1, 2, 3])
+    return dict(B=r.choice([1, 2, 3]), Hkv=hkv, Hq=hkv * r.choice([1, 2, 4]), nq=r.randint(1, 2000),
+                nk=r.randint(1, 2000), d=r.choice([64, 128]), dtype=r.choice(["fp16", "bf16"]),
+                layout=r.choice(["HND", "NHD"]), gran=r.choice(["per_block", "per_thread"]),
+                k_off_var=r.choice([0.0, 4.0, 40.0]))
+
+
+QUANT = [_quant_config(i) for i in range(24)]
+
+
+@pytest.mark.parametrize("i", range(len(QUANT)))
+def test_random_quant_stages(i):
+    """Every quantisation stage on a random shape (independent query and key
+    counts), bit for bit against the oracle: the K mean, Q/K INT8 codes and
+    scales at the drawn granularity, V e4m3 codes (with the zero padding) and
+    scales, and every MXFP4 stage."""
+    from tests.test_gpu_fp4 import check_fp4_stages
+    c = QUANT[i]
+    say("random quant stages", i, c)
+    n = max(c["nq"], c["nk"])
+    w = W.TINY.with_(B=c["B"], Hq=c["Hq"], Hkv=c["Hkv"], N=n, d=c["d"], dtype=c["dtype"], layout=c["layout"],
+                     k_off_var=c["k_off_var"], seed=11000 + i)
+    q, k, v = W.generate(w)
+    q, k, v = _cut(q, c["nq"], c["layout"]), _cut(k, c["nk"], c["layout"]), _cut(v, c["nk"], c["layout"])
+    qg, kg, vg = q.cuda(), k.cuda(), v.cuda()
+    qk = sage.sage_quant_qk(qg, kg, tensor_layout=c["layout"], qk_gran=c["gran"])
+    vc, vs = sage.sage_quant_v(vg, tensor_layout=c["layout"])
+    f4 = sage.sage_quant_fp4(qg, kg, vg, tensor_layout=c["layout"], sm_scale=w.sm_scale)
+    torch.cuda.synchronize()
+    qn, kn, vn = (sage_ref.as_hnd(t.float().numpy(), c["layout"]) for t in (q, k, v))
+    bq, bk = GRAN_BLK[c["gran"]]
+    ref = sage_ref.quant_qk(qn, kn, blk_q=bq, blk_k=bk)
+    assert np.array_equal(qk["k_mean"].cpu().numpy(), ref["k_mean"])
+    assert np.array_equal(qk["q_scale"].cpu().numpy(), ref["q_scale"])
+    assert np.array_equal(qk["k_scale"].cpu().numpy(), ref["k_scale"])
+    assert np.array_equal(qk["q_codes"].cpu().numpy(), ref["q8"])
+    assert np.array_equal(qk["k_codes"].cpu().numpy(), ref["k8"])
+    rc, rs = sage_ref.quant_v_fp8(vn)
+    vc = vc.cpu().numpy()
+    assert np.array_equal(vs.cpu().numpy(), rs)
+    assert np.array_equal(vc[..., :c["nk"]], rc) and not vc[..., c["nk"]:].any()
+    check_fp4_stages({n_: t for n_, t in f4.items()}, qn, kn, vn, w.sm_scale)
