@@ -49,23 +49,34 @@ __global__ __launch_bounds__(256) void channel_stats_kernel(
   float vm[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) { ks[e] = 0.0; vm[e] = 0.0f; }
-#pragma unroll 4
-  for (int t = t_begin + r0; t < t_end; t += RPI) {   // (unrolled: several loads in flight)
-    const int64_t off = base + (int64_t)t * geo.tok_stride;
-    if (WITH_K) {
-      i32x4 raw = *reinterpret_cast<const i32x4*>(k + off);
+  // All of the thread's rows are loaded before any is used, so every load is
+  // in flight at once (16 rows of 16 bytes per tensor). Rows past the end
+  // re-read the chunk's first row and add -0.0 to the sums (an exact
+  // identity) or 0 to the maxima. (A chunk wholly past a packed sequence's
+  // keys loads nothing and writes zero partials.)
+  constexpr int ROWS = kStatChunk / RPI;
+  i32x4 rk[WITH_K ? ROWS : 1], rv[WITH_V ? ROWS : 1];
+  if (t_begin < t_end) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint16_t bits = (uint16_t)(((uint32_t)raw[e / 2]) >> (16 * (e & 1)));
-        ks[e] += (double)T::to_f32(bits);
-      }
+    for (int i = 0; i < ROWS; ++i) {
+      const int t = t_begin + r0 + i * RPI;
+      const int64_t off = base + (int64_t)(t < t_end ? t : t_begin) * geo.tok_stride;
+      if (WITH_K) rk[i] = *reinterpret_cast<const i32x4*>(k + off);
+      if (WITH_V) rv[i] = *reinterpret_cast<const i32x4*>(v + off);
     }
-    if (WITH_V) {
-      i32x4 raw = *reinterpret_cast<const i32x4*>(v + off);
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) {
+      const bool live = t_begin + r0 + i * RPI < t_end;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        uint16_t bits = (uint16_t)(((uint32_t)raw[e / 2]) >> (16 * (e & 1)));
-        vm[e] = fmaxf(vm[e], fabsf(T::to_f32(bits)));
+        if (WITH_K) {
+          const uint16_t bits = (uint16_t)(((uint32_t)rk[i][e / 2]) >> (16 * (e & 1)));
+          ks[e] += live ? (double)T::to_f32(bits) : -0.0;
+        }
+        if (WITH_V) {
+          const uint16_t bits = (uint16_t)(((uint32_t)rv[i][e / 2]) >> (16 * (e & 1)));
+          vm[e] = fmaxf(vm[e], live ? fabsf(T::to_f32(bits)) : 0.0f);
+        }
       }
     }
   }
@@ -94,36 +105,53 @@ __global__ __launch_bounds__(256) void channel_stats_kernel(
 // fp32); s_v = a_v / 448 and 448 / a_v (both correctly rounded fp32 divides).
 // (packed batches: the token count is the sequence's; a sequence without keys
 // gets a zero mean)
+// kFinalizeThreads threads per (b, kv-head): P = kFinalizeThreads / D threads
+// per channel, thread p folding chunks p, p + P, ... with eight independent
+// accumulators (eight loads in flight each), the P results combined in a
+// fixed order through LDS, so the result does not depend on timing.
+constexpr int kFinalizeThreads = 512;
 template <int D, bool WITH_K, bool WITH_V>
-__global__ __launch_bounds__(D) void channel_finalize_kernel(
+__global__ __launch_bounds__(kFinalizeThreads) void channel_finalize_kernel(
     int N, int chunks, const double* __restrict__ ksum_part, const float* __restrict__ vmax_part,
     float* __restrict__ k_mean, float* __restrict__ v_scale, float* __restrict__ v_inv, int H,
     const SeqSpan* __restrict__ seq) {
-  const int bh = blockIdx.x, c = threadIdx.x;
+  constexpr int P = kFinalizeThreads / D;
+  constexpr int U = 8;
+  __shared__ double part_k[WITH_K ? P : 1][D];
+  __shared__ float part_v[WITH_V ? P : 1][D];
+  const int bh = blockIdx.x, c = threadIdx.x % D, pi = threadIdx.x / D;
   const int n = seq ? seq[bh / H].nk : N;
   const int64_t p = (int64_t)bh * chunks * D + c;
-  // Eight independent accumulators keep eight loads in flight (a single chain
-  // would wait one memory latency per chunk); they are combined in a fixed
-  // order, so the result does not depend on timing.
-  constexpr int U = 8;
   if (WITH_K) {
     double s[U] = {};
-    int i = 0;
-    for (; i + U <= chunks; i += U)
+    int i = pi;
+    for (; i + (U - 1) * P < chunks; i += U * P)
 #pragma unroll
-      for (int u = 0; u < U; ++u) s[u] += ksum_part[p + (int64_t)(i + u) * D];
-    for (; i < chunks; ++i) s[0] += ksum_part[p + (int64_t)i * D];
-    const double total = ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
-    k_mean[bh * D + c] = n > 0 ? (float)(total / (double)n) : 0.0f;
+      for (int u = 0; u < U; ++u) s[u] += ksum_part[p + (int64_t)(i + u * P) * D];
+    for (; i < chunks; i += P) s[0] += ksum_part[p + (int64_t)i * D];
+    part_k[pi][c] = ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
   }
   if (WITH_V) {
     float a[U] = {};
-    int i = 0;
-    for (; i + U <= chunks; i += U)
+    int i = pi;
+    for (; i + (U - 1) * P < chunks; i += U * P)
 #pragma unroll
-      for (int u = 0; u < U; ++u) a[u] = fmaxf(a[u], vmax_part[p + (int64_t)(i + u) * D]);
-    for (; i < chunks; ++i) a[0] = fmaxf(a[0], vmax_part[p + (int64_t)i * D]);
-    const float m = fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])), fmaxf(fmaxf(a[4], a[5]), fmaxf(a[6], a[7])));
+      for (int u = 0; u < U; ++u) a[u] = fmaxf(a[u], vmax_part[p + (int64_t)(i + u * P) * D]);
+    for (; i < chunks; i += P) a[0] = fmaxf(a[0], vmax_part[p + (int64_t)i * D]);
+    part_v[pi][c] = fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])), fmaxf(fmaxf(a[4], a[5]), fmaxf(a[6], a[7])));
+  }
+  __syncthreads();
+  if (threadIdx.x >= D) return;
+  if (WITH_K) {
+    double total = part_k[0][c];
+#pragma unroll
+    for (int q = 1; q < P; ++q) total += part_k[q][c];
+    k_mean[bh * D + c] = n > 0 ? (float)(total / (double)n) : 0.0f;
+  }
+  if (WITH_V) {
+    float m = part_v[0][c];
+#pragma unroll
+    for (int q = 1; q < P; ++q) m = fmaxf(m, part_v[q][c]);
     v_scale[bh * D + c] = m / kE4m3Max;
     v_inv[bh * D + c] = m > 0.0f ? kE4m3Max / m : 0.0f;
   }
@@ -446,7 +474,7 @@ static hipError_t launch_qk_t(const QuantQKArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((channel_stats_kernel<T, D, true, false>), dim3(chunks, bhk), dim3(256), 0, st,
                        (const uint16_t*)a.k, (const uint16_t*)nullptr, a.kgeo, a.Hkv, a.Nk, chunks,
                        a.ksum_part, (float*)nullptr, a.seq);
-    hipLaunchKernelGGL((channel_finalize_kernel<D, true, false>), dim3(bhk), dim3(D), 0, st,
+    hipLaunchKernelGGL((channel_finalize_kernel<D, true, false>), dim3(bhk), dim3(kFinalizeThreads), 0, st,
                        a.Nk, chunks, a.ksum_part, (const float*)nullptr, a.k_mean, (float*)nullptr,
                        (float*)nullptr, a.Hkv, a.seq);
     if (a.fine)
@@ -481,8 +509,8 @@ static hipError_t launch_k_mean_t(const void* k, TensorGeom kgeo, int B, int Hkv
   hipLaunchKernelGGL((channel_stats_kernel<T, D, true, false>), dim3(chunks, bhk), dim3(256), 0, st,
                      (const uint16_t*)k, (const uint16_t*)nullptr, kgeo, Hkv, Nk, chunks, ksum_part, (float*)nullptr,
                      seq);
-  hipLaunchKernelGGL((channel_finalize_kernel<D, true, false>), dim3(bhk), dim3(D), 0, st, Nk, chunks, ksum_part,
-                     (const float*)nullptr, k_mean, (float*)nullptr, (float*)nullptr, Hkv, seq);
+  hipLaunchKernelGGL((channel_finalize_kernel<D, true, false>), dim3(bhk), dim3(kFinalizeThreads), 0, st, Nk, chunks,
+                     ksum_part, (const float*)nullptr, k_mean, (float*)nullptr, (float*)nullptr, Hkv, seq);
   return hipGetLastError();
 }
 
@@ -507,7 +535,7 @@ static hipError_t launch_v_t(const QuantVArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((channel_stats_kernel<T, D, false, true>), dim3(chunks, bhk), dim3(256), 0, st,
                        (const uint16_t*)nullptr, (const uint16_t*)a.v, a.vgeo, a.Hkv, a.Nk, chunks,
                        (double*)nullptr, a.vmax_part, a.seq);
-    hipLaunchKernelGGL((channel_finalize_kernel<D, false, true>), dim3(bhk), dim3(D), 0, st,
+    hipLaunchKernelGGL((channel_finalize_kernel<D, false, true>), dim3(bhk), dim3(kFinalizeThreads), 0, st,
                        a.Nk, chunks, (const double*)nullptr, a.vmax_part, (float*)nullptr, a.v_scale,
                        a.v_inv, a.Hkv, a.seq);
     hipLaunchKernelGGL((transpose_v_kernel<T, D, true>), dim3(tiles, bhk), dim3(256), 0, st,
