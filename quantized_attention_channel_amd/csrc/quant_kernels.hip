@@ -16,7 +16,6 @@
 
 namespace sage {
 
-constexpr int kStatChunk = 256;  // tokens per statistics work-group
 
 // Per (b, kv-head, 256-token chunk): fp64 sums of K over tokens per channel and,
 // optionally, fp32 max |V| per channel. Partials go to [B*H][chunks][D] in a
@@ -212,12 +211,28 @@ __global__ __launch_bounds__((QuantThreads<D, BLK>::value)) void quant_int8_kern
 #pragma unroll
   for (int e = 0; e < 8; ++e) mu[e] = SMOOTH ? mean[bh * D + col + e] : 0.0f;
 
-  // One pass per TOKS-token tile. A dense launch has one tile per work-group;
-  // a packed batch's grid covers about the average sequence, and its
-  // work-groups stride over the tiles of longer ones (rather than launching
-  // the longest sequence's tile count for every sequence, mostly empty).
-  for (int bx = gridDim.x - 1 - blockIdx.x; bx * TOKS < N; bx += gridDim.x) {
+  // One pass per TOKS-token tile. Work-group i takes the tiles ntiles-1-i,
+  // ntiles-1-i-G, ... (G = gridDim.x): a dense launch has kQuantTilesPerWg of
+  // them per work-group; a packed batch's grid covers about the average
+  // sequence, and its work-groups stride over the tiles of longer ones (rather
+  // than launching the longest sequence's tile count for every sequence,
+  // mostly empty). The next tile's loads are issued before the current tile's
+  // reduction, so they are in flight during its barrier and its stores.
+  const int ntiles = (N + TOKS - 1) / TOKS;
+  auto load_tile = [&](int bx, i32x4 (&raw)[ITER]) {
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const int t = bx * TOKS + (it * NT + tid) / TPR;
+      raw[it] = t < N ? *reinterpret_cast<const i32x4*>(x + base + (int64_t)t * geo.tok_stride) : i32x4{0, 0, 0, 0};
+    }
+  };
+  const int g = (int)gridDim.x;
+  i32x4 cur[ITER], nxt[ITER];
+  if ((int)blockIdx.x < ntiles) load_tile(ntiles - 1 - (int)blockIdx.x, cur);
+  for (int idx = blockIdx.x; idx < ntiles; idx += g) {
+    const int bx = ntiles - 1 - idx;
     const int t0 = bx * TOKS;
+    if (idx + g < ntiles) load_tile(ntiles - 1 - idx - g, nxt);
     float val[ITER][8];
     float amax[ITER];
 #pragma unroll
@@ -225,10 +240,9 @@ __global__ __launch_bounds__((QuantThreads<D, BLK>::value)) void quant_int8_kern
       const int t = t0 + (it * NT + tid) / TPR;
       amax[it] = 0.0f;
       if (t < N) {
-        i32x4 raw = *reinterpret_cast<const i32x4*>(x + base + (int64_t)t * geo.tok_stride);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          uint16_t bits = (uint16_t)(((uint32_t)raw[e / 2]) >> (16 * (e & 1)));
+          uint16_t bits = (uint16_t)(((uint32_t)cur[it][e / 2]) >> (16 * (e & 1)));
           float f = T::to_f32(bits);
           if (SMOOTH) f = f - mu[e];
           val[it][e] = f;
@@ -289,14 +303,20 @@ __global__ __launch_bounds__((QuantThreads<D, BLK>::value)) void quant_int8_kern
         *reinterpret_cast<i32x2*>(out + (int64_t)t * D) = i32x2{(int)w[0], (int)w[1]};
       }
     }
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) cur[it] = nxt[it];
   }
 }
 
 // Work-groups along the token axis for `units` slots of `per_unit` tokens: one
 // per slot, or, for a packed batch, about the average sequence's slot count
 // (the kernels then stride over the slots of longer sequences).
+// Tiles per work-group of a dense quantisation launch. One: same machine, the
+// whole quantisation took 0.328 ms with one tile per work-group and 0.339,
+// 0.346, 0.359, 0.365 ms with 2, 4, 8, 16 (fewer work-groups in flight).
+constexpr int kQuantTilesPerWg = 1;
 static int token_wgs(int units, int per_unit, const SeqSpan* seq, int B, int total) {
-  if (!seq) return units;
+  if (!seq) return (units + kQuantTilesPerWg - 1) / kQuantTilesPerWg;
   const int64_t per = (int64_t)B * per_unit;
   return (int)std::max<int64_t>(1, std::min<int64_t>(units, ((int64_t)total + per - 1) / per));
 }
@@ -315,8 +335,8 @@ static void launch_quant_int8(const void* x, TensorGeom geo, int BH, int H, int 
                      (const uint16_t*)x, geo, H, N, nblk, mean, codes, scale, seq, side, total);
 }
 
-// One work-group per (b, kv-head, 64-token tile): V transposed to
-// [D][Nk_pad] with keys contiguous per channel. FP8: e4m3(v * (448/a_v[c]));
+// V transposed to [D][Nk_pad] with keys contiguous per channel, in 64-token
+// tiles, kQuantTilesPerWg of them per work-group of a (b, kv-head). FP8: e4m3(v * (448/a_v[c]));
 // otherwise the 16-bit values are copied. Tokens >= N are written as 0.
 // Packed batches (seq set): b is the sequence, its keys [k0, k0 + nk) go to the
 // columns [kp0, kp0 + nk rounded up to the KV tile) of rows [H][D][n_pad].
@@ -328,61 +348,75 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(
   constexpr int ROWB = 64 * EB;                 // bytes per channel row of the tile
   constexpr int UNITS = (64 / 4) * (D / 8);     // 4 tokens x 8 channels per unit
   __shared__ __attribute__((aligned(16))) uint8_t tile[D * ROWB];
+  static_assert(UNITS <= 256, "one unit per thread at most");
   const int tid = threadIdx.x;
   // reverse launch order, as in quant_int8_kernel (V's statistics pass ran just before)
   const int bh = gridDim.y - 1 - blockIdx.y;
   const int b = bh / H, h = bh % H;
-  const int t0 = (gridDim.x - 1 - blockIdx.x) * 64;
   int64_t base = (int64_t)b * geo.batch_stride + (int64_t)h * geo.head_stride;
   int64_t dst0 = (int64_t)bh * D * n_pad;
+  int ntiles = n_pad / 64;
   if (seq) {
     const SeqSpan sp = seq[b];
-    if (t0 >= (sp.nk + kVPad - 1) / kVPad * kVPad) return;   // past this sequence's padded keys
+    ntiles = (sp.nk + kVPad - 1) / kVPad * (kVPad / 64);   // this sequence's padded keys
     N = sp.nk;
     base += (int64_t)sp.k0 * geo.tok_stride;
     dst0 = (int64_t)h * D * n_pad + sp.kp0;
   }
-
-  for (int u = tid; u < UNITS; u += 256) {
-    const int c0 = (u % (D / 8)) * 8;
-    const int tt = (u / (D / 8)) * 4;           // first token of the unit inside the tile
-    uint32_t raw16[4][8];
+  const bool has_unit = tid < UNITS;
+  const int c0 = (tid % (D / 8)) * 8;
+  const int tt = (tid / (D / 8)) * 4;           // first token of the unit inside the tile
+  // Work-group i takes the tiles ntiles-1-i, ntiles-1-i-G, ... (G = gridDim.x),
+  // with the next tile's loads in flight while the current one is converted,
+  // transposed through LDS and stored.
+  auto load_tile = [&](int t0, i32x4 (&raw)[4]) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int t = t0 + tt + j;
-      if (t < N) {
-        i32x4 raw = *reinterpret_cast<const i32x4*>(v + base + (int64_t)t * geo.tok_stride + c0);
+      raw[j] = has_unit && t < N ? *reinterpret_cast<const i32x4*>(v + base + (int64_t)t * geo.tok_stride + c0)
+                                 : i32x4{0, 0, 0, 0};   // +0.0 in both dtypes and in e4m3
+    }
+  };
+  const int g = (int)gridDim.x;
+  i32x4 cur[4], nxt[4];
+  if ((int)blockIdx.x < ntiles) load_tile((ntiles - 1 - (int)blockIdx.x) * 64, cur);
+  for (int idx = blockIdx.x; idx < ntiles; idx += g) {
+    const int t0 = (ntiles - 1 - idx) * 64;
+    if (idx + g < ntiles) load_tile((ntiles - 1 - idx - g) * 64, nxt);
+    if (has_unit) {
+      uint32_t raw16[4][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) raw16[j][e] = (((uint32_t)raw[e / 2]) >> (16 * (e & 1))) & 0xffffu;
-      } else {
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) raw16[j][e] = 0u;   // +0.0 in both dtypes and in e4m3
+        for (int e = 0; e < 8; ++e) raw16[j][e] = (((uint32_t)cur[j][e / 2]) >> (16 * (e & 1))) & 0xffffu;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = c0 + e;
+        if (FP8) {
+          const float s = v_inv[bh * D + c];
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(T::to_f32((uint16_t)raw16[0][e]) * s,
+                                                  T::to_f32((uint16_t)raw16[1][e]) * s, 0, false);
+          w = __builtin_amdgcn_cvt_pk_fp8_f32(T::to_f32((uint16_t)raw16[2][e]) * s,
+                                              T::to_f32((uint16_t)raw16[3][e]) * s, w, true);
+          *reinterpret_cast<int*>(tile + c * ROWB + tt) = w;
+        } else {
+          const uint32_t lo = raw16[0][e] | (raw16[1][e] << 16);
+          const uint32_t hi = raw16[2][e] | (raw16[3][e] << 16);
+          *reinterpret_cast<i32x2*>(tile + c * ROWB + tt * 2) = i32x2{(int)lo, (int)hi};
+        }
       }
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int c = c0 + e;
-      if (FP8) {
-        const float s = v_inv[bh * D + c];
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(T::to_f32((uint16_t)raw16[0][e]) * s,
-                                                T::to_f32((uint16_t)raw16[1][e]) * s, 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(T::to_f32((uint16_t)raw16[2][e]) * s,
-                                            T::to_f32((uint16_t)raw16[3][e]) * s, w, true);
-        *reinterpret_cast<int*>(tile + c * ROWB + tt) = w;
-      } else {
-        const uint32_t lo = raw16[0][e] | (raw16[1][e] << 16);
-        const uint32_t hi = raw16[2][e] | (raw16[3][e] << 16);
-        *reinterpret_cast<i32x2*>(tile + c * ROWB + tt * 2) = i32x2{(int)lo, (int)hi};
-      }
+    __syncthreads();
+    uint8_t* dst = reinterpret_cast<uint8_t*>(out) + (dst0 + t0) * EB;
+    constexpr int CHUNKS = D * ROWB / 16;
+    for (int ci = tid; ci < CHUNKS; ci += 256) {
+      const int c = ci / (ROWB / 16), j = ci % (ROWB / 16);
+      *reinterpret_cast<i32x4*>(dst + (int64_t)c * n_pad * EB + j * 16) =
+          *reinterpret_cast<const i32x4*>(tile + c * ROWB + j * 16);
     }
-  }
-  __syncthreads();
-  uint8_t* dst = reinterpret_cast<uint8_t*>(out) + (dst0 + t0) * EB;
-  constexpr int CHUNKS = D * ROWB / 16;
-  for (int ci = tid; ci < CHUNKS; ci += 256) {
-    const int c = ci / (ROWB / 16), j = ci % (ROWB / 16);
-    *reinterpret_cast<i32x4*>(dst + (int64_t)c * n_pad * EB + j * 16) =
-        *reinterpret_cast<const i32x4*>(tile + c * ROWB + j * 16);
+    __syncthreads();                         // the tile is rewritten by the next pass
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cur[j] = nxt[j];
   }
 }
 
@@ -529,7 +563,8 @@ static hipError_t launch_v_t(const QuantVArgs& a, hipStream_t st) {
   const int bhk = a.B * a.Hkv;
   // (packed batches: n_pad is the padded-key bound of all sequences; a
   //  sequence spans at most the longest one rounded up to the tile)
-  const int tiles = (a.seq ? (a.Nk + kVPad - 1) / kVPad * kVPad : a.n_pad) / 64;
+  const int tiles = ((a.seq ? (a.Nk + kVPad - 1) / kVPad * kVPad : a.n_pad) / 64 + kQuantTilesPerWg - 1) /
+                    kQuantTilesPerWg;
   if (a.fp8) {
     const int chunks = (a.Nk + kStatChunk - 1) / kStatChunk;
     hipLaunchKernelGGL((channel_stats_kernel<T, D, false, true>), dim3(chunks, bhk), dim3(256), 0, st,

@@ -18,7 +18,7 @@ namespace {
 
 using sage::TensorGeom;
 
-constexpr int kStatChunk = 256;
+using sage::kStatChunk;
 constexpr int64_t kMaxSeq = int64_t(1) << 20;
 
 struct Dims {

@@ -25,6 +25,12 @@ struct SeqSpan {
   int32_t reserved[2];
 };
 
+// Tokens per channel-statistics work-group: the K sums and V maxima are kept
+// as one partial per (b, kv-head, chunk of kStatChunk tokens, channel), and
+// the workspace is sized for them.
+// (128 and 512 measured the same as 256 on one machine, within 0.5%.)
+constexpr int kStatChunk = 256;
+
 // The packed work list holds at most total_q / 256 + B query pairs.
 inline int64_t varlen_qpair_bound(int64_t total_q, int64_t B) { return total_q / 256 + B; }
 
