@@ -83,43 +83,58 @@ __global__ __launch_bounds__(256) void quant_rows_fp4_kernel(const uint16_t* __r
   constexpr int ITER = 4;
   // (a work-group covers whole 4-chunk blocks: 256 is a multiple of 4, and a
   //  block past the end is past it in all four lanes)
+  // The ITER chunk loads of a pass are issued together (chunks past the end
+  // read as zero and are not stored), then converted.
   for (int64_t c0 = (int64_t)blockIdx.x * (256 * ITER) + threadIdx.x; c0 < total_chunks;
-       c0 += (int64_t)gridDim.x * (256 * ITER))
+       c0 += (int64_t)gridDim.x * (256 * ITER)) {
+    i32x4 raw[ITER];
 #pragma unroll
-  for (int it = 0; it < ITER; ++it) {
-    const int64_t ci = c0 + it * 256;
-    if (ci >= total_chunks) break;
-    const int64_t row = ci / CPR;
-    const int col = (int)(ci % CPR) * 8;
-    const int64_t bh = row / N;
-    const int t = (int)(row % N);
-    const int b = (int)(bh / H), h = (int)(bh % H);
-    const i32x4 raw = *reinterpret_cast<const i32x4*>(x + (int64_t)b * geo.batch_stride +
-                                                      (int64_t)h * geo.head_stride + (int64_t)t * geo.tok_stride + col);
-    int64_t mrow = bh;                               // row of the smoothing mean
-    if (SMOOTH && seq) {
-      int lo = 0, hi = n_seq - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (seq[mid].k0 <= t) lo = mid; else hi = mid - 1;
+    for (int it = 0; it < ITER; ++it) {
+      const int64_t ci = c0 + it * 256;
+      const int64_t row = ci / CPR;
+      const int col = (int)(ci % CPR) * 8;
+      const int64_t bh = row / N;
+      const int t = (int)(row % N);
+      const int b = (int)(bh / H), h = (int)(bh % H);
+      raw[it] = ci < total_chunks ? *reinterpret_cast<const i32x4*>(x + (int64_t)b * geo.batch_stride +
+                                                                    (int64_t)h * geo.head_stride +
+                                                                    (int64_t)t * geo.tok_stride + col)
+                                  : i32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const int64_t ci = c0 + it * 256;
+      if (ci >= total_chunks) break;
+      const int64_t row = ci / CPR;
+      const int col = (int)(ci % CPR) * 8;
+      const int64_t bh = row / N;
+      const int t = (int)(row % N);
+      const int h = (int)(bh % H);
+      int64_t mrow = bh;                               // row of the smoothing mean
+      if (SMOOTH && seq) {
+        int lo = 0, hi = n_seq - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (seq[mid].k0 <= t) lo = mid; else hi = mid - 1;
+        }
+        mrow = (int64_t)lo * H + h;
       }
-      mrow = (int64_t)lo * H + h;
-    }
-    float v[8];
-    float amax = 0.0f;
+      float v[8];
+      float amax = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float f = T::to_f32((uint16_t)(((uint32_t)raw[e / 2]) >> (16 * (e & 1))));
-      if (SMOOTH) f = f - mean[mrow * D + col + e]; // K: smoothed
-      else f = f * mul;                              // Q: times the score factor
-      v[e] = f;
-      amax = fmaxf(amax, fabsf(f));
+      for (int e = 0; e < 8; ++e) {
+        float f = T::to_f32((uint16_t)(((uint32_t)raw[it][e / 2]) >> (16 * (e & 1))));
+        if (SMOOTH) f = f - mean[mrow * D + col + e]; // K: smoothed
+        else f = f * mul;                              // Q: times the score factor
+        v[e] = f;
+        amax = fmaxf(amax, fabsf(f));
+      }
+      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+      amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+      const int byte = mx_scale_byte(amax);
+      codes[ci] = pack8(v, byte);
+      if ((col & 31) == 0) scale[row * (D / kMx) + col / kMx] = (uint8_t)byte;
     }
-    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-    const int byte = mx_scale_byte(amax);
-    codes[ci] = pack8(v, byte);
-    if ((col & 31) == 0) scale[row * (D / kMx) + col / kMx] = (uint8_t)byte;
   }
 }
 
@@ -157,12 +172,22 @@ __global__ __launch_bounds__(256) void quant_v_fp4_kernel(const uint16_t* __rest
     col0 = sp.kp0 + t0;
     tile0 = sp.kp0 / kBkv + tt;
   }
-  for (int ci = tid; ci < ROWS * D / 8; ci += 256) {
+  // every chunk load of the tile in flight before the first LDS store
+  constexpr int LOADS = ROWS * D / 8 / 256;
+  static_assert(LOADS * 256 == ROWS * D / 8, "the tile's chunks tile the work-group");
+  i32x4 raw[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int ci = tid + 256 * i;
     const int r = ci / (D / 8), c = (ci % (D / 8)) * 8;
     const int t = t0 + r;
-    i32x4 raw = {0, 0, 0, 0};
-    if (t < n) raw = *reinterpret_cast<const i32x4*>(v + base + (int64_t)t * geo.tok_stride + c);
-    *reinterpret_cast<i32x4*>(tile + r * D + c) = raw;
+    raw[i] = t < n ? *reinterpret_cast<const i32x4*>(v + base + (int64_t)t * geo.tok_stride + c) : i32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int ci = tid + 256 * i;
+    const int r = ci / (D / 8), c = (ci % (D / 8)) * 8;
+    *reinterpret_cast<i32x4*>(tile + r * D + c) = raw[i];
   }
   __syncthreads();
   for (int p = tid; p < D * 4; p += 256) {
