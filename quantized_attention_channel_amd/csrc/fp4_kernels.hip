@@ -83,23 +83,39 @@ __global__ __launch_bounds__(256) void quant_rows_fp4_kernel(const uint16_t* __r
   constexpr int ITER = 4;
   // (a work-group covers whole 4-chunk blocks: 256 is a multiple of 4, and a
   //  block past the end is past it in all four lanes)
-  // The ITER chunk loads of a pass are issued together (chunks past the end
-  // read as zero and are not stored), then converted.
+  // The ITER chunk loads of a pass (and, for K, the chunks' smoothing means)
+  // are issued together, then converted. Chunks past the end read as zero and
+  // are not stored.
   for (int64_t c0 = (int64_t)blockIdx.x * (256 * ITER) + threadIdx.x; c0 < total_chunks;
        c0 += (int64_t)gridDim.x * (256 * ITER)) {
     i32x4 raw[ITER];
+    f32x4 mu[ITER][2];
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
       const int64_t ci = c0 + it * 256;
+      const bool live = ci < total_chunks;
       const int64_t row = ci / CPR;
       const int col = (int)(ci % CPR) * 8;
       const int64_t bh = row / N;
       const int t = (int)(row % N);
       const int b = (int)(bh / H), h = (int)(bh % H);
-      raw[it] = ci < total_chunks ? *reinterpret_cast<const i32x4*>(x + (int64_t)b * geo.batch_stride +
-                                                                    (int64_t)h * geo.head_stride +
-                                                                    (int64_t)t * geo.tok_stride + col)
-                                  : i32x4{0, 0, 0, 0};
+      raw[it] = live ? *reinterpret_cast<const i32x4*>(x + (int64_t)b * geo.batch_stride +
+                                                       (int64_t)h * geo.head_stride + (int64_t)t * geo.tok_stride + col)
+                     : i32x4{0, 0, 0, 0};
+      if (SMOOTH) {
+        int64_t mrow = bh;                             // row of the smoothing mean
+        if (seq && live) {
+          int lo = 0, hi = n_seq - 1;
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (seq[mid].k0 <= t) lo = mid; else hi = mid - 1;
+          }
+          mrow = (int64_t)lo * H + h;
+        }
+        const f32x4* mp = reinterpret_cast<const f32x4*>(mean + mrow * D + col);
+        mu[it][0] = live ? mp[0] : f32x4{0.f, 0.f, 0.f, 0.f};
+        mu[it][1] = live ? mp[1] : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     }
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
@@ -107,24 +123,12 @@ __global__ __launch_bounds__(256) void quant_rows_fp4_kernel(const uint16_t* __r
       if (ci >= total_chunks) break;
       const int64_t row = ci / CPR;
       const int col = (int)(ci % CPR) * 8;
-      const int64_t bh = row / N;
-      const int t = (int)(row % N);
-      const int h = (int)(bh % H);
-      int64_t mrow = bh;                               // row of the smoothing mean
-      if (SMOOTH && seq) {
-        int lo = 0, hi = n_seq - 1;
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (seq[mid].k0 <= t) lo = mid; else hi = mid - 1;
-        }
-        mrow = (int64_t)lo * H + h;
-      }
       float v[8];
       float amax = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float f = T::to_f32((uint16_t)(((uint32_t)raw[it][e / 2]) >> (16 * (e & 1))));
-        if (SMOOTH) f = f - mean[mrow * D + col + e]; // K: smoothed
+        if (SMOOTH) f = f - mu[it][e / 4][e % 4];      // K: smoothed
         else f = f * mul;                              // Q: times the score factor
         v[e] = f;
         amax = fmaxf(amax, fabsf(f));

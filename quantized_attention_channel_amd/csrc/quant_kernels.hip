@@ -233,6 +233,9 @@ __global__ __launch_bounds__((QuantThreads<D, BLK>::value)) void quant_int8_kern
     const int bx = ntiles - 1 - idx;
     const int t0 = bx * TOKS;
     if (idx + g < ntiles) load_tile(ntiles - 1 - idx - g, nxt);
+    else
+#pragma unroll
+      for (int it = 0; it < ITER; ++it) nxt[it] = i32x4{0, 0, 0, 0};
     float val[ITER][8];
     float amax[ITER];
 #pragma unroll
@@ -383,6 +386,9 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(
   for (int idx = blockIdx.x; idx < ntiles; idx += g) {
     const int t0 = (ntiles - 1 - idx) * 64;
     if (idx + g < ntiles) load_tile((ntiles - 1 - idx - g) * 64, nxt);
+    else
+#pragma unroll
+      for (int j = 0; j < 4; ++j) nxt[j] = i32x4{0, 0, 0, 0};
     if (has_unit) {
       uint32_t raw16[4][8];
 #pragma unroll
