@@ -28,6 +28,7 @@ import json
 import math
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -176,10 +177,10 @@ def time_steps(plan: Plan, steps: int, warmup: int):
         e2.record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    quant_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / steps
-    attn_ms = sum(b.elapsed_time(c) for _, b, c in ev) / steps
+    quant = [a.elapsed_time(b) for a, b, _ in ev]
+    attn = [b.elapsed_time(c) for _, b, c in ev]
     gpu_ms = sum(a.elapsed_time(c) for a, _, c in ev) / steps
-    return wall * 1e3, gpu_ms, quant_ms, attn_ms
+    return wall * 1e3, gpu_ms, sum(quant) / steps, sum(attn) / steps, statistics.median(quant), statistics.median(attn)
 
 
 def time_fused_entry(plan: Plan, steps: int):
@@ -360,10 +361,11 @@ def host_info():
 def measure(w: W.Workload, pv: str, steps: int, warmup: int, qk_gran: str = "per_block"):
     q, k, v = W.generate(w, device="cuda")
     plan = Fp4Plan(w, q, k, v) if pv == "fp4" else Plan(w, pv, q, k, v, qk_gran)
-    wall_ms, gpu_ms, quant_ms, attn_ms = time_steps(plan, steps, warmup)
+    wall_ms, gpu_ms, quant_ms, attn_ms, quant_med, attn_med = time_steps(plan, steps, warmup)
     fused_ms = time_fused_entry(plan, max(3, steps // 4))
     ops = counted_ops(w)
     return dict(wall_ms=wall_ms, gpu_ms=gpu_ms, quant_ms=quant_ms, attn_ms=attn_ms, fused_ms=fused_ms,
+                quant_median_ms=quant_med, attn_median_ms=attn_med,
                 tops=ops / (wall_ms * 1e-3) / 1e12, attn_tops=ops / (attn_ms * 1e-3) / 1e12,
                 quant_bytes=3.0 * (w.B * w.Hq * w.N * w.d + 2 * w.B * w.Hkv * w.N * w.d))
 
@@ -456,7 +458,7 @@ def main():
             "kernel": ("attn_fp4_kernel" if pv == "fp4" else
                        "attn_fwd_fine_kernel" if args.qk_gran == "per_thread" else "attn_fwd_kernel"),
             "ops_per_launch": counted_ops(w),
-            "mean_launch_ms": round(r["attn_ms"], 4)}
+            "mean_launch_ms": round(r["attn_ms"], 4), "median_launch_ms": round(r["attn_median_ms"], 4)}
     if util:
         roof["counters_pct"] = util     # rocprofv3 VALUBusy / MfmaUtil of the same kernel (profiles/)
     out = {
@@ -471,7 +473,8 @@ def main():
         "mfma_peak_frac": round(r["tops"] / peak, 4),
         "roofline": roof,
         "breakdown_ms": {"gpu_step": round(r["gpu_ms"], 4), "quant": round(r["quant_ms"], 4),
-                         "attention": round(r["attn_ms"], 4), "sage_attn_fwd_single_call": round(r["fused_ms"], 4)},
+                         "attention": round(r["attn_ms"], 4), "sage_attn_fwd_single_call": round(r["fused_ms"], 4),
+                         "quant_median": round(r["quant_median_ms"], 4), "attention_median": round(r["attn_median_ms"], 4)},
         "quant_hbm": {"algorithmic_bytes": r["quant_bytes"], "copy_GBps": round(copy_gbps, 1),
                       "frac_of_copy": round(r["quant_bytes"] / (r["quant_ms"] * 1e-3) / 1e9 / copy_gbps, 4),
                       "GBps": round(r["quant_bytes"] / (r["quant_ms"] * 1e-3) / 1e9, 1),
